@@ -1,0 +1,308 @@
+"""Pins of the fp64 oracle against routes that do not share its arithmetic.
+
+Each pin would fail on a plausible mistake in the oracle (a dropped term, a
+wrong sign or index, a transposed operand); test_pins_catch_planted_mistakes
+plants such mistakes in the oracle, on the CPU, and checks that they are caught.
+
+Independent routes used:
+  * torch.autograd on an attention forward written with torch ops (first
+    derivatives for the finite-difference objective; second derivatives with
+    create_graph for the whole BoB);
+  * central finite differences of the scalar objective;
+  * forward-mode JVP of attention (graddO is the JVP along the cotangents);
+  * second derivatives of the forward along a line (quadratic form);
+  * torch's scaled_dot_product_attention backward (special case gQ = gK = 0);
+  * identities the mathematics fixes: Hessian symmetry, Euler identity,
+    bilinearity, zero cotangents, N = 1, key-shift invariance.
+"""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import bob_oracle
+
+torch.set_default_dtype(torch.float64)
+
+SHAPES = [(1, 3), (5, 4), (33, 8), (64, 16)]
+
+
+def rand_inputs(N, d, seed, qk=1.0):
+    rng = np.random.default_rng(seed)
+    xs = [rng.standard_normal((N, d)) for _ in range(7)]
+    xs[0] *= qk
+    xs[1] *= qk
+    return xs
+
+
+def rel(a, b):
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    nb = np.linalg.norm(b)
+    return np.linalg.norm(a - b) / (nb if nb > 0 else 1.0)
+
+
+# ----------------------------------------------------------------------------
+# independent torch routes (no oracle code)
+
+
+def torch_attn(Q, K, V, scale):
+    return torch.softmax(scale * Q @ K.T, dim=-1) @ V
+
+
+def torch_first_backward(Q, K, V, dO, scale, create_graph):
+    """(dQ, dK, dV) = gradient of <dO, attention(Q, K, V)> by torch.autograd."""
+    f = torch.sum(dO * torch_attn(Q, K, V, scale))
+    return torch.autograd.grad(f, (Q, K, V), create_graph=create_graph)
+
+
+def torch_L(xs, scale):
+    Q, K, V, dO, gQ, gK, gV = [torch.tensor(x, requires_grad=True) for x in xs]
+    dQ, dK, dV = torch_first_backward(Q, K, V, dO, scale, create_graph=True)
+    L = torch.sum(gQ * dQ) + torch.sum(gK * dK) + torch.sum(gV * dV)
+    return L, (Q, K, V, dO)
+
+
+def torch_bob(xs, scale):
+    L, prim = torch_L(xs, scale)
+    grads = torch.autograd.grad(L, prim, allow_unused=True)
+    return [np.zeros(x.shape) if g is None else g.detach().numpy() for g, x in zip(grads, xs[:4])]
+
+
+def L_value(xs, scale):
+    """Objective through torch first derivatives only (no second order)."""
+    Q, K, V, dO = [torch.tensor(x, requires_grad=True) for x in xs[:4]]
+    dQ, dK, dV = torch_first_backward(Q, K, V, dO, scale, create_graph=False)
+    gQ, gK, gV = [torch.tensor(x) for x in xs[4:]]
+    return float(torch.sum(gQ * dQ) + torch.sum(gK * dK) + torch.sum(gV * dV))
+
+
+# ----------------------------------------------------------------------------
+# pins
+
+
+@pytest.mark.parametrize("N,d", SHAPES)
+def test_matches_autograd_double_backward(N, d):
+    xs = rand_inputs(N, d, seed=10 * N + d)
+    s = 1.0 / math.sqrt(d)
+    got = oracle.bob_head(*xs, s)
+    ref = torch_bob(xs, s)
+    for g, r in zip(got, ref):
+        if np.linalg.norm(r) == 0:
+            assert np.abs(g).max() < 1e-12
+        else:
+            assert rel(g, r) < 1e-12
+
+
+@pytest.mark.parametrize("N,d", [(5, 4), (33, 8)])
+def test_central_finite_differences(N, d):
+    xs = rand_inputs(N, d, seed=7 + N)
+    s = 1.0 / math.sqrt(d)
+    got = oracle.bob_head(*xs, s)
+    rng = np.random.default_rng(99)
+    h = 1e-5
+    for k in range(4):  # Q, K, V, dO
+        u = rng.standard_normal(xs[k].shape)
+        xp = list(xs)
+        xm = list(xs)
+        xp[k] = xs[k] + h * u
+        xm[k] = xs[k] - h * u
+        fd = (L_value(xp, s) - L_value(xm, s)) / (2 * h)
+        an = float(np.sum(got[k] * u))
+        assert abs(fd - an) <= 1e-7 * max(1.0, abs(an)), (k, fd, an)
+
+
+@pytest.mark.parametrize("N,d", SHAPES)
+def test_graddO_is_forward_jvp(N, d):
+    xs = rand_inputs(N, d, seed=3 * N + d)
+    s = 1.0 / math.sqrt(d)
+    _, _, _, graddO = oracle.bob_head(*xs, s)
+    prim = tuple(torch.tensor(x) for x in xs[:3])
+    tang = tuple(torch.tensor(x) for x in xs[4:])
+    _, jvp = torch.func.jvp(lambda q, k, v: torch_attn(q, k, v, s), prim, tang)
+    assert rel(graddO, jvp.numpy()) < 1e-12
+
+
+@pytest.mark.parametrize("N,d", [(5, 4), (33, 8), (64, 16)])
+def test_hessian_symmetry(N, d):
+    xs = rand_inputs(N, d, seed=N + 5 * d)
+    hs = rand_inputs(N, d, seed=N + 5 * d + 1)[4:]
+    s = 1.0 / math.sqrt(d)
+    bg = oracle.bob_head(*xs, s)
+    bh = oracle.bob_head(*xs[:4], *hs, s)
+    lhs = sum(np.sum(h * b) for h, b in zip(hs, bg[:3]))
+    rhs = sum(np.sum(g * b) for g, b in zip(xs[4:], bh[:3]))
+    assert abs(lhs - rhs) <= 1e-12 * max(1.0, abs(lhs))
+
+
+@pytest.mark.parametrize("N,d", [(5, 4), (33, 8)])
+def test_quadratic_form_is_second_derivative_of_forward(N, d):
+    xs = rand_inputs(N, d, seed=11 * N + d)
+    s = 1.0 / math.sqrt(d)
+    Q, K, V, dO, gQ, gK, gV = [torch.tensor(x) for x in xs]
+    gradQ, gradK, gradV, _ = oracle.bob_head(*xs, s)
+    quad = np.sum(xs[4] * gradQ) + np.sum(xs[5] * gradK) + np.sum(xs[6] * gradV)
+    t = torch.zeros((), requires_grad=True)
+    f = torch.sum(dO * torch_attn(Q + t * gQ, K + t * gK, V + t * gV, s))
+    (df,) = torch.autograd.grad(f, t, create_graph=True)
+    (d2f,) = torch.autograd.grad(df, t)
+    assert abs(float(d2f) - quad) <= 1e-10 * max(1.0, abs(quad))
+
+
+@pytest.mark.parametrize("N,d", SHAPES)
+def test_euler_identity(N, d):
+    xs = rand_inputs(N, d, seed=2 * N + d)
+    s = 1.0 / math.sqrt(d)
+    _, _, _, graddO = oracle.bob_head(*xs, s)
+    L = L_value(xs, s)
+    assert abs(np.sum(xs[3] * graddO) - L) <= 1e-12 * max(1.0, abs(L))
+
+
+def test_bilinearity():
+    xs = rand_inputs(33, 8, seed=1)
+    s = 1.0 / math.sqrt(8)
+    base = oracle.bob_head(*xs, s)
+    x2 = list(xs)
+    x2[3] = 2.0 * xs[3]
+    two = oracle.bob_head(*x2, s)
+    for k in range(3):
+        assert rel(two[k], 2.0 * base[k]) < 1e-13
+    assert rel(two[3], base[3]) < 1e-13
+    x3 = list(xs)
+    for k in range(4, 7):
+        x3[k] = 3.0 * xs[k]
+    three = oracle.bob_head(*x3, s)
+    for k in range(4):
+        assert rel(three[k], 3.0 * base[k]) < 1e-13
+
+
+def test_zero_cotangents_and_zero_dO():
+    xs = rand_inputs(33, 8, seed=2)
+    s = 1.0 / math.sqrt(8)
+    z = list(xs)
+    for k in range(4, 7):
+        z[k] = np.zeros_like(xs[k])
+    for out in oracle.bob_head(*z, s):
+        assert np.all(out == 0.0)
+    z = list(xs)
+    z[3] = np.zeros_like(xs[3])
+    gq, gk, gv, gdo = oracle.bob_head(*z, s)
+    assert np.all(gq == 0) and np.all(gk == 0) and np.all(gv == 0)
+    assert np.linalg.norm(gdo) > 0
+
+
+@pytest.mark.parametrize("N,d", [(5, 4), (64, 16)])
+def test_gQ_gK_zero_reduces_to_textbook_attention_backward(N, d):
+    xs = rand_inputs(N, d, seed=17 + N)
+    xs[4] = np.zeros_like(xs[4])
+    xs[5] = np.zeros_like(xs[5])
+    s = 1.0 / math.sqrt(d)
+    gq, gk, gv, gdo = oracle.bob_head(*xs, s)
+    Q, K, gV, dO = [torch.tensor(x, requires_grad=True) for x in (xs[0], xs[1], xs[6], xs[3])]
+    O = torch.nn.functional.scaled_dot_product_attention(
+        Q[None, None], K[None, None], gV[None, None], scale=s)[0, 0]
+    dq, dk = torch.autograd.grad(torch.sum(dO * O), (Q, K))
+    assert rel(gq, dq.numpy()) < 1e-12
+    assert rel(gk, dk.numpy()) < 1e-12
+    assert np.all(gv == 0.0)
+    assert rel(gdo, O.detach().numpy()) < 1e-12
+
+
+def test_single_key_gives_zero_gradients_and_gV():
+    xs = rand_inputs(1, 8, seed=4)
+    gq, gk, gv, gdo = oracle.bob_head(*xs, 0.35)
+    # P = 1 exactly, so dS = dP - D and A = G - c vanish up to the rounding of
+    # two fp64 dot products of the same vectors
+    tol = 1e-14 * max(np.abs(x).max() for x in xs) ** 3
+    assert np.abs(gq).max() < tol and np.abs(gk).max() < tol and np.abs(gv).max() < tol
+    assert np.abs(gdo - xs[6]).max() < tol
+
+
+@pytest.mark.parametrize("N,d", SHAPES)
+def test_key_shift_invariance_column_sums(N, d):
+    xs = rand_inputs(N, d, seed=5 * N + d)
+    gq, gk, gv, _ = oracle.bob_head(*xs, 1.0 / math.sqrt(d))
+    scale_k = max(1.0, np.abs(gk).max())
+    scale_v = max(1.0, np.abs(gv).max())
+    assert np.abs(gk.sum(axis=0)).max() < 1e-12 * N * scale_k
+    assert np.abs(gv.sum(axis=0)).max() < 1e-12 * N * scale_v
+
+
+@pytest.mark.parametrize("N,d,block", [(33, 8, 7), (64, 16, 16), (64, 16, 64)])
+def test_row_stats_three_routes(N, d, block):
+    xs = rand_inputs(N, d, seed=N * d)
+    s = 1.0 / math.sqrt(d)
+    lse, D, c, r = oracle.row_stats_head(*xs, s)
+    D2, c2, r2 = oracle.row_stats_closed_forms_head(*xs, s)
+    lse3, D3, c3, r3 = oracle.row_stats_online_head(*xs, s, block)
+    S = s * xs[0] @ xs[1].T
+    lse_lib = np.logaddexp.reduce(S, axis=1)
+    for a, b in ((lse, lse_lib), (lse3, lse_lib), (D, D2), (D, D3), (c, c2), (c, c3), (r, r2), (r, r3)):
+        assert np.abs(a - b).max() < 1e-12 * max(1.0, np.abs(b).max())
+
+
+def test_blocked_and_row_forms_match_full():
+    xs = rand_inputs(64, 8, seed=9)
+    s = 1.0 / math.sqrt(8)
+    full = oracle.bob_head(*xs, s)
+    blk = oracle.bob_blocked_head(*xs, s, block=24)
+    for a, b in zip(blk, full):
+        assert rel(a, b) < 1e-13
+    rows = np.arange(16, 40)
+    gq, gdo = oracle.bob_rows_head(*xs, s, rows)
+    assert rel(gq, full[0][rows]) < 1e-13
+    assert rel(gdo, full[3][rows]) < 1e-13
+
+
+def test_batched_wrappers_loop_heads():
+    rng = np.random.default_rng(0)
+    xs = [rng.standard_normal((2, 3, 17, 4)) for _ in range(7)]
+    out = oracle.bob(*xs, 0.5)
+    outb = oracle.bob_blocked(*xs, 0.5, block=5)
+    for b in range(2):
+        for h in range(3):
+            ref = oracle.bob_head(*[x[b, h] for x in xs], 0.5)
+            for k in range(4):
+                assert rel(out[k][b, h], ref[k]) < 1e-14
+                assert rel(outb[k][b, h], ref[k]) < 1e-13
+
+
+# ----------------------------------------------------------------------------
+# the pins above catch plausible mistakes (planted in the oracle, CPU only)
+
+MUTATIONS = {
+    "drop_P_H_term": lambda t: t.update(dS2=t["dS"] * (t["G"] - t["c"])),
+    "no_centering_c": lambda t: t.update(A=t["P"] * t["G"]),
+    "r_sign": lambda t: t.update(dS2=t["dS"] * (t["G"] - t["c"]) + t["P"] * (t["H"] + t["r"])),
+    "D_as_constant": lambda t: t.update(A=t["P"] * t["G"],
+                                        dS2=t["dS"] * t["G"] + t["P"] * (t["H"] - t["r"])),
+    "LSE_as_constant": lambda t: t.update(dS2=t["dS"] * (t["G"] - t["c"]) + t["P"] * t["H"]),
+    "transposed_G": lambda t: t.update(dS2=t["dS"] * (t["G"].T - t["c"]) + t["P"] * (t["H"] - t["r"])),
+    "H_from_V": lambda t: t.update(H=t["dP"]),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTATIONS))
+def test_pins_catch_planted_mistakes(name, monkeypatch):
+    N, d = 16, 4
+    xs = rand_inputs(N, d, seed=123)
+    s = 1.0 / math.sqrt(d)
+    orig = bob_oracle._tiles
+
+    def mutated(*a, **k):
+        t = orig(*a, **k)
+        if name == "H_from_V":
+            MUTATIONS[name](t)
+            t["dS2"] = t["dS"] * (t["G"] - t["c"]) + t["P"] * (t["H"] - t["r"])
+        else:
+            MUTATIONS[name](t)
+        return t
+
+    monkeypatch.setattr(bob_oracle, "_tiles", mutated)
+    got = oracle.bob_head(*xs, s)
+    ref = torch_bob(xs, s)
+    worst = max(rel(g, r) for g, r in zip(got, ref))
+    assert worst > 1e-3, f"mutation {name} not caught (worst rel {worst})"
