@@ -1,0 +1,219 @@
+// Host side of the C ABI declared in include/flashbob.h: argument checks
+// (all before any HIP call), workspace split, and the two kernel launches of
+// the BoB schedule on the caller's stream.
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+#include <string>
+
+#include "flashbob.h"
+
+namespace flashbob {
+typedef __bf16 bf16;
+template <typename T, int D>
+hipError_t launch_rowstats(const void* Q, const void* K, const void* V, const void* dO, const void* gQ,
+                           const void* gK, const void* gV, float* lse, float* Dv, float* cv, float* rv,
+                           float* zero_a, float* zero_b, int BH, int N, float scale, hipStream_t stream);
+template <typename T, int D>
+hipError_t launch_pass2(const void* Q, const void* K, const void* V, const void* dO, const void* gQ,
+                        const void* gK, const void* gV, const float* stats, float* gradQ, float* gradK,
+                        float* gradV, float* graddO, int BH, int N, float scale, hipStream_t stream);
+}  // namespace flashbob
+
+namespace {
+
+thread_local std::string g_last_hip_error = "no HIP error recorded";
+
+int hip_fail(hipError_t e) {
+  g_last_hip_error = std::string(hipGetErrorName(e)) + ": " + hipGetErrorString(e);
+  return FLASHBOB_ERR_HIP;
+}
+
+struct Range {
+  uintptr_t lo, hi;  // [lo, hi)
+};
+
+bool overlaps(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi; }
+
+// Shared validation. On success fills the element count of one tensor.
+int check_common(const void* const* ins, int B, int H, int N, int d, float scale, int dtype, size_t* numel) {
+  if (B < 0 || H < 0 || N < 0) return FLASHBOB_ERR_SHAPE;
+  if (d != 64 && d != 128) return FLASHBOB_ERR_UNSUPPORTED_D;
+  if (dtype != FLASHBOB_F32 && dtype != FLASHBOB_BF16) return FLASHBOB_ERR_DTYPE;
+  if (!std::isfinite(scale)) return FLASHBOB_ERR_SCALE;
+  // B*H*N*d < 2^62 (fits every index computed in size_t) and B*H*N < 2^31
+  const unsigned __int128 n = (unsigned __int128)B * H * N * d;
+  if (n >= ((unsigned __int128)1 << 62)) return FLASHBOB_ERR_SHAPE;
+  if ((unsigned __int128)B * H * N >= ((unsigned __int128)1 << 31)) return FLASHBOB_ERR_SHAPE;
+  if ((long long)B * H >= (1LL << 31)) return FLASHBOB_ERR_SHAPE;
+  *numel = (size_t)n;
+  if (*numel == 0) return FLASHBOB_OK;
+  for (int i = 0; i < 7; ++i) {
+    if (ins[i] == nullptr) return FLASHBOB_ERR_NULL;
+    if (reinterpret_cast<uintptr_t>(ins[i]) % 16) return FLASHBOB_ERR_ALIGN;
+  }
+  return FLASHBOB_OK;
+}
+
+int check_outputs(const void* const* ins, size_t in_bytes, void* const* outs, const size_t* out_bytes, int nout) {
+  for (int i = 0; i < nout; ++i) {
+    if (outs[i] == nullptr) return FLASHBOB_ERR_NULL;
+    if (reinterpret_cast<uintptr_t>(outs[i]) % 16) return FLASHBOB_ERR_ALIGN;
+  }
+  for (int i = 0; i < nout; ++i) {
+    const Range ro{reinterpret_cast<uintptr_t>(outs[i]), reinterpret_cast<uintptr_t>(outs[i]) + out_bytes[i]};
+    for (int j = 0; j < 7; ++j) {
+      const Range ri{reinterpret_cast<uintptr_t>(ins[j]), reinterpret_cast<uintptr_t>(ins[j]) + in_bytes};
+      if (overlaps(ro, ri)) return FLASHBOB_ERR_ALIAS;
+    }
+    for (int j = i + 1; j < nout; ++j) {
+      const Range rj{reinterpret_cast<uintptr_t>(outs[j]), reinterpret_cast<uintptr_t>(outs[j]) + out_bytes[j]};
+      if (overlaps(ro, rj)) return FLASHBOB_ERR_ALIAS;
+    }
+  }
+  return FLASHBOB_OK;
+}
+
+template <typename T>
+hipError_t run_rowstats(int d, const void* const* in, float* lse, float* Dv, float* cv, float* rv, float* za,
+                        float* zb, int BH, int N, float scale, hipStream_t st) {
+  if (d == 64)
+    return flashbob::launch_rowstats<T, 64>(in[0], in[1], in[2], in[3], in[4], in[5], in[6], lse, Dv, cv, rv,
+                                            za, zb, BH, N, scale, st);
+  return flashbob::launch_rowstats<T, 128>(in[0], in[1], in[2], in[3], in[4], in[5], in[6], lse, Dv, cv, rv, za,
+                                           zb, BH, N, scale, st);
+}
+
+template <typename T>
+hipError_t run_pass2(int d, const void* const* in, const float* stats, float* gQo, float* gKo, float* gVo,
+                     float* gdOo, int BH, int N, float scale, hipStream_t st) {
+  if (d == 64)
+    return flashbob::launch_pass2<T, 64>(in[0], in[1], in[2], in[3], in[4], in[5], in[6], stats, gQo, gKo, gVo,
+                                         gdOo, BH, N, scale, st);
+  return flashbob::launch_pass2<T, 128>(in[0], in[1], in[2], in[3], in[4], in[5], in[6], stats, gQo, gKo, gVo,
+                                        gdOo, BH, N, scale, st);
+}
+
+size_t stats_bytes(int B, int H, int N) {
+  const size_t raw = (size_t)4 * sizeof(float) * (size_t)B * (size_t)H * (size_t)N;
+  return (raw + 255) & ~(size_t)255;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t flashbob_workspace_bytes(int B, int H, int N, int d) {
+  (void)d;
+  if (B <= 0 || H <= 0 || N <= 0) return 0;
+  return stats_bytes(B, H, N);
+}
+
+static int bob_passes(const void* Q, const void* K, const void* V, const void* dO, const void* gQ,
+                      const void* gK, const void* gV, float* gradQ, float* gradK, float* gradV, float* graddO,
+                      int B, int H, int N, int d, float scale, int dtype, void* workspace,
+                      size_t workspace_bytes, void* stream, bool run1, bool run2) {
+  const void* ins[7] = {Q, K, V, dO, gQ, gK, gV};
+  size_t numel = 0;
+  int rc = check_common(ins, B, H, N, d, scale, dtype, &numel);
+  if (rc != FLASHBOB_OK || numel == 0) return rc;
+  const size_t esz = dtype == FLASHBOB_BF16 ? 2 : 4;
+  const size_t ws_need = stats_bytes(B, H, N);
+  if (workspace == nullptr) return FLASHBOB_ERR_NULL;
+  if (workspace_bytes < ws_need) return FLASHBOB_ERR_WORKSPACE;
+  void* outs[5] = {gradQ, gradK, gradV, graddO, workspace};
+  const size_t ob[5] = {numel * 4, numel * 4, numel * 4, numel * 4, ws_need};
+  rc = check_outputs(ins, numel * esz, outs, ob, 5);
+  if (rc != FLASHBOB_OK) return rc;
+
+  const int BH = B * H;
+  const size_t BHN = (size_t)BH * N;
+  float* ws = static_cast<float*>(workspace);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  hipError_t e;
+  if (run1) {
+    if (dtype == FLASHBOB_BF16)
+      e = run_rowstats<__bf16>(d, ins, ws, ws + BHN, ws + 2 * BHN, ws + 3 * BHN, gradQ, graddO, BH, N, scale, st);
+    else
+      e = run_rowstats<float>(d, ins, ws, ws + BHN, ws + 2 * BHN, ws + 3 * BHN, gradQ, graddO, BH, N, scale, st);
+    if (e != hipSuccess) return hip_fail(e);
+  }
+  if (run2) {
+    if (dtype == FLASHBOB_BF16)
+      e = run_pass2<__bf16>(d, ins, ws, gradQ, gradK, gradV, graddO, BH, N, scale, st);
+    else
+      e = run_pass2<float>(d, ins, ws, gradQ, gradK, gradV, graddO, BH, N, scale, st);
+    if (e != hipSuccess) return hip_fail(e);
+  }
+  return FLASHBOB_OK;
+}
+
+int flashbob_bob(const void* Q, const void* K, const void* V, const void* dO, const void* gQ, const void* gK,
+                 const void* gV, float* gradQ, float* gradK, float* gradV, float* graddO, int B, int H, int N,
+                 int d, float scale, int dtype, void* workspace, size_t workspace_bytes, void* stream) {
+  return bob_passes(Q, K, V, dO, gQ, gK, gV, gradQ, gradK, gradV, graddO, B, H, N, d, scale, dtype, workspace,
+                    workspace_bytes, stream, true, true);
+}
+
+int flashbob_bob_pass1(const void* Q, const void* K, const void* V, const void* dO, const void* gQ,
+                       const void* gK, const void* gV, float* gradQ, float* gradK, float* gradV, float* graddO,
+                       int B, int H, int N, int d, float scale, int dtype, void* workspace,
+                       size_t workspace_bytes, void* stream) {
+  return bob_passes(Q, K, V, dO, gQ, gK, gV, gradQ, gradK, gradV, graddO, B, H, N, d, scale, dtype, workspace,
+                    workspace_bytes, stream, true, false);
+}
+
+int flashbob_bob_pass2(const void* Q, const void* K, const void* V, const void* dO, const void* gQ,
+                       const void* gK, const void* gV, float* gradQ, float* gradK, float* gradV, float* graddO,
+                       int B, int H, int N, int d, float scale, int dtype, void* workspace,
+                       size_t workspace_bytes, void* stream) {
+  return bob_passes(Q, K, V, dO, gQ, gK, gV, gradQ, gradK, gradV, graddO, B, H, N, d, scale, dtype, workspace,
+                    workspace_bytes, stream, false, true);
+}
+
+int flashbob_rowstats(const void* Q, const void* K, const void* V, const void* dO, const void* gQ,
+                      const void* gK, const void* gV, float* lse, float* Dv, float* cv, float* rv, int B, int H,
+                      int N, int d, float scale, int dtype, void* stream) {
+  const void* ins[7] = {Q, K, V, dO, gQ, gK, gV};
+  size_t numel = 0;
+  int rc = check_common(ins, B, H, N, d, scale, dtype, &numel);
+  if (rc != FLASHBOB_OK || numel == 0) return rc;
+  const size_t esz = dtype == FLASHBOB_BF16 ? 2 : 4;
+  const size_t vb = (size_t)B * H * N * sizeof(float);
+  void* outs[4] = {lse, Dv, cv, rv};
+  const size_t ob[4] = {vb, vb, vb, vb};
+  rc = check_outputs(ins, numel * esz, outs, ob, 4);
+  if (rc != FLASHBOB_OK) return rc;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  hipError_t e;
+  if (dtype == FLASHBOB_BF16)
+    e = run_rowstats<__bf16>(d, ins, lse, Dv, cv, rv, nullptr, nullptr, B * H, N, scale, st);
+  else
+    e = run_rowstats<float>(d, ins, lse, Dv, cv, rv, nullptr, nullptr, B * H, N, scale, st);
+  if (e != hipSuccess) return hip_fail(e);
+  return FLASHBOB_OK;
+}
+
+const char* flashbob_strerror(int code) {
+  switch (code) {
+    case FLASHBOB_OK: return "ok";
+    case FLASHBOB_ERR_NULL: return "a required pointer is NULL";
+    case FLASHBOB_ERR_SHAPE: return "invalid shape (negative size or too many elements)";
+    case FLASHBOB_ERR_UNSUPPORTED_D: return "unsupported head dimension (d must be 64 or 128)";
+    case FLASHBOB_ERR_UNSUPPORTED_N: return "unsupported sequence length";
+    case FLASHBOB_ERR_DTYPE: return "unknown dtype";
+    case FLASHBOB_ERR_ALIGN: return "a pointer is not 16-byte aligned";
+    case FLASHBOB_ERR_WORKSPACE: return "workspace too small";
+    case FLASHBOB_ERR_ALIAS: return "an output overlaps an input, the workspace or another output";
+    case FLASHBOB_ERR_SCALE: return "scale is not finite";
+    case FLASHBOB_ERR_HIP: return g_last_hip_error.c_str();
+    default: return "unknown error code";
+  }
+}
+
+int flashbob_version(void) { return 100; }
+
+}  // extern "C"

@@ -1,0 +1,183 @@
+"""Python binding of the C ABI in include/flashbob.h (argument marshalling only).
+
+Every step of the computation runs in the HIP kernels of libflashbob.so; torch
+only provides device memory and the current stream. If the library is not
+built, loading fails loudly: there is no fallback path.
+"""
+
+import ctypes
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libflashbob.so")
+
+FLASHBOB_F32 = 0
+FLASHBOB_BF16 = 1
+
+ERRORS = {
+    0: "OK",
+    -1: "ERR_NULL",
+    -2: "ERR_SHAPE",
+    -3: "ERR_UNSUPPORTED_D",
+    -4: "ERR_UNSUPPORTED_N",
+    -5: "ERR_DTYPE",
+    -6: "ERR_ALIGN",
+    -7: "ERR_WORKSPACE",
+    -8: "ERR_ALIAS",
+    -9: "ERR_SCALE",
+    -100: "ERR_HIP",
+}
+
+EXPORTS = (
+    "flashbob_workspace_bytes",
+    "flashbob_bob",
+    "flashbob_bob_pass1",
+    "flashbob_bob_pass2",
+    "flashbob_rowstats",
+    "flashbob_strerror",
+    "flashbob_version",
+)
+
+_lib = None
+
+
+class FlashBoBError(RuntimeError):
+    def __init__(self, code, msg):
+        super().__init__(f"flashbob error {code} ({ERRORS.get(code, '?')}): {msg}")
+        self.code = code
+
+
+def load_library(path=LIB_PATH):
+    """Load libflashbob.so and declare the C signatures."""
+    global _lib
+    if _lib is not None and path == LIB_PATH:
+        return _lib
+    if not os.path.exists(path):
+        raise FileNotFoundError(
+            f"{path} is missing: build it with `python -m exact_second_order_amd.build`")
+    lib = ctypes.CDLL(path)
+    vp, i, f, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    lib.flashbob_workspace_bytes.argtypes = [i, i, i, i]
+    lib.flashbob_workspace_bytes.restype = sz
+    lib.flashbob_bob.argtypes = [vp] * 7 + [vp] * 4 + [i, i, i, i, f, i, vp, sz, vp]
+    lib.flashbob_bob.restype = i
+    for name in ("flashbob_bob_pass1", "flashbob_bob_pass2"):
+        fn = getattr(lib, name)
+        fn.argtypes = [vp] * 7 + [vp] * 4 + [i, i, i, i, f, i, vp, sz, vp]
+        fn.restype = i
+    lib.flashbob_rowstats.argtypes = [vp] * 7 + [vp] * 4 + [i, i, i, i, f, i, vp]
+    lib.flashbob_rowstats.restype = i
+    lib.flashbob_strerror.argtypes = [i]
+    lib.flashbob_strerror.restype = ctypes.c_char_p
+    lib.flashbob_version.argtypes = []
+    lib.flashbob_version.restype = i
+    if path == LIB_PATH:
+        _lib = lib
+    return lib
+
+
+def _check(code):
+    if code != 0:
+        msg = load_library().flashbob_strerror(code).decode()
+        raise FlashBoBError(code, msg)
+
+
+def _dtype_code(dt):
+    if dt == torch.bfloat16:
+        return FLASHBOB_BF16
+    if dt == torch.float32:
+        return FLASHBOB_F32
+    raise TypeError(f"unsupported dtype {dt}; use torch.bfloat16 or torch.float32")
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+
+def _stream_handle(device, stream):
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _inputs(Q, K, V, dO, gQ, gK, gV):
+    ins = (Q, K, V, dO, gQ, gK, gV)
+    for t in ins:
+        if not isinstance(t, torch.Tensor) or not t.is_cuda:
+            raise TypeError("all inputs must be device tensors")
+        if t.shape != Q.shape or t.dtype != Q.dtype or t.device != Q.device:
+            raise ValueError("all inputs need the same shape, dtype and device")
+        if not t.is_contiguous():
+            raise ValueError("inputs must be contiguous [B, H, N, d]")
+    if Q.dim() != 4:
+        raise ValueError("inputs must be [B, H, N, d]")
+    return ins
+
+
+def workspace_bytes(B, H, N, d):
+    return int(load_library().flashbob_workspace_bytes(B, H, N, d))
+
+
+def bob_pass(which, Q, K, V, dO, gQ, gK, gV, out, workspace, scale=None, stream=None):
+    """One half of bob(): which=1 (row scalars, zero gradQ/graddO) or 2 (accumulate)."""
+    lib = load_library()
+    ins = _inputs(Q, K, V, dO, gQ, gK, gV)
+    B, H, N, d = Q.shape
+    if scale is None:
+        scale = d ** -0.5
+    fn = lib.flashbob_bob_pass1 if which == 1 else lib.flashbob_bob_pass2
+    rc = fn(*[_ptr(t) for t in ins], *[_ptr(t) for t in out], B, H, N, d, ctypes.c_float(scale),
+            _dtype_code(Q.dtype), _ptr(workspace),
+            ctypes.c_size_t(workspace.numel() * workspace.element_size()),
+            _stream_handle(Q.device, stream))
+    _check(rc)
+
+
+def bob(Q, K, V, dO, gQ, gK, gV, scale=None, out=None, workspace=None, stream=None):
+    """Exact BoB of softmax attention: (gradQ, gradK, gradV, graddO), float32.
+
+    Inputs [B, H, N, d] bf16 or fp32 device tensors; `scale` defaults to
+    1/sqrt(d). `out` (four float32 tensors) and `workspace` (uint8 tensor of
+    at least workspace_bytes(B, H, N, d)) may be given to avoid allocation.
+    """
+    lib = load_library()
+    ins = _inputs(Q, K, V, dO, gQ, gK, gV)
+    B, H, N, d = Q.shape
+    if scale is None:
+        scale = d ** -0.5
+    if out is None:
+        out = tuple(torch.empty((B, H, N, d), dtype=torch.float32, device=Q.device) for _ in range(4))
+    nws = lib.flashbob_workspace_bytes(B, H, N, d)
+    if workspace is None:
+        workspace = torch.empty(max(nws, 1), dtype=torch.uint8, device=Q.device)
+    rc = lib.flashbob_bob(*[_ptr(t) for t in ins], *[_ptr(t) for t in out], B, H, N, d,
+                          ctypes.c_float(scale), _dtype_code(Q.dtype), _ptr(workspace),
+                          ctypes.c_size_t(workspace.numel() * workspace.element_size()),
+                          _stream_handle(Q.device, stream))
+    _check(rc)
+    return tuple(out)
+
+
+def rowstats(Q, K, V, dO, gQ, gK, gV, scale=None, stream=None):
+    """Pass 1 alone: (LSE, D, c, r) per query row, each [B, H, N] float32."""
+    lib = load_library()
+    ins = _inputs(Q, K, V, dO, gQ, gK, gV)
+    B, H, N, d = Q.shape
+    if scale is None:
+        scale = d ** -0.5
+    outs = tuple(torch.empty((B, H, N), dtype=torch.float32, device=Q.device) for _ in range(4))
+    rc = lib.flashbob_rowstats(*[_ptr(t) for t in ins], *[_ptr(t) for t in outs], B, H, N, d,
+                               ctypes.c_float(scale), _dtype_code(Q.dtype),
+                               _stream_handle(Q.device, stream))
+    _check(rc)
+    return outs
+
+
+def raw_bob(ptrs_in, ptrs_out, B, H, N, d, scale, dtype_code, ws_ptr, ws_bytes, stream_ptr=0):
+    """Direct C-ABI call with integer pointers; returns the integer status code."""
+    lib = load_library()
+    return lib.flashbob_bob(*[ctypes.c_void_p(p) for p in ptrs_in], *[ctypes.c_void_p(p) for p in ptrs_out],
+                            B, H, N, d, ctypes.c_float(scale), dtype_code, ctypes.c_void_p(ws_ptr),
+                            ctypes.c_size_t(ws_bytes), ctypes.c_void_p(stream_ptr))

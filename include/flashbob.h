@@ -1,0 +1,133 @@
+/*
+ * flashbob.h - C ABI of the MI355X (gfx950) exact backward-over-backward (BoB)
+ * of softmax attention.
+ *
+ * Method: "FlashBoB: I/O-Efficient Exact Backward-over-Backward for Softmax
+ * Attention" (arXiv 2609.24089), Abstract. BoB is the exact derivative of the
+ * attention first backward; two row-wise scalars fix every output through
+ * affine maps, so the work runs as two tiled passes that never hold an N x N
+ * tensor in device memory.
+ *
+ * Per head (b, h), with s = scale, P = softmax_rows(s Q K^T), O = P V and the
+ * textbook first backward
+ *     dP = dO V^T,  D = rowsum(dO o O),  dS = P o (dP - D),
+ *     dQ = s dS K,  dK = s dS^T Q,  dV = P^T dO,
+ * the library returns the gradients of the scalar
+ *     L = <gQ, dQ> + <gK, dK> + <gV, dV>
+ * with respect to Q, K, V and dO. LSE and D are differentiated through (they
+ * are functions of the inputs). Non-causal, no dropout, no bias, no gradient
+ * for `scale`.
+ *
+ * Conventions shared by every entry point
+ *   - Tensors are contiguous [B, H, N, d] arrays, d fastest, in device memory
+ *     owned by the caller; the library allocates and frees nothing.
+ *   - Inputs are read only. Outputs are fully overwritten. No output may
+ *     overlap an input, the workspace or another output.
+ *   - Every device pointer must be 16-byte aligned.
+ *   - `stream` is a hipStream_t (NULL = the default stream). Work is enqueued
+ *     asynchronously; no host synchronisation happens inside the call and the
+ *     library keeps no state between calls, so calls on different streams
+ *     with disjoint buffers may run concurrently.
+ *   - Supported: d in {64, 128}; N >= 1 (any length, ragged tails masked);
+ *     B, H >= 0 (B*H*N == 0 is a no-op returning FLASHBOB_OK);
+ *     B*H*N*d < 2^62; dtype FLASHBOB_F32 or FLASHBOB_BF16.
+ *   - Errors are negative return codes. Every argument check runs before any
+ *     HIP call, so a rejected call touches no device state. A failed kernel
+ *     launch returns FLASHBOB_ERR_HIP; flashbob_strerror then gives the HIP
+ *     error text of the last failure on the calling thread.
+ */
+#ifndef FLASHBOB_H
+#define FLASHBOB_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  FLASHBOB_F32 = 0,  /* inputs float32; all arithmetic float32 */
+  FLASHBOB_BF16 = 1  /* inputs bfloat16; MFMA operands bf16, accumulation and row scalars float32 */
+} flashbob_dtype;
+
+enum {
+  FLASHBOB_OK = 0,
+  FLASHBOB_ERR_NULL = -1,           /* a required pointer is NULL */
+  FLASHBOB_ERR_SHAPE = -2,          /* negative size, or B*H*N*d too large */
+  FLASHBOB_ERR_UNSUPPORTED_D = -3,  /* d not in {64, 128} */
+  FLASHBOB_ERR_UNSUPPORTED_N = -4,  /* reserved (no N is rejected today besides N < 0) */
+  FLASHBOB_ERR_DTYPE = -5,          /* unknown dtype */
+  FLASHBOB_ERR_ALIGN = -6,          /* a pointer is not 16-byte aligned */
+  FLASHBOB_ERR_WORKSPACE = -7,      /* workspace smaller than flashbob_workspace_bytes */
+  FLASHBOB_ERR_ALIAS = -8,          /* an output overlaps an input, the workspace or another output */
+  FLASHBOB_ERR_SCALE = -9,          /* scale is not finite */
+  FLASHBOB_ERR_HIP = -100           /* a HIP call failed; see flashbob_strerror */
+};
+
+/* Bytes of device workspace flashbob_bob needs: four float32 row-scalar
+ * vectors [B, H, N] (LSE, D, c, r), rounded up to 256 bytes. Returns 0 for
+ * B*H*N == 0 or for invalid (negative) sizes. */
+size_t flashbob_workspace_bytes(int B, int H, int N, int d);
+
+/* Exact BoB (the method's two-pass schedule).
+ *   Q, K, V, dO      [B, H, N, d] inputs of the attention first backward
+ *   gQ, gK, gV       [B, H, N, d] cotangents on its outputs dQ, dK, dV
+ *                    (all seven in `dtype`)
+ *   gradQ, gradK,
+ *   gradV, graddO    [B, H, N, d] float32 outputs: dL/dQ, dL/dK, dL/dV, dL/ddO
+ *   scale            softmax scale s (finite; commonly 1/sqrt(d))
+ *   workspace        device buffer of at least flashbob_workspace_bytes(B,H,N,d)
+ *                    bytes; its contents on entry do not matter and on return
+ *                    hold the row scalars (LSE, D, c, r) as [4][B][H][N] float32.
+ * Pass 1 (one kernel) computes the row scalars of every query and zeroes
+ * gradQ and graddO; pass 2 (one kernel) recomputes the score tiles per key
+ * block and accumulates all four gradients. */
+int flashbob_bob(const void* Q, const void* K, const void* V, const void* dO,
+                 const void* gQ, const void* gK, const void* gV,
+                 float* gradQ, float* gradK, float* gradV, float* graddO,
+                 int B, int H, int N, int d, float scale, int dtype,
+                 void* workspace, size_t workspace_bytes, void* stream);
+
+/* The two halves of flashbob_bob, for callers that time or schedule the
+ * passes separately. Same arguments and checks as flashbob_bob; calling
+ * flashbob_bob_pass1 and then flashbob_bob_pass2 on one stream with the same
+ * buffers is exactly flashbob_bob.
+ *   pass 1: writes the row scalars into `workspace` and zeroes gradQ and
+ *           graddO (gradK, gradV untouched);
+ *   pass 2: reads the row scalars from `workspace`, adds into gradQ and
+ *           graddO (which must hold pass 1's zeros) and writes gradK, gradV. */
+int flashbob_bob_pass1(const void* Q, const void* K, const void* V, const void* dO,
+                       const void* gQ, const void* gK, const void* gV,
+                       float* gradQ, float* gradK, float* gradV, float* graddO,
+                       int B, int H, int N, int d, float scale, int dtype,
+                       void* workspace, size_t workspace_bytes, void* stream);
+int flashbob_bob_pass2(const void* Q, const void* K, const void* V, const void* dO,
+                       const void* gQ, const void* gK, const void* gV,
+                       float* gradQ, float* gradK, float* gradV, float* graddO,
+                       int B, int H, int N, int d, float scale, int dtype,
+                       void* workspace, size_t workspace_bytes, void* stream);
+
+/* Pass 1 alone (row statistics), exported for testing the first pass.
+ * Writes, per query row, LSE (natural-log log-sum-exp of s Q K^T), the
+ * first-backward scalar D = rowsum(dO o O) and the two BoB row scalars
+ *     c = rowsum(P o G),   r = rowsum(dS o G) + rowsum(P o H),
+ * where G = s (gQ K^T + Q gK^T) and H = dO gV^T; each output is [B, H, N]
+ * float32. Inputs as for flashbob_bob. */
+int flashbob_rowstats(const void* Q, const void* K, const void* V, const void* dO,
+                      const void* gQ, const void* gK, const void* gV,
+                      float* lse, float* D, float* c, float* r,
+                      int B, int H, int N, int d, float scale, int dtype,
+                      void* stream);
+
+/* Static description of an error code; for FLASHBOB_ERR_HIP, the HIP error
+ * text of the calling thread's last failure. Never NULL. */
+const char* flashbob_strerror(int code);
+
+/* ABI version (major * 100 + minor). */
+int flashbob_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FLASHBOB_H */

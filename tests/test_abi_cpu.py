@@ -1,0 +1,177 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+that include/flashbob.h declares, and rejects bad arguments with the documented
+error codes before making any HIP call (fake, never-dereferenced pointers)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from exact_second_order_amd import flashbob as fb
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "flashbob.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(fb.LIB_PATH), reason="libflashbob.so not built")
+
+F32, BF16 = fb.FLASHBOB_F32, fb.FLASHBOB_BF16
+OK, NULL, SHAPE, UD, DT, ALIGN, WS, ALIAS, SCALE = 0, -1, -2, -3, -5, -6, -7, -8, -9
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(flashbob_\w+)\s*\(", text)))
+
+
+def test_header_declares_expected_entry_points():
+    assert header_functions() == sorted(fb.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(fb.LIB_PATH)
+    for name in header_functions():
+        assert hasattr(lib, name), name
+
+
+def test_version_and_strerror():
+    lib = fb.load_library()
+    assert lib.flashbob_version() == 100
+    for code in (0, -1, -2, -3, -4, -5, -6, -7, -8, -9, -100, 12345):
+        s = lib.flashbob_strerror(code)
+        assert isinstance(s, bytes) and len(s) > 0
+
+
+def test_workspace_bytes():
+    lib = fb.load_library()
+    assert lib.flashbob_workspace_bytes(1, 1, 128, 64) == 2048
+    assert lib.flashbob_workspace_bytes(1, 4, 65536, 64) == 4 * 4 * 4 * 65536
+    assert lib.flashbob_workspace_bytes(1, 1, 3, 64) == 256  # rounded up
+    assert lib.flashbob_workspace_bytes(0, 1, 128, 64) == 0
+    assert lib.flashbob_workspace_bytes(1, 1, -1, 64) == 0
+
+
+# fake device addresses: 16-byte aligned, disjoint, never dereferenced
+BASE = 1 << 40
+STRIDE = 1 << 32
+
+
+def fake_args(B=1, H=1, N=128, d=64, dtype=F32, scale=0.125, ws=None):
+    ins = [BASE + i * STRIDE for i in range(7)]
+    outs = [BASE + (7 + i) * STRIDE for i in range(4)]
+    wsp = BASE + 11 * STRIDE
+    nws = fb.load_library().flashbob_workspace_bytes(B, H, N, d) if ws is None else ws
+    return ins, outs, B, H, N, d, scale, dtype, wsp, nws
+
+
+def call(ins, outs, B, H, N, d, scale, dtype, wsp, nws):
+    return fb.raw_bob(ins, outs, B, H, N, d, scale, dtype, wsp, nws)
+
+
+@pytest.mark.parametrize("d", [0, 32, 63, 96, 256])
+def test_rejects_unsupported_d(d):
+    a = list(fake_args())
+    a[5] = d
+    assert call(*a) == UD
+
+
+def test_rejects_negative_sizes_and_overflow():
+    for idx in (2, 3, 4):
+        a = list(fake_args())
+        a[idx] = -1
+        assert call(*a) == SHAPE
+    a = list(fake_args(B=1 << 20, H=1 << 10, N=1 << 20, d=128))
+    assert call(*a) == SHAPE
+
+
+def test_rejects_bad_dtype_and_scale():
+    a = list(fake_args())
+    a[7] = 7
+    assert call(*a) == DT
+    for bad in (float("nan"), float("inf"), -float("inf")):
+        a = list(fake_args())
+        a[6] = bad
+        assert call(*a) == SCALE
+
+
+def test_rejects_null_pointers():
+    for k in range(7):
+        a = list(fake_args())
+        a[0] = list(a[0])
+        a[0][k] = 0
+        assert call(*a) == NULL
+    for k in range(4):
+        a = list(fake_args())
+        a[1] = list(a[1])
+        a[1][k] = 0
+        assert call(*a) == NULL
+    a = list(fake_args())
+    a[8] = 0
+    assert call(*a) == NULL
+
+
+def test_rejects_misaligned_pointers():
+    a = list(fake_args())
+    a[0] = list(a[0])
+    a[0][3] += 8
+    assert call(*a) == ALIGN
+    a = list(fake_args())
+    a[1] = list(a[1])
+    a[1][2] += 4
+    assert call(*a) == ALIGN
+
+
+def test_rejects_small_workspace():
+    a = fake_args(ws=1024)
+    assert call(*a) == WS
+
+
+def test_rejects_aliasing_outputs():
+    a = list(fake_args())
+    a[1] = list(a[1])
+    a[1][0] = a[0][0]  # gradQ on top of Q
+    assert call(*a) == ALIAS
+    a = list(fake_args())
+    a[1] = list(a[1])
+    a[1][1] = a[1][0] + 64  # gradK overlaps gradQ
+    assert call(*a) == ALIAS
+    a = list(fake_args())
+    a[8] = a[1][3] + 16  # workspace inside graddO
+    assert call(*a) == ALIAS
+
+
+def test_inputs_may_alias_each_other():
+    # read-only inputs may share memory; the call then fails only because
+    # there is no device here, which must surface as ERR_HIP, not as a
+    # validation error. Skipped when a GPU is present (it would launch).
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("would launch kernels on a real device with fake pointers")
+    a = list(fake_args())
+    a[0] = [a[0][0]] * 7
+    rc = call(*a)
+    assert rc == -100
+
+
+def test_empty_problem_is_a_noop():
+    for B, H, N in ((0, 1, 128), (1, 0, 128), (1, 1, 0)):
+        a = list(fake_args(B=B, H=H, N=N))
+        a[0] = [0] * 7  # even NULL pointers are fine when there is nothing to do
+        a[1] = [0] * 4
+        a[8] = 0
+        assert call(*a) == OK
+
+
+def test_rowstats_validation():
+    lib = fb.load_library()
+    vp = ctypes.c_void_p
+    ins = [vp(BASE + i * STRIDE) for i in range(7)]
+    outs = [vp(BASE + (7 + i) * STRIDE) for i in range(4)]
+    assert lib.flashbob_rowstats(*ins, *outs, 1, 1, 128, 80, ctypes.c_float(0.1), F32, vp(0)) == UD
+    bad = list(outs)
+    bad[2] = vp(0)
+    assert lib.flashbob_rowstats(*ins, *bad, 1, 1, 128, 64, ctypes.c_float(0.1), F32, vp(0)) == NULL
+    bad = list(outs)
+    bad[1] = vp(BASE + 7 * STRIDE + 4)
+    assert lib.flashbob_rowstats(*ins, *bad, 1, 1, 128, 64, ctypes.c_float(0.1), F32, vp(0)) == ALIGN
