@@ -23,8 +23,9 @@ sys.path.insert(0, ROOT)
 
 METRIC = "BoB TFLOP/s + ms/call at N=65536,d=64 (1 MI355X); % of bf16 MFMA peak"
 PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}  # MI355X published dense MFMA peaks
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "pass2_traffic.json")
-KERNEL_SOURCES = ("exact_second_order_amd/csrc/bob_pass2.hip", "exact_second_order_amd/csrc/bob_device.h")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+KERNEL_SOURCES = ("exact_second_order_amd/csrc/bob_query.hip", "exact_second_order_amd/csrc/bob_key.hip",
+                  "exact_second_order_amd/csrc/bob_device.h")
 
 
 def log(*a):
@@ -39,9 +40,9 @@ def kernel_source_hash():
     return h.hexdigest()[:16]
 
 
-def measured_traffic():
-    """HBM bytes per pass-2 launch from committed rocprofv3 counters, if they
-    were taken on the current kernel source; else None."""
+def measured_traffic(stage):
+    """HBM bytes per launch of `stage` from committed rocprofv3 counters, if
+    they were taken on the current kernel sources; else None."""
     try:
         with open(TRAFFIC_FILE) as f:
             t = json.load(f)
@@ -49,7 +50,7 @@ def measured_traffic():
         return None
     if t.get("kernel_source_sha256_16") != kernel_source_hash():
         return None
-    return t.get("bytes_per_launch")
+    return t.get("bytes_per_launch", {}).get(stage)
 
 
 def cpu_baseline(w, rows, block=512):
@@ -85,6 +86,8 @@ def main():
     ap.add_argument("--workload", type=int, default=3, help="index into the workload table")
     ap.add_argument("--cpu-rows", type=int, default=6144, help="oracle sample size (query rows)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-mb", type=int, default=0,
+                    help="run one plain device copy of this many MiB first (calibrates HBM byte counters)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -105,23 +108,35 @@ def main():
     out = tuple(torch.empty(x[0].shape, dtype=torch.float32, device=dev) for _ in range(4))
     ws = torch.empty(fb.workspace_bytes(w.B, w.H, w.N, w.d), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev)
+    if args.copy_mb > 0:
+        src = torch.ones(args.copy_mb << 18, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"[bench] copy calibration: {args.copy_mb} MiB read + {args.copy_mb} MiB written")
+        del src, dst
+
+    stages = list(fb.STAGES)
+    # algorithmic flops of each kernel: its N x N x d products x 2 N^2 d
+    units = {"pass1": 5, "pass2_query": 9, "pass2_key": 8}
+    kernel_names = {"pass1": "query_kernel<.., false>", "pass2_query": "query_kernel<.., true>",
+                    "pass2_key": "key_kernel"}
 
     def step(ev=None):
+        for i, st in enumerate(stages):
+            if ev is not None:
+                ev[i].record(stream)
+            fb.bob_stage(st, *x, out=out, workspace=ws, scale=w.scale)
         if ev is not None:
-            ev[0].record(stream)
-        fb.bob_pass(1, *x, out=out, workspace=ws, scale=w.scale)
-        if ev is not None:
-            ev[1].record(stream)
-        fb.bob_pass(2, *x, out=out, workspace=ws, scale=w.scale)
-        if ev is not None:
-            ev[2].record(stream)
+            ev[len(stages)].record(stream)
 
     log(f"[bench] warmup {args.warmup}")
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
 
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)] for _ in range(args.steps)]
     log(f"[bench] timing {args.steps} steps")
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -130,23 +145,22 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
 
-    p1 = [e[0].elapsed_time(e[1]) for e in evs]
-    p2 = [e[1].elapsed_time(e[2]) for e in evs]
     ms_step = wall * 1e3 / args.steps
     flops = w.flops
     tflops = flops / (ms_step * 1e-3) / 1e12
     peak = PEAK_TFLOPS[w.dtype_name]
-    p1_avg, p2_avg = sum(p1) / len(p1), sum(p2) / len(p2)
-    f1 = 10.0 * w.B * w.H * w.N * w.N * w.d  # algorithmic flops of pass 1 (5 N x N x d products)
-    f2 = 24.0 * w.B * w.H * w.N * w.N * w.d  # pass 2 (12 products)
-    log(f"[bench] ms/step {ms_step:.3f} (events: pass1 {p1_avg:.3f} ms, pass2 {p2_avg:.3f} ms); "
-        f"{tflops:.1f} TFLOP/s = {100 * tflops / peak:.1f}% of {peak} peak")
-    dom = ("bob_pass2_kernel", f2, p2_avg) if p2_avg >= p1_avg else ("rowstats_kernel", f1, p1_avg)
-    achieved = dom[1] / (dom[2] * 1e-3) / 1e12
-    roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
-                "frac": round(achieved / peak, 4),
-                "traffic": measured_traffic() if dom[0] == "bob_pass2_kernel" else None,
-                "kernel": dom[0], "launch_ms": round(dom[2], 4)}
+    per_kernel = {}
+    for i, st in enumerate(stages):
+        ms = sum(e[i].elapsed_time(e[i + 1]) for e in evs) / args.steps
+        kf = 2.0 * units[st] * w.B * w.H * w.N * w.N * w.d
+        per_kernel[st] = {"ms": round(ms, 4), "tflops": round(kf / (ms * 1e-3) / 1e12, 2),
+                          "frac": round(kf / (ms * 1e-3) / 1e12 / peak, 4), "units": units[st]}
+    log(f"[bench] ms/step {ms_step:.3f}; {tflops:.1f} TFLOP/s = {100 * tflops / peak:.1f}% of {peak} peak; "
+        f"kernels {per_kernel}")
+    dom = max(stages, key=lambda st: per_kernel[st]["ms"])
+    roofline = {"bound": "mfma", "achieved": per_kernel[dom]["tflops"], "peak": peak, "unit": "TFLOP/s",
+                "frac": per_kernel[dom]["frac"], "traffic": measured_traffic(dom),
+                "kernel": kernel_names[dom], "launch_ms": per_kernel[dom]["ms"]}
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -170,7 +184,7 @@ def main():
         "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d, "dtype": w.dtype_name,
                    "scale": w.scale, "causal": False, "seed": WORKLOADS.index(w),
                    "flops_per_step": flops, "frac_of_peak": round(tflops / peak, 4),
-                   "pass1_ms": round(p1_avg, 4), "pass2_ms": round(p2_avg, 4)},
+                   "kernels": per_kernel},
         "roofline": roofline,
         "cpu_baseline": cpu,
     }

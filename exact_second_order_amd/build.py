@@ -13,7 +13,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libflashbob.so")
 
-SOURCES = ["flashbob_api.hip", "rowstats.hip", "bob_pass2.hip"]
+SOURCES = ["flashbob_api.hip", "bob_query.hip", "bob_key.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",

@@ -116,6 +116,114 @@ __device__ __forceinline__ f32x8 ld_cols(const float* p, int ld) {
   return v;
 }
 
+// ---------------------------------------------------------------------------
+// Accumulator blocks as MFMA operands.
+//
+// A 32 x 32 accumulator block C (rows = the contraction index of the next
+// product) can feed the next MFMA as its B operand without leaving registers:
+// 16-row chunk cc of C is held by slots 8*cc .. 8*cc+7, and slot s of lane
+// half h is row 16*cc + kperm(h, s). The other operand of that product must
+// present its k index in the same order, which ld_cols_perm does.
+
+__device__ __forceinline__ constexpr int kperm(int h, int s) { return 8 * (s >> 2) + 4 * h + (s & 3); }
+
+// Chunk cc of an accumulator block as an operand fragment (values rounded to
+// the element type).
+__device__ __forceinline__ f32x8 acc_chunk(const f32x16& c, int cc) {
+  return cc == 0 ? __builtin_shufflevector(c, c, 0, 1, 2, 3, 4, 5, 6, 7)
+                 : __builtin_shufflevector(c, c, 8, 9, 10, 11, 12, 13, 14, 15);
+}
+
+__device__ __forceinline__ void acc_to_frag(bf16x8& f, const f32x16& c, int cc) {
+  f = __builtin_convertvector(acc_chunk(c, cc), bf16x8);  // round to nearest even
+}
+
+__device__ __forceinline__ void acc_to_frag(f32x8& f, const f32x16& c, int cc) { f = acc_chunk(c, cc); }
+
+// Eight fp32 values (one accumulator chunk) as an operand fragment.
+__device__ __forceinline__ void to_frag(bf16x8& f, const f32x8& v) { f = __builtin_convertvector(v, bf16x8); }
+__device__ __forceinline__ void to_frag(f32x8& f, const f32x8& v) { f = v; }
+
+// Like ld_cols (storage rows = k), but slot s of lane half h holds storage row
+// kperm(h, s): rows 4h..4h+3 and 8+4h..8+4h+3 of the 16-row chunk.
+__device__ __forceinline__ bf16x8 ld_cols_perm(const bf16* p, int ld) {
+  const int l = lane_id();
+  const int g = l >> 4, j = l & 15;
+  const int col = 16 * (g & 1) + 4 * (j & 3);
+  const int krow = 4 * (g >> 1) + (j >> 2);
+  const bf16* a0 = p + krow * ld + col;
+  const bf16* a1 = a0 + 8 * ld;
+  typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(a0));
+  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(a1));
+  const s16x8 v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  return __builtin_bit_cast(bf16x8, v);
+}
+
+__device__ __forceinline__ f32x8 ld_cols_perm(const float* p, int ld) {
+  const int l = lane_id();
+  const int h = l >> 5;
+  const float* q = p + (l & 31);
+  f32x8 v;
+#pragma unroll
+  for (int s = 0; s < 8; ++s) v[s] = q[kperm(h, s) * ld];
+  return v;
+}
+
+// ---------------------------------------------------------------------------
+// Swizzled 32 x 64 bf16 stage tiles (128-byte rows, no padding).
+//
+// The 16-byte chunk c of row r is stored at chunk position c ^ swz(r). swz
+// gives rows of equal parity 8 distinct positions (so 16 lanes reading one
+// column chunk of 16 rows hit 64 distinct banks) and puts rows r and r + 2 in
+// different 64-byte halves (so the 4-row x 32-byte footprint of a transpose
+// read is conflict free as well).
+
+__device__ __forceinline__ constexpr int swz(int r) { return (((r >> 1) & 1) << 2) | ((r >> 2) & 3); }
+
+__device__ __forceinline__ const bf16* sw_addr(const bf16* t, int row, int col) {
+  return t + row * 64 + 8 * ((col >> 3) ^ swz(row)) + (col & 7);
+}
+
+// ld_rows on a swizzled tile: lane reads row row0 + l%32 at k = 16*c16 + kmap.
+__device__ __forceinline__ bf16x8 ld_rows_sw(const bf16* t, int row0, int c16) {
+  const int l = lane_id();
+  return *reinterpret_cast<const bf16x8*>(sw_addr(t, row0 + (l & 31), 16 * c16 + 8 * (l >> 5)));
+}
+
+// ld_cols_perm on a swizzled tile: storage rows krow0 .. krow0+15 are k (in
+// kperm order), lane reads column col0 + l%32.
+__device__ __forceinline__ bf16x8 ld_cols_perm_sw(const bf16* t, int krow0, int col0) {
+  const int l = lane_id();
+  const int g = l >> 4, j = l & 15;
+  const int col = col0 + 16 * (g & 1) + 4 * (j & 3);
+  const int kr = krow0 + 4 * (g >> 1) + (j >> 2);
+  typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)sw_addr(t, kr, col));
+  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)sw_addr(t, kr + 8, col));
+  const s16x8 v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  return __builtin_bit_cast(bf16x8, v);
+}
+
+// Direct global -> LDS copy of a 32 x 64 bf16 tile into swizzled layout, one
+// global_load_lds_dwordx4 per wave: wave w fills rows 8w .. 8w+7 (the
+// hardware writes lane L's 16 bytes at LDS chunk L of the wave's window, so
+// lane L fetches the global chunk that belongs there). Rows at or past
+// `nvalid` (>= 1) re-read row nvalid-1: every address stays inside the source,
+// and callers mask those rows.
+__device__ __forceinline__ void load_tile_sw(bf16* t, const bf16* src, int nvalid) {
+  const int l = lane_id(), w = wave_id();
+  const int row = 8 * w + (l >> 3);
+  const int c = (l & 7) ^ swz(row);
+  const int srow = row < nvalid ? row : nvalid - 1;
+  typedef __attribute__((address_space(3))) void lds_void;
+  __builtin_amdgcn_global_load_lds((const void*)(src + srow * 64 + 8 * c), (lds_void*)(t + 8 * w * 64), 16, 0,
+                                   0);
+}
+
+// Wait for this wave's outstanding global loads, including direct-to-LDS ones.
+__device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
 // Store four consecutive elements (one accumulator slot group) to LDS.
 __device__ __forceinline__ void st4(bf16* p, float a, float b, float c, float d) {
   bf16x4 v;
@@ -150,6 +258,37 @@ __device__ __forceinline__ void copy_rows_to_lds(T* dst, int ldd, const T* src, 
     *reinterpret_cast<v4i*>(dst + r * ldd + cv * VEC) = v;
   }
 }
+
+// Register-staged copy of a [ROWS][COLS] row block (16 bytes per lane per
+// step): load() issues the global reads early, store() writes LDS later, so
+// the global latency hides behind the work done in between.
+template <typename T, int ROWS, int COLS, int NTHREADS>
+struct RowPrefetch {
+  static constexpr int VEC = 16 / sizeof(T);
+  static constexpr int VPR = COLS / VEC;
+  static constexpr int NIT = ROWS * VPR / NTHREADS;  // ROWS = 0: unused placeholder
+  static_assert((ROWS * VPR) % NTHREADS == 0, "copy must split evenly over the workgroup");
+  typedef __attribute__((__vector_size__(16))) int v4i;
+  v4i r[NIT > 0 ? NIT : 1];
+
+  __device__ __forceinline__ void load(const T* src, int nrows_valid) {
+#pragma unroll
+    for (int it = 0; it < NIT; ++it) {
+      const int idx = it * NTHREADS + (int)threadIdx.x;
+      const int row = idx / VPR, cv = idx % VPR;
+      r[it] = v4i{0, 0, 0, 0};
+      if (row < nrows_valid) r[it] = *reinterpret_cast<const v4i*>(src + (size_t)row * COLS + cv * VEC);
+    }
+  }
+  __device__ __forceinline__ void store(T* dst, int ldd) const {
+#pragma unroll
+    for (int it = 0; it < NIT; ++it) {
+      const int idx = it * NTHREADS + (int)threadIdx.x;
+      const int row = idx / VPR, cv = idx % VPR;
+      *reinterpret_cast<v4i*>(dst + row * ldd + cv * VEC) = r[it];
+    }
+  }
+};
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 

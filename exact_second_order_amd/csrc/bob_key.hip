@@ -1,0 +1,387 @@
+// Key-major kernel of the BoB schedule: the key side of pass 2 (gradK, gradV).
+//
+// FlashBoB (arXiv 2609.24089), Abstract: with the two row scalars known from
+// the first pass, every output is an affine map of recomputed tiles. For the
+// key-side outputs, per (query i, key j):
+//   P = exp(s S - LSE),  dS = P (dP - D),  A = P (G - c),
+//   dS2 = dS (G - c) + P (H - r),
+//   gradK_j = s sum_i (dS2_ij Q_i + dS_ij gQ_i),   gradV_j = sum_i A_ij dO_i,
+// with S = Q K^T, dP = dO V^T, G = s (gQ K^T + Q gK^T), H = dO gV^T.
+//
+// gfx950 schedule: a workgroup of 4 waves owns 128 keys (32 per wave) and
+// streams the queries (Q, gQ, dO and their row scalars) in 32-row stages
+// through LDS buffers, issuing each stage's global reads one or two stages
+// ahead (software pipelined like the query-major kernel). Per 32-query block a wave builds S, G, dP, H (queries x its keys)
+// with MFMA, so each lane holds one key and 16 queries; the queries' row
+// scalars come from LDS as broadcast reads. P, dS, dS2, A then feed the next
+// MFMAs straight from the accumulator registers as B operands (k = queries in
+// accumulator row order), against Q^T, gQ^T, dO^T read from the LDS stage with
+// transpose loads in the same order. gradK^T and gradV^T stay in registers for
+// the whole sweep.
+
+#include <type_traits>
+
+#include "bob_device.h"
+
+namespace flashbob {
+
+template <typename T, int D_>
+struct KeyCfg {
+  static constexpr int D = D_;
+  static constexpr int BC = 128;                       // keys per workgroup (4 waves x 32)
+  static constexpr int BQ = 32;                        // queries per LDS stage (one MFMA block)
+  static constexpr int LDQ = D + 16 / (int)sizeof(T);  // padded LDS row (elements)
+  static constexpr int NCH = D / 16, NDB = D / 32;
+  // same pipelining and staging choices as the query-major kernel
+  static constexpr bool PIPE = sizeof(T) == 2 && D == 64;
+  static constexpr bool SWZ = PIPE;
+  static constexpr int NBUF = PIPE ? 4 : 2;
+  static constexpr int AHEAD = PIPE ? 2 : 1;
+  static constexpr int ROWLEN = SWZ ? D : LDQ;
+  static constexpr int QSTAGE = 3 * BQ * ROWLEN;       // Q, gQ, dO elements of one stage
+  static constexpr int SSTAGE = 4 * BQ;                // row scalars of one stage (floats)
+  static constexpr size_t LDS_BYTES = NBUF * (QSTAGE * sizeof(T) + SSTAGE * sizeof(float));
+  static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
+};
+
+__device__ __forceinline__ bf16x8 load_key_frag(const bf16* row, bool valid, int c) {
+  bf16x8 f = {};
+  if (valid) f = *reinterpret_cast<const bf16x8*>(row + 16 * c + 8 * (lane_id() >> 5));
+  return f;
+}
+
+__device__ __forceinline__ f32x8 load_key_frag(const float* row, bool valid, int c) {
+  f32x8 f = {};
+  const int h = lane_id() >> 5;
+  if (valid) {
+#pragma unroll
+    for (int s = 0; s < 8; ++s) f[s] = row[16 * c + Elem<float>::kmap(h, s)];
+  }
+  return f;
+}
+
+// Elementwise step of 16-query chunk cc of a 32-query block (slot i <-> query
+// row acc_row(h, i), lane <-> key), turned into B operands with k = queries.
+// TAIL zeroes P for keys past the sequence end and for query rows at or past
+// nq_rel.
+template <typename T, bool TAIL>
+__device__ __forceinline__ void key_chunk(int cc, const f32x16& S, const f32x16& G, const f32x16& dP,
+                                          const f32x16& H, const float* sl, const float* sd, const float* sc,
+                                          const float* sr, float sl2, float scale, bool kvalid, int nq_rel,
+                                          typename Elem<T>::frag& fdS, typename Elem<T>::frag& fdS2,
+                                          typename Elem<T>::frag& fA) {
+  const int h = lane_id() >> 5;
+  f32x8 dS, dS2, A;
+#pragma unroll
+  for (int gg = 0; gg < 2; ++gg) {
+    const int g = 2 * cc + gg;
+    const int r0 = 8 * g + 4 * h;  // this lane-half's 4 consecutive query rows
+    const f32x4 L4 = *reinterpret_cast<const f32x4*>(sl + r0);
+    const f32x4 D4 = *reinterpret_cast<const f32x4*>(sd + r0);
+    const f32x4 C4 = *reinterpret_cast<const f32x4*>(sc + r0);
+    const f32x4 R4 = *reinterpret_cast<const f32x4*>(sr + r0);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int i = 4 * g + e, s = 4 * gg + e;
+      float p = fast_exp2(fmaf(S[i], sl2, -L4[e]));
+      if (TAIL && (!kvalid || r0 + e >= nq_rel)) p = 0.f;
+      const float ds = p * (dP[i] - D4[e]);
+      const float gv = fmaf(G[i], scale, -C4[e]);
+      dS[s] = ds;
+      A[s] = p * gv;
+      dS2[s] = fmaf(ds, gv, p * (H[i] - R4[e]));
+    }
+  }
+  to_frag(fdS, dS);
+  to_frag(fdS2, dS2);
+  to_frag(fA, A);
+}
+
+template <typename T, int D>
+__global__ __launch_bounds__(256, 1) void key_kernel(
+    const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V, const T* __restrict__ dO,
+    const T* __restrict__ gQ, const T* __restrict__ gK, const T* __restrict__ gV,
+    const float* __restrict__ lse2, const float* __restrict__ Dv, const float* __restrict__ cv,
+    const float* __restrict__ rv, float* __restrict__ gradK, float* __restrict__ gradV, int N, int nkblk,
+    float scale) {
+  using Cfg = KeyCfg<T, D>;
+  using E = Elem<T>;
+  using F = typename E::frag;
+  constexpr int BQ = Cfg::BQ, LDQ = Cfg::LDQ, NCH = Cfg::NCH, NDB = Cfg::NDB, NBUF = Cfg::NBUF;
+  constexpr int ROWLEN = Cfg::ROWLEN;
+  constexpr bool PIPE = Cfg::PIPE, SWZ = Cfg::SWZ;
+  // [NBUF][3][BQ][ROWLEN] Q, gQ, dO rows, then [NBUF][4][BQ] row scalars.
+  // (Addresses are always formed from the __shared__ array itself so that
+  // they stay LDS addresses.)
+  __shared__ __attribute__((aligned(16))) char smem[Cfg::LDS_BYTES];
+  auto tile = [&](int b, int t) __attribute__((always_inline)) { return reinterpret_cast<T*>(smem) + (b * 3 + t) * BQ * ROWLEN; };
+  auto sQ = [&](int b, int t, int row, int col) __attribute__((always_inline)) { return tile(b, t) + row * ROWLEN + col; };
+  auto sS = [&](int b, int t) __attribute__((always_inline)) {
+    return reinterpret_cast<float*>(smem + NBUF * Cfg::QSTAGE * sizeof(T)) + (b * 4 + t) * BQ;
+  };
+  auto lds_rows = [&](int b, int t, int c16) __attribute__((always_inline)) -> F {
+    if constexpr (SWZ) return ld_rows_sw(tile(b, t), 0, c16);
+    else return ld_rows(sQ(b, t, 0, 16 * c16), LDQ);
+  };
+  auto lds_cols = [&](int b, int t, int krow0, int col0) __attribute__((always_inline)) -> F {
+    if constexpr (SWZ) return ld_cols_perm_sw(tile(b, t), krow0, col0);
+    else return ld_cols_perm(sQ(b, t, krow0, col0), LDQ);
+  };
+
+  const int head = blockIdx.x / nkblk;
+  const int kblk = blockIdx.x % nkblk;
+  const size_t hoff = (size_t)head * N * D;
+  const size_t soff = (size_t)head * N;
+  const int w = wave_id(), l = lane_id(), h = l >> 5, col = l & 31;
+  const int key = kblk * Cfg::BC + 32 * w + col;  // this lane's key
+  const bool kvalid = key < N;
+  const bool ktail = kblk * Cfg::BC + Cfg::BC > N;
+
+  // B operands of the wave's 32 keys (lane <-> key, k over d)
+  F bK[NCH], bgK[NCH], bV[NCH], bgV[NCH];
+  {
+    const size_t ro = hoff + (size_t)key * D;
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+      bK[c] = load_key_frag(K + ro, kvalid, c);
+      bgK[c] = load_key_frag(gK + ro, kvalid, c);
+      bV[c] = load_key_frag(V + ro, kvalid, c);
+      bgV[c] = load_key_frag(gV + ro, kvalid, c);
+    }
+  }
+  // gradK^T, gradV^T: d rows x the wave's 32 keys
+  f32x16 accK[NDB], accV[NDB];
+#pragma unroll
+  for (int j = 0; j < NDB; ++j) {
+    accK[j] = f32x16{};
+    accV[j] = f32x16{};
+  }
+  const float sl2 = scale * kLog2e;
+  const int nblk = (N + BQ - 1) / BQ;  // 32-query blocks = stages
+
+  // staging of stage n (Q, gQ, dO rows and their row scalars)
+  RowPrefetch<T, SWZ ? 0 : BQ, D, 256> pq, pg, pd;
+  float pstat = 0.f;
+  auto prefetch = [&](int n) __attribute__((always_inline)) {
+    const int q0 = n * BQ;
+    const int nq = min(BQ, N - q0);
+    if constexpr (SWZ) {
+      const int b = n % NBUF;
+      load_tile_sw(tile(b, 0), Q + hoff + (size_t)q0 * D, nq);
+      load_tile_sw(tile(b, 1), gQ + hoff + (size_t)q0 * D, nq);
+      load_tile_sw(tile(b, 2), dO + hoff + (size_t)q0 * D, nq);
+      if (w < 2) {
+        // waves 0 and 1 fetch (LSE*log2e, D) and (c, r): lane L -> array
+        // 2w + L/32, row L%32, written at LDS float L of the wave's window
+        const int a = 2 * w + (l >> 5), i = l & 31;
+        const float* arr = a == 0 ? lse2 : a == 1 ? Dv : a == 2 ? cv : rv;
+        const size_t o = soff + q0 + (i < nq ? i : nq - 1);
+        typedef __attribute__((address_space(3))) void lds_void;
+        __builtin_amdgcn_global_load_lds((const void*)(arr + o), (lds_void*)(sS(b, 0) + 64 * w), 4, 0, 0);
+      }
+    } else {
+      pq.load(Q + hoff + (size_t)q0 * D, nq);
+      pg.load(gQ + hoff + (size_t)q0 * D, nq);
+      pd.load(dO + hoff + (size_t)q0 * D, nq);
+      if ((int)threadIdx.x < 4 * BQ) {
+        const int t = threadIdx.x / BQ, i = threadIdx.x % BQ;
+        const bool ok = i < nq;
+        const size_t o = soff + q0 + i;
+        // queries past the end get LSE = +inf, hence P = 0
+        if (t == 0) pstat = ok ? lse2[o] : INFINITY;
+        else if (t == 1) pstat = ok ? Dv[o] : 0.f;
+        else if (t == 2) pstat = ok ? cv[o] : 0.f;
+        else pstat = ok ? rv[o] : 0.f;
+      }
+    }
+  };
+  auto commit = [&](int n) __attribute__((always_inline)) {
+    if constexpr (SWZ) {
+      wait_vmem();
+    } else {
+      const int b = n % NBUF;
+      pq.store(sQ(b, 0, 0, 0), LDQ);
+      pg.store(sQ(b, 1, 0, 0), LDQ);
+      pd.store(sQ(b, 2, 0, 0), LDQ);
+      if ((int)threadIdx.x < 4 * BQ) sS(b, threadIdx.x / BQ)[threadIdx.x % BQ] = pstat;
+    }
+  };
+
+  struct Tiles {
+    f32x16 S, G, dP, H;
+  };
+  // d-chunks [c0, c1) of S, G, dP, H of query block n (queries x this wave's keys)
+  auto recompute = [&](int n, Tiles& t, int c0, int c1) __attribute__((always_inline)) {
+    const int b = n % NBUF;
+    if (c0 == 0) {
+      t.S = f32x16{};
+      t.G = f32x16{};
+      t.dP = f32x16{};
+      t.H = f32x16{};
+    }
+#pragma unroll
+    for (int c = c0; c < c1; ++c) {
+      const F aq = lds_rows(b, 0, c);  // lane <-> query, k over d
+      const F agq = lds_rows(b, 1, c);
+      const F ado = lds_rows(b, 2, c);
+      E::mma(t.S, aq, bK[c]);
+      E::mma(t.G, agq, bK[c]);
+      E::mma(t.G, aq, bgK[c]);
+      E::mma(t.dP, ado, bV[c]);
+      E::mma(t.H, ado, bgV[c]);
+    }
+  };
+  struct Frags {
+    F dS[2], dS2[2], A[2];
+  };
+  // TAIL: masks keys past the end (the whole sweep of the last key block)
+  // and query rows past the end (last query block)
+  auto elementwise = [&](auto tail, int n, int cc, const Tiles& t, Frags& f) __attribute__((always_inline)) {
+    constexpr bool TAIL = decltype(tail)::value;
+    const int b = n % NBUF;
+    key_chunk<T, TAIL>(cc, t.S, t.G, t.dP, t.H, sS(b, 0), sS(b, 1), sS(b, 2), sS(b, 3), sl2, scale, kvalid,
+                       N - n * BQ, f.dS[cc], f.dS2[cc], f.A[cc]);
+  };
+  auto outputs = [&](int n, int cc, const Frags& f) __attribute__((always_inline)) {
+    const int b = n % NBUF;
+#pragma unroll
+    for (int j = 0; j < NDB; ++j) {
+      // lane <-> d, k over this chunk's queries (accumulator row order)
+      const F tQ = lds_cols(b, 0, 16 * cc, 32 * j);
+      const F tgQ = lds_cols(b, 1, 16 * cc, 32 * j);
+      const F tdO = lds_cols(b, 2, 16 * cc, 32 * j);
+      E::mma(accK[j], tQ, f.dS2[cc]);
+      E::mma(accK[j], tgQ, f.dS[cc]);
+      E::mma(accV[j], tdO, f.A[cc]);
+    }
+  };
+
+#pragma unroll
+  for (int n = 0; n < Cfg::AHEAD; ++n) {
+    if (n < nblk) {
+      prefetch(n);
+      commit(n);
+    }
+  }
+  __syncthreads();
+
+  using F0 = std::integral_constant<bool, false>;
+  using F1 = std::integral_constant<bool, true>;
+  const bool last_partial = N % BQ != 0;
+  if constexpr (PIPE) {
+    Tiles tA, tB;
+    Frags fA, fB;
+    recompute(0, tA, 0, NCH);
+    // iteration n: recompute n+1 (MFMA), elementwise n (VALU), outputs n-1
+    // (MFMA), as two fenced phases; branch-free in the steady state
+    // (1 <= n <= nblk-3)
+    auto body = [&](auto steady, auto tail, int n, Tiles& cur, Tiles& nxt, Frags& fcur, Frags& fprev) __attribute__((always_inline)) {
+      constexpr bool STEADY = decltype(steady)::value;
+      const bool pf = STEADY || n + 2 < nblk;
+      const bool rec = STEADY || n + 1 < nblk;
+      const bool out = STEADY || n >= 1;
+      if (pf) prefetch(n + 2);  // its buffer last held stage n-2, read in iteration n-1
+#pragma unroll
+      for (int ph = 0; ph < 2; ++ph) {
+        if (rec) recompute(n + 1, nxt, ph * NCH / 2, (ph + 1) * NCH / 2);
+        elementwise(tail, n, ph, cur, fcur);
+        if (out) outputs(n - 1, ph, fprev);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      if (pf) commit(n + 2);
+      __syncthreads();
+    };
+    auto edge = [&](int n, Tiles& cur, Tiles& nxt, Frags& fcur, Frags& fprev) __attribute__((always_inline)) {
+      if (ktail || (n == nblk - 1 && last_partial))
+        body(F0{}, F1{}, n, cur, nxt, fcur, fprev);
+      else
+        body(F0{}, F0{}, n, cur, nxt, fcur, fprev);
+    };
+    edge(0, tA, tB, fA, fB);
+    int n = 1;
+    if (ktail) {
+      for (; n + 3 < nblk; n += 2) {
+        body(F1{}, F1{}, n, tB, tA, fB, fA);
+        body(F1{}, F1{}, n + 1, tA, tB, fA, fB);
+      }
+    } else {
+      for (; n + 3 < nblk; n += 2) {
+        body(F1{}, F0{}, n, tB, tA, fB, fA);
+        body(F1{}, F0{}, n + 1, tA, tB, fA, fB);
+      }
+    }
+    for (; n < nblk; ++n) {
+      if (n & 1)
+        edge(n, tB, tA, fB, fA);
+      else
+        edge(n, tA, tB, fA, fB);
+    }
+#pragma unroll
+    for (int cc = 0; cc < 2; ++cc) {
+      if ((nblk - 1) & 1)
+        outputs(nblk - 1, cc, fB);
+      else
+        outputs(nblk - 1, cc, fA);
+    }
+  } else {
+    Tiles t;
+    Frags f;
+    for (int n = 0; n < nblk; ++n) {
+      const bool pf = n + 1 < nblk;
+      if (pf) prefetch(n + 1);
+      recompute(n, t, 0, NCH);
+#pragma unroll
+      for (int cc = 0; cc < 2; ++cc) {
+        if (ktail || (n == nblk - 1 && last_partial))
+          elementwise(F1{}, n, cc, t, f);
+        else
+          elementwise(F0{}, n, cc, t, f);
+        outputs(n, cc, f);
+      }
+      if (pf) commit(n + 1);  // its buffer last held stage n-1, read in iteration n-1
+      __syncthreads();
+    }
+  }
+
+  // accK[j] slot i holds d = 32 j + acc_row(h, i) of this lane's key
+  if (kvalid) {
+    float* gk = gradK + hoff + (size_t)key * D;
+    float* gv = gradV + hoff + (size_t)key * D;
+#pragma unroll
+    for (int j = 0; j < NDB; ++j) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int d0 = 32 * j + 8 * g + 4 * h;
+        *reinterpret_cast<float4*>(gk + d0) = make_float4(scale * accK[j][4 * g], scale * accK[j][4 * g + 1],
+                                                          scale * accK[j][4 * g + 2], scale * accK[j][4 * g + 3]);
+        *reinterpret_cast<float4*>(gv + d0) =
+            make_float4(accV[j][4 * g], accV[j][4 * g + 1], accV[j][4 * g + 2], accV[j][4 * g + 3]);
+      }
+    }
+  }
+}
+
+template <typename T, int D>
+hipError_t launch_key(const void* Q, const void* K, const void* V, const void* dO, const void* gQ, const void* gK,
+                      const void* gV, const float* lse2, const float* Dv, const float* cv, const float* rv,
+                      float* gradK, float* gradV, int BH, int N, float scale, hipStream_t stream) {
+  using Cfg = KeyCfg<T, D>;
+  const int nkblk = (N + Cfg::BC - 1) / Cfg::BC;
+  const long long nblocks = (long long)nkblk * BH;
+  if (nblocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  key_kernel<T, D><<<dim3((unsigned)nblocks), dim3(256), 0, stream>>>(
+      (const T*)Q, (const T*)K, (const T*)V, (const T*)dO, (const T*)gQ, (const T*)gK, (const T*)gV, lse2, Dv, cv,
+      rv, gradK, gradV, N, nkblk, scale);
+  return hipGetLastError();
+}
+
+#define FLASHBOB_INST_KEY(T, D)                                                                            \
+  template hipError_t launch_key<T, D>(const void*, const void*, const void*, const void*, const void*,   \
+                                       const void*, const void*, const float*, const float*, const float*, \
+                                       const float*, float*, float*, int, int, float, hipStream_t);
+FLASHBOB_INST_KEY(bf16, 64)
+FLASHBOB_INST_KEY(bf16, 128)
+FLASHBOB_INST_KEY(float, 64)
+FLASHBOB_INST_KEY(float, 128)
+
+}  // namespace flashbob

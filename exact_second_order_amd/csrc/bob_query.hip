@@ -1,0 +1,514 @@
+// Query-major kernels of the BoB schedule: pass 1 (row scalars) and the
+// query side of pass 2 (gradQ, graddO). Both sweep the whole key sequence for
+// a block of queries, so they share one kernel template.
+//
+// FlashBoB (arXiv 2609.24089), Abstract: two row-wise scalars fix every BoB
+// output through affine maps; a first pass gathers them, a second pass
+// recomputes the score tiles (FlashAttention-style recomputation) and turns
+// them into the outputs, never holding an N x N tensor off chip.
+//
+// With S = Q K^T, P = exp(s S - LSE), dP = dO V^T, G = s (gQ K^T + Q gK^T),
+// H = dO gV^T:
+//   pass 1:  D = rowsum(P o dP),  c = rowsum(P o G),
+//            r = rowsum(dS o G) + rowsum(P o H),  dS = P o (dP - D).
+//            One sweep with an online running max m: accumulate
+//            l = sum Pt, aD = sum Pt dP, ac = sum Pt G, ae = sum Pt dP G,
+//            ah = sum Pt H (Pt = exp(s S - m)), then D = aD/l, c = ac/l,
+//            r = ae/l - D c + ah/l, LSE = m + ln l.
+//   pass 2q: dS  = P (dP - D),  A = P (G - c),  dS2 = dS (G - c) + P (H - r),
+//            gradQ = s (dS2 K + dS gK),  graddO = A V + P gV.
+//
+// gfx950 schedule: a workgroup of 4 waves owns 128 queries (32 per wave) and
+// streams the keys in 32-row stages (K, gK, V, gV) through LDS buffers, with
+// each stage's global reads issued into registers one or two stages ahead. Per 32-key block a wave builds the transposed tiles S^T, G^T,
+// dP^T, H^T (keys x its queries) with MFMA; the accumulator layout then puts
+// one query per lane, so the row scalars are per-lane registers. In pass 2q
+// the elementwise results (P, dS, dS2, A) go straight from the accumulator
+// registers into the next MFMAs as B operands (k = keys, in the accumulator's
+// row order); the A operands K^T, gK^T, V^T, gV^T come from the LDS stage via
+// transpose reads in the same k order. gradQ^T and graddO^T stay in registers
+// for the whole sweep: no atomics, no cross-wave reduction.
+
+#include <type_traits>
+
+#include "bob_device.h"
+
+namespace flashbob {
+
+template <typename T, int D_, bool GRADQ>
+struct QueryCfg {
+  static constexpr int D = D_;
+  static constexpr int BQ = 128;                       // queries per workgroup (4 waves x 32)
+  static constexpr int BK = 32;                        // keys per LDS stage (one MFMA block)
+  static constexpr int LDK = D + 16 / (int)sizeof(T);  // padded LDS row (elements)
+  static constexpr int NCH = D / 16;                   // 16-wide k chunks over d
+  static constexpr int NDB = D / 32;                   // 32-row blocks of d
+  // Software pipelining (bf16, d = 64): iteration n recomputes block n+1,
+  // does the elementwise work of block n and the output products of block
+  // n-1, so MFMA and VALU streams are independent; four stage buffers (n-1
+  // .. n+2) are live. Otherwise one block per iteration, two buffers.
+  static constexpr bool PIPE = sizeof(T) == 2 && D == 64;
+  // The pipelined variant stages tiles with direct global->LDS loads into
+  // swizzled unpadded rows (no staging registers); the others stage through
+  // registers into padded rows.
+  static constexpr bool SWZ = PIPE;
+  static constexpr int NBUF = PIPE ? 4 : 2;
+  static constexpr int AHEAD = PIPE ? 2 : 1;           // prefetch distance in stages
+  static constexpr int STAGE = 4 * BK * (SWZ ? D : LDK);  // elements of one stage
+  static constexpr size_t LDS_BYTES = NBUF * STAGE * sizeof(T);
+  static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
+};
+
+// One fragment (16 k values of d) of a row held by this lane; zero for rows
+// past the sequence end.
+__device__ __forceinline__ bf16x8 load_row_frag(const bf16* row, bool valid, int c) {
+  bf16x8 f = {};
+  if (valid) f = *reinterpret_cast<const bf16x8*>(row + 16 * c + 8 * (lane_id() >> 5));
+  return f;
+}
+
+__device__ __forceinline__ f32x8 load_row_frag(const float* row, bool valid, int c) {
+  f32x8 f = {};
+  const int h = lane_id() >> 5;
+  if (valid) {
+#pragma unroll
+    for (int s = 0; s < 8; ++s) f[s] = row[16 * c + Elem<float>::kmap(h, s)];
+  }
+  return f;
+}
+
+// ---------------------------------------------------------------------------
+// pass 1 running sums of one lane (one query, the keys of its half-wave).
+// Level-1 sums are scaled to the current running max m and absorb one 32-key
+// block at a time (block sums first); every kFlush blocks they move into
+// level-2 sums kept at their own max m2 (every two blocks in the pipelined
+// loop, every kFlush blocks otherwise). At 262144 keys this keeps every fp32
+// chain at a few thousand additions at most instead of 131072.
+struct OnlineSums {
+  float m = -INFINITY, l = 0.f, aD = 0.f, ac = 0.f, ae = 0.f, ah = 0.f;
+  float m2 = -INFINITY, l2 = 0.f, aD2 = 0.f, ac2 = 0.f, ae2 = 0.f, ah2 = 0.f;
+
+  __device__ __forceinline__ void flush() {
+    const float mu = (m == -INFINITY) ? 0.f : m;
+    const float c2 = fast_exp2(m2 - mu);
+    l2 = fmaf(l2, c2, l);
+    aD2 = fmaf(aD2, c2, aD);
+    ac2 = fmaf(ac2, c2, ac);
+    ae2 = fmaf(ae2, c2, ae);
+    ah2 = fmaf(ah2, c2, ah);
+    m2 = m;
+    l = aD = ac = ae = ah = 0.f;
+  }
+};
+
+constexpr int kFlush = 64;  // blocks per level-1 chain
+
+// Online accumulation of one 32-key block (per lane: 16 keys of one query),
+// in two calls: chunk 0 first takes the block maximum and rescales, then each
+// chunk adds its 8 keys. In the TAIL variant keys at relative index
+// >= nvalid_rel are masked out.
+template <bool TAIL>
+__device__ __forceinline__ void online_chunk(int cc, const f32x16& S, const f32x16& G, const f32x16& dP,
+                                             const f32x16& H, float sl2, bool pos_scale, int nvalid_rel,
+                                             OnlineSums& st, float& mu) {
+  const int h = lane_id() >> 5;
+  if (cc == 0) {
+    // block extreme of the raw score (the max of s*S is s*max S for s >= 0,
+    // s*min S otherwise)
+    float ext = pos_scale ? -INFINITY : INFINITY;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const bool ok = !TAIL || acc_row(h, i) < nvalid_rel;
+      if (ok) ext = pos_scale ? fmaxf(ext, S[i]) : fminf(ext, S[i]);
+    }
+    const float mb = (ext == INFINITY || ext == -INFINITY) ? -INFINITY : ext * sl2;
+    const float mn = fmaxf(st.m, mb);
+    mu = (mn == -INFINITY) ? 0.f : mn;
+    const float alpha = fast_exp2(st.m - mu);
+    st.l *= alpha;
+    st.aD *= alpha;
+    st.ac *= alpha;
+    st.ae *= alpha;
+    st.ah *= alpha;
+    st.m = mn;
+  }
+  float bl = 0.f, bD = 0.f, bc = 0.f, be = 0.f, bh = 0.f;
+#pragma unroll
+  for (int s = 0; s < 8; ++s) {
+    const int i = 8 * cc + s;
+    float p = fast_exp2(fmaf(S[i], sl2, -mu));
+    if (TAIL && acc_row(h, i) >= nvalid_rel) p = 0.f;
+    const float t = p * dP[i];
+    bl += p;
+    bD += t;
+    bc = fmaf(p, G[i], bc);
+    be = fmaf(t, G[i], be);
+    bh = fmaf(p, H[i], bh);
+  }
+  st.l += bl;
+  st.aD += bD;
+  st.ac += bc;
+  st.ae += be;
+  st.ah += bh;
+}
+
+// pass 2q elementwise step of one 16-key chunk cc of a 32-key block, turned
+// into B operands (k = keys in accumulator row order). TAIL masks keys at
+// relative index >= nvalid_rel.
+template <typename T, bool TAIL>
+__device__ __forceinline__ void query_chunk(int cc, const f32x16& S, const f32x16& G, const f32x16& dP,
+                                            const f32x16& H, float sl2, float scale, float l2, float Dq,
+                                            float cq, float rq, int nvalid_rel, typename Elem<T>::frag& fP,
+                                            typename Elem<T>::frag& fdS, typename Elem<T>::frag& fdS2,
+                                            typename Elem<T>::frag& fA) {
+  const int h = lane_id() >> 5;
+  f32x8 P, dS, dS2, A;
+#pragma unroll
+  for (int s = 0; s < 8; ++s) {
+    const int i = 8 * cc + s;
+    float p = fast_exp2(fmaf(S[i], sl2, -l2));
+    if (TAIL && acc_row(h, i) >= nvalid_rel) p = 0.f;
+    const float ds = p * (dP[i] - Dq);
+    const float g = fmaf(G[i], scale, -cq);
+    P[s] = p;
+    dS[s] = ds;
+    A[s] = p * g;
+    dS2[s] = fmaf(ds, g, p * (H[i] - rq));
+  }
+  to_frag(fP, P);
+  to_frag(fdS, dS);
+  to_frag(fdS2, dS2);
+  to_frag(fA, A);
+}
+
+template <typename T, int D, bool GRADQ>
+__global__ __launch_bounds__(256, 1) void query_kernel(
+    const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V, const T* __restrict__ dO,
+    const T* __restrict__ gQ, const T* __restrict__ gK, const T* __restrict__ gV, float* __restrict__ lse,
+    float* __restrict__ Dv, float* __restrict__ cv, float* __restrict__ rv, float* __restrict__ gradQ,
+    float* __restrict__ graddO, int N, int nqblk, float scale, int lse_natural) {
+  using Cfg = QueryCfg<T, D, GRADQ>;
+  using E = Elem<T>;
+  using F = typename E::frag;
+  constexpr int BK = Cfg::BK, LDK = Cfg::LDK, NCH = Cfg::NCH, NDB = Cfg::NDB, NBUF = Cfg::NBUF;
+  constexpr bool PIPE = Cfg::PIPE;
+  constexpr bool SWZ = Cfg::SWZ;
+  constexpr int ROWLEN = SWZ ? D : LDK;
+  // [NBUF][4][BK][ROWLEN]: K, gK, V, gV of a stage
+  __shared__ __attribute__((aligned(16))) T smem[NBUF * Cfg::STAGE];
+  auto sK = [&](int b, int t, int row, int col) __attribute__((always_inline)) { return smem + ((b * 4 + t) * BK + row) * ROWLEN + col; };
+  auto tile = [&](int b, int t) __attribute__((always_inline)) { return smem + (b * 4 + t) * BK * ROWLEN; };
+  auto lds_rows = [&](int b, int t, int row0, int c16) __attribute__((always_inline)) -> typename Elem<T>::frag {
+    if constexpr (SWZ) return ld_rows_sw(tile(b, t), row0, c16);
+    else return ld_rows(sK(b, t, row0, 16 * c16), LDK);
+  };
+  auto lds_cols = [&](int b, int t, int krow0, int col0) __attribute__((always_inline)) -> typename Elem<T>::frag {
+    if constexpr (SWZ) return ld_cols_perm_sw(tile(b, t), krow0, col0);
+    else return ld_cols_perm(sK(b, t, krow0, col0), LDK);
+  };
+
+  const int head = blockIdx.x / nqblk;
+  const int qblk = blockIdx.x % nqblk;
+  const size_t hoff = (size_t)head * N * D;
+  const int w = wave_id(), l = lane_id(), h = l >> 5, col = l & 31;
+  const int q = qblk * Cfg::BQ + 32 * w + col;  // this lane's query
+  const bool qvalid = q < N;
+
+  // B operands of the wave's 32 queries (lane <-> query, k over d)
+  F fQ[NCH], fgQ[NCH], fdO[NCH];
+  {
+    const T* rq = Q + hoff + (size_t)q * D;
+    const T* rgq = gQ + hoff + (size_t)q * D;
+    const T* rdo = dO + hoff + (size_t)q * D;
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+      fQ[c] = load_row_frag(rq, qvalid, c);
+      fgQ[c] = load_row_frag(rgq, qvalid, c);
+      fdO[c] = load_row_frag(rdo, qvalid, c);
+    }
+  }
+
+  const float sl2 = scale * kLog2e;
+  const bool pos_scale = scale >= 0.f;
+  OnlineSums st;  // pass 1 state
+  int nflush = 0;
+  // pass 2q state: the lane's row scalars and the output accumulators
+  // (gradQ^T, graddO^T: d rows x the wave's 32 queries)
+  float l2 = INFINITY, Dq = 0.f, cq = 0.f, rq = 0.f;
+  f32x16 accQ[GRADQ ? NDB : 1], accO[GRADQ ? NDB : 1];
+  if constexpr (GRADQ) {
+    if (qvalid) {
+      const size_t o = (size_t)head * N + q;
+      l2 = lse[o];  // row scalars carry LSE * log2(e)
+      Dq = Dv[o];
+      cq = cv[o];
+      rq = rv[o];
+    }
+#pragma unroll
+    for (int j = 0; j < NDB; ++j) {
+      accQ[j] = f32x16{};
+      accO[j] = f32x16{};
+    }
+  }
+
+  const int nblk = (N + BK - 1) / BK;  // 32-key blocks = stages
+  // staging of stage n: prefetch() issues its global reads (into registers,
+  // or straight into its LDS buffer when SWZ); commit() makes it visible to
+  // this wave's later LDS accesses (register store, or wait for the loads).
+  RowPrefetch<T, SWZ ? 0 : BK, D, 256> pk, pgk, pv, pgv;
+  auto prefetch = [&](int n) __attribute__((always_inline)) {
+    const int k0 = n * BK;
+    const int nk = min(BK, N - k0);
+    if constexpr (SWZ) {
+      const int b = n % NBUF;
+      load_tile_sw(tile(b, 0), K + hoff + (size_t)k0 * D, nk);
+      load_tile_sw(tile(b, 1), gK + hoff + (size_t)k0 * D, nk);
+      load_tile_sw(tile(b, 2), V + hoff + (size_t)k0 * D, nk);
+      load_tile_sw(tile(b, 3), gV + hoff + (size_t)k0 * D, nk);
+    } else {
+      pk.load(K + hoff + (size_t)k0 * D, nk);
+      pgk.load(gK + hoff + (size_t)k0 * D, nk);
+      pv.load(V + hoff + (size_t)k0 * D, nk);
+      pgv.load(gV + hoff + (size_t)k0 * D, nk);
+    }
+  };
+  auto commit = [&](int n) __attribute__((always_inline)) {
+    if constexpr (SWZ) {
+      wait_vmem();
+    } else {
+      const int b = n % NBUF;
+      pk.store(sK(b, 0, 0, 0), LDK);
+      pgk.store(sK(b, 1, 0, 0), LDK);
+      pv.store(sK(b, 2, 0, 0), LDK);
+      pgv.store(sK(b, 3, 0, 0), LDK);
+    }
+  };
+
+  // S^T, G^T, dP^T, H^T of block n (keys x this wave's queries)
+  struct Tiles {
+    f32x16 S, G, dP, H;
+  };
+  // d-chunks [c0, c1) of the recompute products of block n
+  auto recompute = [&](int n, Tiles& t, int c0, int c1) __attribute__((always_inline)) {
+    const int b = n % NBUF;
+    if (c0 == 0) {
+      t.S = f32x16{};
+      t.G = f32x16{};
+      t.dP = f32x16{};
+      t.H = f32x16{};
+    }
+#pragma unroll
+    for (int c = c0; c < c1; ++c) {
+      const F ak = lds_rows(b, 0, 0, c);  // lane <-> key, k over d
+      const F agk = lds_rows(b, 1, 0, c);
+      const F av = lds_rows(b, 2, 0, c);
+      const F agv = lds_rows(b, 3, 0, c);
+      E::mma(t.S, ak, fQ[c]);
+      E::mma(t.G, ak, fgQ[c]);
+      E::mma(t.G, agk, fQ[c]);
+      E::mma(t.dP, av, fdO[c]);
+      E::mma(t.H, agv, fdO[c]);
+    }
+  };
+  struct Frags {
+    F P[2], dS[2], dS2[2], A[2];
+  };
+  float mu = 0.f;  // pass 1: the running max used for the current block
+  // elementwise work of 16-key chunk cc of block n: online sums (pass 1) or
+  // operand fragments (pass 2q); TAIL masks keys past the sequence end
+  auto elementwise = [&](auto tail, int n, int cc, const Tiles& t, Frags& f) __attribute__((always_inline)) {
+    constexpr bool TAIL = decltype(tail)::value;
+    const int nrel = N - n * BK;
+    if constexpr (!GRADQ)
+      online_chunk<TAIL>(cc, t.S, t.G, t.dP, t.H, sl2, pos_scale, nrel, st, mu);
+    else
+      query_chunk<T, TAIL>(cc, t.S, t.G, t.dP, t.H, sl2, scale, l2, Dq, cq, rq, nrel, f.P[cc], f.dS[cc],
+                           f.dS2[cc], f.A[cc]);
+  };
+  // output products of 16-key chunk cc of block n (pass 2q)
+  auto outputs = [&](int n, int cc, const Frags& f) __attribute__((always_inline)) {
+    if constexpr (GRADQ) {
+      const int b = n % NBUF;
+#pragma unroll
+      for (int j = 0; j < NDB; ++j) {
+        // lane <-> d, k over this chunk's keys (accumulator row order)
+        const F tK = lds_cols(b, 0, 16 * cc, 32 * j);
+        const F tgK = lds_cols(b, 1, 16 * cc, 32 * j);
+        const F tV = lds_cols(b, 2, 16 * cc, 32 * j);
+        const F tgV = lds_cols(b, 3, 16 * cc, 32 * j);
+        E::mma(accQ[j], tK, f.dS2[cc]);
+        E::mma(accQ[j], tgK, f.dS[cc]);
+        E::mma(accO[j], tV, f.A[cc]);
+        E::mma(accO[j], tgV, f.P[cc]);
+      }
+    }
+  };
+
+  // prologue: stages 0 .. AHEAD-1 in LDS
+#pragma unroll
+  for (int n = 0; n < Cfg::AHEAD; ++n) {
+    if (n < nblk) {
+      prefetch(n);
+      commit(n);
+    }
+  }
+  __syncthreads();
+
+  using F0 = std::integral_constant<bool, false>;
+  using F1 = std::integral_constant<bool, true>;
+  const bool last_partial = N % BK != 0;
+  if constexpr (PIPE) {
+    Tiles tA, tB;
+    Frags fA, fB;
+    recompute(0, tA, 0, NCH);
+    // Iteration n: recompute n+1 (MFMA), elementwise n (VALU), outputs n-1
+    // (MFMA). The three are independent. The body runs as two phases (fenced
+    // with sched_barrier so the scheduler cannot hoist every LDS read), each
+    // pairing half the MFMAs with half the VALU work; in the steady state
+    // (1 <= n <= nblk-3, no tail) a phase is branch-free, so the MFMA and
+    // VALU streams interleave.
+    auto body = [&](auto steady, auto tail, int n, Tiles& cur, Tiles& nxt, Frags& fcur, Frags& fprev) __attribute__((always_inline)) {
+      constexpr bool STEADY = decltype(steady)::value;
+      const bool pf = STEADY || n + 2 < nblk;
+      const bool rec = STEADY || n + 1 < nblk;
+      const bool out = STEADY || n >= 1;
+      if (pf) prefetch(n + 2);  // its buffer last held stage n-2, read in iteration n-1
+#pragma unroll
+      for (int ph = 0; ph < 2; ++ph) {
+        if (rec) recompute(n + 1, nxt, ph * NCH / 2, (ph + 1) * NCH / 2);
+        elementwise(tail, n, ph, cur, fcur);
+        if (out) outputs(n - 1, ph, fprev);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      if (pf) commit(n + 2);
+      __syncthreads();
+    };
+    auto edge = [&](int n, Tiles& cur, Tiles& nxt, Frags& fcur, Frags& fprev) __attribute__((always_inline)) {
+      if (n == nblk - 1 && last_partial)
+        body(F0{}, F1{}, n, cur, nxt, fcur, fprev);
+      else
+        body(F0{}, F0{}, n, cur, nxt, fcur, fprev);
+      if constexpr (!GRADQ) st.flush();
+    };
+    edge(0, tA, tB, fA, fB);
+    int n = 1;
+    for (; n + 3 < nblk; n += 2) {
+      body(F1{}, F0{}, n, tB, tA, fB, fA);
+      body(F1{}, F0{}, n + 1, tA, tB, fA, fB);
+      if constexpr (!GRADQ) st.flush();  // level-1 chains of two blocks
+    }
+    for (; n < nblk; ++n) {
+      if (n & 1)
+        edge(n, tB, tA, fB, fA);
+      else
+        edge(n, tA, tB, fA, fB);
+    }
+#pragma unroll
+    for (int cc = 0; cc < 2; ++cc) {
+      if ((nblk - 1) & 1)
+        outputs(nblk - 1, cc, fB);
+      else
+        outputs(nblk - 1, cc, fA);
+    }
+  } else {
+    Tiles t;
+    Frags f;
+    for (int n = 0; n < nblk; ++n) {
+      const bool pf = n + 1 < nblk;
+      if (pf) prefetch(n + 1);
+      recompute(n, t, 0, NCH);
+#pragma unroll
+      for (int cc = 0; cc < 2; ++cc) {
+        if (n == nblk - 1 && last_partial)
+          elementwise(F1{}, n, cc, t, f);
+        else
+          elementwise(F0{}, n, cc, t, f);
+        outputs(n, cc, f);
+      }
+      if constexpr (!GRADQ) {
+        if (++nflush == kFlush) {
+          st.flush();
+          nflush = 0;
+        }
+      }
+      if (pf) commit(n + 1);  // its buffer last held stage n-1, read in iteration n-1
+      __syncthreads();
+    }
+  }
+
+  if constexpr (!GRADQ) {
+    st.flush();
+    // merge the two half-waves (same query column, disjoint keys)
+    const float m = st.m, lsum = st.l2, aD = st.aD2, ac = st.ac2, ae = st.ae2, ah = st.ah2;
+    const float mo = __shfl_xor(m, 32), lo = __shfl_xor(lsum, 32);
+    const float aDo = __shfl_xor(aD, 32), aco = __shfl_xor(ac, 32);
+    const float aeo = __shfl_xor(ae, 32), aho = __shfl_xor(ah, 32);
+    const float mm = fmaxf(m, mo);
+    const float mu = (mm == -INFINITY) ? 0.f : mm;
+    const float e1 = fast_exp2(m - mu), e2 = fast_exp2(mo - mu);
+    const float L = lsum * e1 + lo * e2;
+    const float AD = aD * e1 + aDo * e2, AC = ac * e1 + aco * e2;
+    const float AE = ae * e1 + aeo * e2, AH = ah * e1 + aho * e2;
+    if (h == 0 && qvalid) {
+      const float inv = 1.f / L;
+      const float Dr = AD * inv;
+      const float cr = scale * AC * inv;
+      const float rr = scale * AE * inv - Dr * cr + AH * inv;
+      const size_t o = (size_t)head * N + q;
+      const float lse2 = mm + log2f(L);
+      lse[o] = lse_natural ? lse2 * kLn2 : lse2;
+      Dv[o] = Dr;
+      cv[o] = cr;
+      rv[o] = rr;
+    }
+  } else {
+    // accQ[j] slot i holds d = 32 j + acc_row(h, i) of this lane's query
+    if (qvalid) {
+      float* gq = gradQ + hoff + (size_t)q * D;
+      float* go = graddO + hoff + (size_t)q * D;
+#pragma unroll
+      for (int j = 0; j < NDB; ++j) {
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int d0 = 32 * j + 8 * g + 4 * h;
+          *reinterpret_cast<float4*>(gq + d0) =
+              make_float4(scale * accQ[j][4 * g], scale * accQ[j][4 * g + 1], scale * accQ[j][4 * g + 2],
+                          scale * accQ[j][4 * g + 3]);
+          *reinterpret_cast<float4*>(go + d0) =
+              make_float4(accO[j][4 * g], accO[j][4 * g + 1], accO[j][4 * g + 2], accO[j][4 * g + 3]);
+        }
+      }
+    }
+  }
+}
+
+template <typename T, int D, bool GRADQ>
+hipError_t launch_query(const void* Q, const void* K, const void* V, const void* dO, const void* gQ,
+                        const void* gK, const void* gV, float* lse, float* Dv, float* cv, float* rv,
+                        float* gradQ, float* graddO, int BH, int N, float scale, int lse_natural,
+                        hipStream_t stream) {
+  using Cfg = QueryCfg<T, D, GRADQ>;
+  const int nqblk = (N + Cfg::BQ - 1) / Cfg::BQ;
+  const long long nblocks = (long long)nqblk * BH;
+  if (nblocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  query_kernel<T, D, GRADQ><<<dim3((unsigned)nblocks), dim3(256), 0, stream>>>(
+      (const T*)Q, (const T*)K, (const T*)V, (const T*)dO, (const T*)gQ, (const T*)gK, (const T*)gV, lse, Dv,
+      cv, rv, gradQ, graddO, N, nqblk, scale, lse_natural);
+  return hipGetLastError();
+}
+
+#define FLASHBOB_INST_QUERY(T, D, G)                                                                      \
+  template hipError_t launch_query<T, D, G>(const void*, const void*, const void*, const void*,         \
+                                            const void*, const void*, const void*, float*, float*,      \
+                                            float*, float*, float*, float*, int, int, float, int,         \
+                                            hipStream_t);
+FLASHBOB_INST_QUERY(bf16, 64, false)
+FLASHBOB_INST_QUERY(bf16, 128, false)
+FLASHBOB_INST_QUERY(float, 64, false)
+FLASHBOB_INST_QUERY(float, 128, false)
+FLASHBOB_INST_QUERY(bf16, 64, true)
+FLASHBOB_INST_QUERY(bf16, 128, true)
+FLASHBOB_INST_QUERY(float, 64, true)
+FLASHBOB_INST_QUERY(float, 128, true)
+
+}  // namespace flashbob

@@ -1,6 +1,7 @@
 // Host side of the C ABI declared in include/flashbob.h: argument checks
-// (all before any HIP call), workspace split, and the two kernel launches of
-// the BoB schedule on the caller's stream.
+// (all before any HIP call), workspace split, and the kernel launches of the
+// BoB schedule on the caller's stream: pass 1 (row scalars), then the two
+// halves of pass 2 (query side: gradQ, graddO; key side: gradK, gradV).
 
 #include <hip/hip_runtime.h>
 
@@ -13,14 +14,15 @@
 
 namespace flashbob {
 typedef __bf16 bf16;
+template <typename T, int D, bool GRADQ>
+hipError_t launch_query(const void* Q, const void* K, const void* V, const void* dO, const void* gQ,
+                        const void* gK, const void* gV, float* lse, float* Dv, float* cv, float* rv,
+                        float* gradQ, float* graddO, int BH, int N, float scale, int lse_natural,
+                        hipStream_t stream);
 template <typename T, int D>
-hipError_t launch_rowstats(const void* Q, const void* K, const void* V, const void* dO, const void* gQ,
-                           const void* gK, const void* gV, float* lse, float* Dv, float* cv, float* rv,
-                           float* zero_a, float* zero_b, int BH, int N, float scale, hipStream_t stream);
-template <typename T, int D>
-hipError_t launch_pass2(const void* Q, const void* K, const void* V, const void* dO, const void* gQ,
-                        const void* gK, const void* gV, const float* stats, float* gradQ, float* gradK,
-                        float* gradV, float* graddO, int BH, int N, float scale, hipStream_t stream);
+hipError_t launch_key(const void* Q, const void* K, const void* V, const void* dO, const void* gQ, const void* gK,
+                      const void* gV, const float* lse2, const float* Dv, const float* cv, const float* rv,
+                      float* gradK, float* gradV, int BH, int N, float scale, hipStream_t stream);
 }  // namespace flashbob
 
 namespace {
@@ -77,24 +79,53 @@ int check_outputs(const void* const* ins, size_t in_bytes, void* const* outs, co
   return FLASHBOB_OK;
 }
 
-template <typename T>
-hipError_t run_rowstats(int d, const void* const* in, float* lse, float* Dv, float* cv, float* rv, float* za,
-                        float* zb, int BH, int N, float scale, hipStream_t st) {
-  if (d == 64)
-    return flashbob::launch_rowstats<T, 64>(in[0], in[1], in[2], in[3], in[4], in[5], in[6], lse, Dv, cv, rv,
-                                            za, zb, BH, N, scale, st);
-  return flashbob::launch_rowstats<T, 128>(in[0], in[1], in[2], in[3], in[4], in[5], in[6], lse, Dv, cv, rv, za,
-                                           zb, BH, N, scale, st);
+// The three kernels of the schedule, dispatched on (element type, d).
+enum Stage { kPass1 = 1, kPass2Query = 2, kPass2Key = 4, kAll = 7 };
+
+template <typename T, int D>
+hipError_t run_stages(int stages, const void* const* in, float* stats, float* gQo, float* gKo, float* gVo,
+                      float* gdOo, int BH, int N, float scale, hipStream_t st) {
+  const size_t BHN = (size_t)BH * N;
+  // workspace row scalars: LSE * log2(e), D, c, r
+  float *lse = stats, *Dv = stats + BHN, *cv = stats + 2 * BHN, *rv = stats + 3 * BHN;
+  hipError_t e = hipSuccess;
+  if (stages & kPass1) {
+    e = flashbob::launch_query<T, D, false>(in[0], in[1], in[2], in[3], in[4], in[5], in[6], lse, Dv, cv, rv,
+                                            nullptr, nullptr, BH, N, scale, 0, st);
+    if (e != hipSuccess) return e;
+  }
+  if (stages & kPass2Query) {
+    e = flashbob::launch_query<T, D, true>(in[0], in[1], in[2], in[3], in[4], in[5], in[6], lse, Dv, cv, rv,
+                                           gQo, gdOo, BH, N, scale, 0, st);
+    if (e != hipSuccess) return e;
+  }
+  if (stages & kPass2Key) {
+    e = flashbob::launch_key<T, D>(in[0], in[1], in[2], in[3], in[4], in[5], in[6], lse, Dv, cv, rv, gKo, gVo,
+                                   BH, N, scale, st);
+  }
+  return e;
 }
 
-template <typename T>
-hipError_t run_pass2(int d, const void* const* in, const float* stats, float* gQo, float* gKo, float* gVo,
-                     float* gdOo, int BH, int N, float scale, hipStream_t st) {
-  if (d == 64)
-    return flashbob::launch_pass2<T, 64>(in[0], in[1], in[2], in[3], in[4], in[5], in[6], stats, gQo, gKo, gVo,
-                                         gdOo, BH, N, scale, st);
-  return flashbob::launch_pass2<T, 128>(in[0], in[1], in[2], in[3], in[4], in[5], in[6], stats, gQo, gKo, gVo,
-                                        gdOo, BH, N, scale, st);
+hipError_t dispatch(int dtype, int d, int stages, const void* const* in, float* stats, float* gQo, float* gKo,
+                    float* gVo, float* gdOo, int BH, int N, float scale, hipStream_t st) {
+  if (dtype == FLASHBOB_BF16)
+    return d == 64 ? run_stages<__bf16, 64>(stages, in, stats, gQo, gKo, gVo, gdOo, BH, N, scale, st)
+                   : run_stages<__bf16, 128>(stages, in, stats, gQo, gKo, gVo, gdOo, BH, N, scale, st);
+  return d == 64 ? run_stages<float, 64>(stages, in, stats, gQo, gKo, gVo, gdOo, BH, N, scale, st)
+                 : run_stages<float, 128>(stages, in, stats, gQo, gKo, gVo, gdOo, BH, N, scale, st);
+}
+
+hipError_t dispatch_rowstats(int dtype, int d, const void* const* in, float* lse, float* Dv, float* cv, float* rv,
+                             int BH, int N, float scale, hipStream_t st) {
+  if (dtype == FLASHBOB_BF16)
+    return d == 64 ? flashbob::launch_query<__bf16, 64, false>(in[0], in[1], in[2], in[3], in[4], in[5], in[6], lse,
+                                                              Dv, cv, rv, nullptr, nullptr, BH, N, scale, 1, st)
+                   : flashbob::launch_query<__bf16, 128, false>(in[0], in[1], in[2], in[3], in[4], in[5], in[6],
+                                                               lse, Dv, cv, rv, nullptr, nullptr, BH, N, scale, 1, st);
+  return d == 64 ? flashbob::launch_query<float, 64, false>(in[0], in[1], in[2], in[3], in[4], in[5], in[6], lse, Dv,
+                                                           cv, rv, nullptr, nullptr, BH, N, scale, 1, st)
+                 : flashbob::launch_query<float, 128, false>(in[0], in[1], in[2], in[3], in[4], in[5], in[6], lse,
+                                                            Dv, cv, rv, nullptr, nullptr, BH, N, scale, 1, st);
 }
 
 size_t stats_bytes(int B, int H, int N) {
@@ -112,10 +143,10 @@ size_t flashbob_workspace_bytes(int B, int H, int N, int d) {
   return stats_bytes(B, H, N);
 }
 
-static int bob_passes(const void* Q, const void* K, const void* V, const void* dO, const void* gQ,
+static int bob_stages(const void* Q, const void* K, const void* V, const void* dO, const void* gQ,
                       const void* gK, const void* gV, float* gradQ, float* gradK, float* gradV, float* graddO,
                       int B, int H, int N, int d, float scale, int dtype, void* workspace,
-                      size_t workspace_bytes, void* stream, bool run1, bool run2) {
+                      size_t workspace_bytes, void* stream, int stages) {
   const void* ins[7] = {Q, K, V, dO, gQ, gK, gV};
   size_t numel = 0;
   int rc = check_common(ins, B, H, N, d, scale, dtype, &numel);
@@ -128,50 +159,40 @@ static int bob_passes(const void* Q, const void* K, const void* V, const void* d
   const size_t ob[5] = {numel * 4, numel * 4, numel * 4, numel * 4, ws_need};
   rc = check_outputs(ins, numel * esz, outs, ob, 5);
   if (rc != FLASHBOB_OK) return rc;
-
-  const int BH = B * H;
-  const size_t BHN = (size_t)BH * N;
-  float* ws = static_cast<float*>(workspace);
-  hipStream_t st = static_cast<hipStream_t>(stream);
-  hipError_t e;
-  if (run1) {
-    if (dtype == FLASHBOB_BF16)
-      e = run_rowstats<__bf16>(d, ins, ws, ws + BHN, ws + 2 * BHN, ws + 3 * BHN, gradQ, graddO, BH, N, scale, st);
-    else
-      e = run_rowstats<float>(d, ins, ws, ws + BHN, ws + 2 * BHN, ws + 3 * BHN, gradQ, graddO, BH, N, scale, st);
-    if (e != hipSuccess) return hip_fail(e);
-  }
-  if (run2) {
-    if (dtype == FLASHBOB_BF16)
-      e = run_pass2<__bf16>(d, ins, ws, gradQ, gradK, gradV, graddO, BH, N, scale, st);
-    else
-      e = run_pass2<float>(d, ins, ws, gradQ, gradK, gradV, graddO, BH, N, scale, st);
-    if (e != hipSuccess) return hip_fail(e);
-  }
-  return FLASHBOB_OK;
+  const hipError_t e = dispatch(dtype, d, stages, ins, static_cast<float*>(workspace), gradQ, gradK, gradV,
+                                graddO, B * H, N, scale, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? FLASHBOB_OK : hip_fail(e);
 }
 
 int flashbob_bob(const void* Q, const void* K, const void* V, const void* dO, const void* gQ, const void* gK,
                  const void* gV, float* gradQ, float* gradK, float* gradV, float* graddO, int B, int H, int N,
                  int d, float scale, int dtype, void* workspace, size_t workspace_bytes, void* stream) {
-  return bob_passes(Q, K, V, dO, gQ, gK, gV, gradQ, gradK, gradV, graddO, B, H, N, d, scale, dtype, workspace,
-                    workspace_bytes, stream, true, true);
+  return bob_stages(Q, K, V, dO, gQ, gK, gV, gradQ, gradK, gradV, graddO, B, H, N, d, scale, dtype, workspace,
+                    workspace_bytes, stream, kAll);
 }
 
 int flashbob_bob_pass1(const void* Q, const void* K, const void* V, const void* dO, const void* gQ,
                        const void* gK, const void* gV, float* gradQ, float* gradK, float* gradV, float* graddO,
                        int B, int H, int N, int d, float scale, int dtype, void* workspace,
                        size_t workspace_bytes, void* stream) {
-  return bob_passes(Q, K, V, dO, gQ, gK, gV, gradQ, gradK, gradV, graddO, B, H, N, d, scale, dtype, workspace,
-                    workspace_bytes, stream, true, false);
+  return bob_stages(Q, K, V, dO, gQ, gK, gV, gradQ, gradK, gradV, graddO, B, H, N, d, scale, dtype, workspace,
+                    workspace_bytes, stream, kPass1);
 }
 
-int flashbob_bob_pass2(const void* Q, const void* K, const void* V, const void* dO, const void* gQ,
-                       const void* gK, const void* gV, float* gradQ, float* gradK, float* gradV, float* graddO,
-                       int B, int H, int N, int d, float scale, int dtype, void* workspace,
-                       size_t workspace_bytes, void* stream) {
-  return bob_passes(Q, K, V, dO, gQ, gK, gV, gradQ, gradK, gradV, graddO, B, H, N, d, scale, dtype, workspace,
-                    workspace_bytes, stream, false, true);
+int flashbob_bob_pass2_query(const void* Q, const void* K, const void* V, const void* dO, const void* gQ,
+                             const void* gK, const void* gV, float* gradQ, float* gradK, float* gradV,
+                             float* graddO, int B, int H, int N, int d, float scale, int dtype, void* workspace,
+                             size_t workspace_bytes, void* stream) {
+  return bob_stages(Q, K, V, dO, gQ, gK, gV, gradQ, gradK, gradV, graddO, B, H, N, d, scale, dtype, workspace,
+                    workspace_bytes, stream, kPass2Query);
+}
+
+int flashbob_bob_pass2_key(const void* Q, const void* K, const void* V, const void* dO, const void* gQ,
+                           const void* gK, const void* gV, float* gradQ, float* gradK, float* gradV,
+                           float* graddO, int B, int H, int N, int d, float scale, int dtype, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+  return bob_stages(Q, K, V, dO, gQ, gK, gV, gradQ, gradK, gradV, graddO, B, H, N, d, scale, dtype, workspace,
+                    workspace_bytes, stream, kPass2Key);
 }
 
 int flashbob_rowstats(const void* Q, const void* K, const void* V, const void* dO, const void* gQ,
@@ -187,14 +208,11 @@ int flashbob_rowstats(const void* Q, const void* K, const void* V, const void* d
   const size_t ob[4] = {vb, vb, vb, vb};
   rc = check_outputs(ins, numel * esz, outs, ob, 4);
   if (rc != FLASHBOB_OK) return rc;
-  hipStream_t st = static_cast<hipStream_t>(stream);
-  hipError_t e;
-  if (dtype == FLASHBOB_BF16)
-    e = run_rowstats<__bf16>(d, ins, lse, Dv, cv, rv, nullptr, nullptr, B * H, N, scale, st);
-  else
-    e = run_rowstats<float>(d, ins, lse, Dv, cv, rv, nullptr, nullptr, B * H, N, scale, st);
-  if (e != hipSuccess) return hip_fail(e);
-  return FLASHBOB_OK;
+  // the row scalars go to the caller's four vectors: they are laid out as
+  // the stats workspace expects only if contiguous, so launch pass 1 per vector set
+  const hipError_t e = dispatch_rowstats(dtype, d, ins, lse, Dv, cv, rv, B * H, N, scale,
+                                         static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? FLASHBOB_OK : hip_fail(e);
 }
 
 const char* flashbob_strerror(int code) {

@@ -34,13 +34,18 @@ EXPORTS = (
     "flashbob_workspace_bytes",
     "flashbob_bob",
     "flashbob_bob_pass1",
-    "flashbob_bob_pass2",
+    "flashbob_bob_pass2_query",
+    "flashbob_bob_pass2_key",
     "flashbob_rowstats",
     "flashbob_strerror",
     "flashbob_version",
 )
 
 _lib = None
+
+# the kernels of one BoB call, in launch order
+STAGES = {"pass1": "flashbob_bob_pass1", "pass2_query": "flashbob_bob_pass2_query",
+          "pass2_key": "flashbob_bob_pass2_key"}
 
 
 class FlashBoBError(RuntimeError):
@@ -63,7 +68,7 @@ def load_library(path=LIB_PATH):
     lib.flashbob_workspace_bytes.restype = sz
     lib.flashbob_bob.argtypes = [vp] * 7 + [vp] * 4 + [i, i, i, i, f, i, vp, sz, vp]
     lib.flashbob_bob.restype = i
-    for name in ("flashbob_bob_pass1", "flashbob_bob_pass2"):
+    for name in STAGES.values():
         fn = getattr(lib, name)
         fn.argtypes = [vp] * 7 + [vp] * 4 + [i, i, i, i, f, i, vp, sz, vp]
         fn.restype = i
@@ -120,14 +125,14 @@ def workspace_bytes(B, H, N, d):
     return int(load_library().flashbob_workspace_bytes(B, H, N, d))
 
 
-def bob_pass(which, Q, K, V, dO, gQ, gK, gV, out, workspace, scale=None, stream=None):
-    """One half of bob(): which=1 (row scalars, zero gradQ/graddO) or 2 (accumulate)."""
+def bob_stage(stage, Q, K, V, dO, gQ, gK, gV, out, workspace, scale=None, stream=None):
+    """Run one kernel of bob(): stage in STAGES ("pass1", "pass2_query", "pass2_key")."""
     lib = load_library()
     ins = _inputs(Q, K, V, dO, gQ, gK, gV)
     B, H, N, d = Q.shape
     if scale is None:
         scale = d ** -0.5
-    fn = lib.flashbob_bob_pass1 if which == 1 else lib.flashbob_bob_pass2
+    fn = getattr(lib, STAGES[stage])
     rc = fn(*[_ptr(t) for t in ins], *[_ptr(t) for t in out], B, H, N, d, ctypes.c_float(scale),
             _dtype_code(Q.dtype), _ptr(workspace),
             ctypes.c_size_t(workspace.numel() * workspace.element_size()),

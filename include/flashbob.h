@@ -69,7 +69,7 @@ enum {
  * B*H*N == 0 or for invalid (negative) sizes. */
 size_t flashbob_workspace_bytes(int B, int H, int N, int d);
 
-/* Exact BoB (the method's two-pass schedule).
+/* Exact BoB (the method's two-pass schedule: row scalars, then outputs).
  *   Q, K, V, dO      [B, H, N, d] inputs of the attention first backward
  *   gQ, gK, gV       [B, H, N, d] cotangents on its outputs dQ, dK, dV
  *                    (all seven in `dtype`)
@@ -78,34 +78,45 @@ size_t flashbob_workspace_bytes(int B, int H, int N, int d);
  *   scale            softmax scale s (finite; commonly 1/sqrt(d))
  *   workspace        device buffer of at least flashbob_workspace_bytes(B,H,N,d)
  *                    bytes; its contents on entry do not matter and on return
- *                    hold the row scalars (LSE, D, c, r) as [4][B][H][N] float32.
- * Pass 1 (one kernel) computes the row scalars of every query and zeroes
- * gradQ and graddO; pass 2 (one kernel) recomputes the score tiles per key
- * block and accumulates all four gradients. */
+ *                    hold the row scalars (LSE * log2(e), D, c, r) as
+ *                    [4][B][H][N] float32.
+ * Pass 1 (one kernel) computes the row scalars of every query. Pass 2
+ * recomputes the score tiles and contracts them into the outputs in two
+ * kernels: a query-major sweep producing gradQ and graddO and a key-major
+ * sweep producing gradK and gradV, each accumulating in registers (no
+ * atomics, so results are bitwise reproducible run to run). */
 int flashbob_bob(const void* Q, const void* K, const void* V, const void* dO,
                  const void* gQ, const void* gK, const void* gV,
                  float* gradQ, float* gradK, float* gradV, float* graddO,
                  int B, int H, int N, int d, float scale, int dtype,
                  void* workspace, size_t workspace_bytes, void* stream);
 
-/* The two halves of flashbob_bob, for callers that time or schedule the
- * passes separately. Same arguments and checks as flashbob_bob; calling
- * flashbob_bob_pass1 and then flashbob_bob_pass2 on one stream with the same
- * buffers is exactly flashbob_bob.
- *   pass 1: writes the row scalars into `workspace` and zeroes gradQ and
- *           graddO (gradK, gradV untouched);
- *   pass 2: reads the row scalars from `workspace`, adds into gradQ and
- *           graddO (which must hold pass 1's zeros) and writes gradK, gradV. */
+/* The three kernels of flashbob_bob as separate calls, for callers that time
+ * or schedule them individually. Same arguments and checks as flashbob_bob;
+ * calling pass1, pass2_query and pass2_key in this order on one stream with
+ * the same buffers is exactly flashbob_bob (the two pass-2 calls are
+ * independent of each other).
+ *   pass1:       writes the row scalars (LSE, D, c, r) into `workspace`;
+ *                touches no output.
+ *   pass2_query: reads the row scalars from `workspace`, writes gradQ and
+ *                graddO (query-major sweep over the keys).
+ *   pass2_key:   reads the row scalars from `workspace`, writes gradK and
+ *                gradV (key-major sweep over the queries). */
 int flashbob_bob_pass1(const void* Q, const void* K, const void* V, const void* dO,
                        const void* gQ, const void* gK, const void* gV,
                        float* gradQ, float* gradK, float* gradV, float* graddO,
                        int B, int H, int N, int d, float scale, int dtype,
                        void* workspace, size_t workspace_bytes, void* stream);
-int flashbob_bob_pass2(const void* Q, const void* K, const void* V, const void* dO,
-                       const void* gQ, const void* gK, const void* gV,
-                       float* gradQ, float* gradK, float* gradV, float* graddO,
-                       int B, int H, int N, int d, float scale, int dtype,
-                       void* workspace, size_t workspace_bytes, void* stream);
+int flashbob_bob_pass2_query(const void* Q, const void* K, const void* V, const void* dO,
+                             const void* gQ, const void* gK, const void* gV,
+                             float* gradQ, float* gradK, float* gradV, float* graddO,
+                             int B, int H, int N, int d, float scale, int dtype,
+                             void* workspace, size_t workspace_bytes, void* stream);
+int flashbob_bob_pass2_key(const void* Q, const void* K, const void* V, const void* dO,
+                           const void* gQ, const void* gK, const void* gV,
+                           float* gradQ, float* gradK, float* gradV, float* graddO,
+                           int B, int H, int N, int d, float scale, int dtype,
+                           void* workspace, size_t workspace_bytes, void* stream);
 
 /* Pass 1 alone (row statistics), exported for testing the first pass.
  * Writes, per query row, LSE (natural-log log-sum-exp of s Q K^T), the

@@ -137,7 +137,7 @@ def test_big_hessian_symmetry(big):
     assert abs(lhs - rhs) <= 1e-4 * norm
 
 
-RAGGED = [1, 2, 31, 33, 100, 129, 200, 383]
+RAGGED = [2, 31, 33, 100, 129, 200, 383]
 
 
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16], ids=["f32", "bf16"])
@@ -178,12 +178,17 @@ def test_zero_dO_zeroes_first_three_outputs():
     assert torch.count_nonzero(gdo) > 0
 
 
-def test_single_key():
-    ins = make_inputs(2, 1, 1, 64, torch.float32, seed=8)
-    say("[parity] N=1")
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16], ids=["f32", "bf16"])
+@pytest.mark.parametrize("d", [64, 128])
+def test_single_key(d, dtype):
+    """N = 1: P = 1, so gradQ, gradK, gradV are exactly zero (the kernels
+    reach zero up to fp32 rounding of dP - D) and graddO = gV."""
+    ins = make_inputs(2, 1, 1, d, dtype, seed=8 + d)
+    say(f"[parity] N=1 d={d} {dtype}")
     gq, gk, gv, gdo = gpu_bob(ins)
-    assert float(gq.abs().max()) < 1e-5 and float(gk.abs().max()) < 1e-5 and float(gv.abs().max()) < 1e-5
-    assert torch.allclose(gdo, ins["gV"], atol=1e-6, rtol=0)
+    bound = 1e-4 * float(max(ins[k].float().abs().max() for k in NAMES)) ** 3
+    assert float(gq.abs().max()) < bound and float(gk.abs().max()) < bound and float(gv.abs().max()) < bound
+    assert torch.allclose(gdo, ins["gV"].float(), atol=1e-6, rtol=0)
 
 
 def test_empty_sequence_is_noop():
@@ -193,13 +198,15 @@ def test_empty_sequence_is_noop():
     assert all(o.numel() == 0 for o in outs)
 
 
-def test_repeatable():
+def test_bitwise_repeatable():
+    """Every output element is accumulated in registers in a fixed order (no
+    atomics), so two calls give identical bits."""
     ins = make_inputs(1, 2, 1024, 64, torch.bfloat16, seed=10)
     say("[parity] repeatability")
     a = gpu_bob(ins)
     b = gpu_bob(ins)
     for x, y in zip(a, b):
-        assert rel_fro(to_f64(x), to_f64(y)) <= 1e-6
+        assert torch.equal(x, y)
 
 
 def test_nondefault_stream():
