@@ -221,6 +221,20 @@ __device__ __forceinline__ void load_tile_sw(bf16* t, const bf16* src, int nvali
                                    0);
 }
 
+// The same copy of a 32 x 64 tile done by one wave alone (4 loads).
+__device__ __forceinline__ void load_tile_sw_wave(bf16* t, const bf16* src, int nvalid) {
+  const int l = lane_id();
+  typedef __attribute__((address_space(3))) void lds_void;
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    const int row = 8 * p + (l >> 3);
+    const int c = (l & 7) ^ swz(row);
+    const int srow = row < nvalid ? row : nvalid - 1;
+    __builtin_amdgcn_global_load_lds((const void*)(src + srow * 64 + 8 * c), (lds_void*)(t + 8 * p * 64), 16,
+                                     0, 0);
+  }
+}
+
 // Wait for this wave's outstanding global loads, including direct-to-LDS ones.
 __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 

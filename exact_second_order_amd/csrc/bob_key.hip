@@ -40,7 +40,11 @@ struct KeyCfg {
   static constexpr int ROWLEN = SWZ ? D : LDQ;
   static constexpr int QSTAGE = 3 * BQ * ROWLEN;       // Q, gQ, dO elements of one stage
   static constexpr int SSTAGE = 4 * BQ;                // row scalars of one stage (floats)
-  static constexpr size_t LDS_BYTES = NBUF * (QSTAGE * sizeof(T) + SSTAGE * sizeof(float));
+  // SWZ: each wave's K, gK, V, gV rows live in LDS (4 x 32 x 64 per wave)
+  // instead of registers, after the stage buffers
+  static constexpr size_t KSIDE = SWZ ? 4 * 4 * 32 * D * sizeof(T) : 0;
+  static constexpr size_t STAGE_BYTES = NBUF * (QSTAGE * sizeof(T) + SSTAGE * sizeof(float));
+  static constexpr size_t LDS_BYTES = STAGE_BYTES + KSIDE;
   static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
 };
 
@@ -136,10 +140,23 @@ __global__ __launch_bounds__(256, 1) void key_kernel(
   const int key = kblk * Cfg::BC + 32 * w + col;  // this lane's key
   const bool kvalid = key < N;
   const bool ktail = kblk * Cfg::BC + Cfg::BC > N;
+  auto ktile = [&](int t) __attribute__((always_inline)) {
+    return reinterpret_cast<T*>(smem + Cfg::STAGE_BYTES) + (w * 4 + t) * 32 * D;
+  };
 
-  // B operands of the wave's 32 keys (lane <-> key, k over d)
-  F bK[NCH], bgK[NCH], bV[NCH], bgV[NCH];
-  {
+  // B operands of the wave's 32 keys (lane <-> key, k over d): registers, or
+  // (SWZ) this wave's LDS tiles, which keeps the pipelined loop within the
+  // register file
+  F bK[SWZ ? 1 : NCH], bgK[SWZ ? 1 : NCH], bV[SWZ ? 1 : NCH], bgV[SWZ ? 1 : NCH];
+  if constexpr (SWZ) {
+    const int k0w = kblk * Cfg::BC + 32 * w;
+    const int nkw = max(1, min(32, N - k0w));  // waves wholly past the end copy row N-1 (masked)
+    const size_t ro = hoff + (size_t)min(k0w, N - 1) * D;
+    load_tile_sw_wave(ktile(0), K + ro, nkw);
+    load_tile_sw_wave(ktile(1), gK + ro, nkw);
+    load_tile_sw_wave(ktile(2), V + ro, nkw);
+    load_tile_sw_wave(ktile(3), gV + ro, nkw);
+  } else {
     const size_t ro = hoff + (size_t)key * D;
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
@@ -149,6 +166,13 @@ __global__ __launch_bounds__(256, 1) void key_kernel(
       bgV[c] = load_key_frag(gV + ro, kvalid, c);
     }
   }
+  auto keyop = [&](int t, int c) __attribute__((always_inline)) -> F {
+    if constexpr (SWZ) {
+      return ld_rows_sw(ktile(t), 0, c);
+    } else {
+      return t == 0 ? bK[c] : t == 1 ? bgK[c] : t == 2 ? bV[c] : bgV[c];
+    }
+  };
   // gradK^T, gradV^T: d rows x the wave's 32 keys
   f32x16 accK[NDB], accV[NDB];
 #pragma unroll
@@ -224,11 +248,12 @@ __global__ __launch_bounds__(256, 1) void key_kernel(
       const F aq = lds_rows(b, 0, c);  // lane <-> query, k over d
       const F agq = lds_rows(b, 1, c);
       const F ado = lds_rows(b, 2, c);
-      E::mma(t.S, aq, bK[c]);
-      E::mma(t.G, agq, bK[c]);
-      E::mma(t.G, aq, bgK[c]);
-      E::mma(t.dP, ado, bV[c]);
-      E::mma(t.H, ado, bgV[c]);
+      const F k = keyop(0, c);
+      E::mma(t.S, aq, k);
+      E::mma(t.G, agq, k);
+      E::mma(t.G, aq, keyop(1, c));
+      E::mma(t.dP, ado, keyop(2, c));
+      E::mma(t.H, ado, keyop(3, c));
     }
   };
   struct Frags {
@@ -270,58 +295,53 @@ __global__ __launch_bounds__(256, 1) void key_kernel(
   const bool last_partial = N % BQ != 0;
   if constexpr (PIPE) {
     Tiles tA, tB;
-    Frags fA, fB;
+    Frags fr;
     recompute(0, tA, 0, NCH);
-    // iteration n: recompute n+1 (MFMA), elementwise n (VALU), outputs n-1
-    // (MFMA), as two fenced phases; branch-free in the steady state
-    // (1 <= n <= nblk-3)
-    auto body = [&](auto steady, auto tail, int n, Tiles& cur, Tiles& nxt, Frags& fcur, Frags& fprev) __attribute__((always_inline)) {
+    // Iteration n, three fenced phases: [recompute n+1 first half |
+    // elementwise n chunk 0], [recompute n+1 second half, outputs n chunk 0 |
+    // elementwise n chunk 1], [outputs n chunk 1]. MFMA and VALU work in a
+    // phase are independent; only one set of operand fragments is live.
+    // Branch-free in the steady state (1 <= n <= nblk-3).
+    auto body = [&](auto steady, auto tail, int n, Tiles& cur, Tiles& nxt) __attribute__((always_inline)) {
       constexpr bool STEADY = decltype(steady)::value;
       const bool pf = STEADY || n + 2 < nblk;
       const bool rec = STEADY || n + 1 < nblk;
-      const bool out = STEADY || n >= 1;
       if (pf) prefetch(n + 2);  // its buffer last held stage n-2, read in iteration n-1
-#pragma unroll
-      for (int ph = 0; ph < 2; ++ph) {
-        if (rec) recompute(n + 1, nxt, ph * NCH / 2, (ph + 1) * NCH / 2);
-        elementwise(tail, n, ph, cur, fcur);
-        if (out) outputs(n - 1, ph, fprev);
-        __builtin_amdgcn_sched_barrier(0);
-      }
+      if (rec) recompute(n + 1, nxt, 0, NCH / 2);
+      elementwise(tail, n, 0, cur, fr);
+      __builtin_amdgcn_sched_barrier(0);
+      if (rec) recompute(n + 1, nxt, NCH / 2, NCH);
+      outputs(n, 0, fr);
+      elementwise(tail, n, 1, cur, fr);
+      __builtin_amdgcn_sched_barrier(0);
+      outputs(n, 1, fr);
       if (pf) commit(n + 2);
       __syncthreads();
     };
-    auto edge = [&](int n, Tiles& cur, Tiles& nxt, Frags& fcur, Frags& fprev) __attribute__((always_inline)) {
+    auto edge = [&](int n, Tiles& cur, Tiles& nxt) __attribute__((always_inline)) {
       if (ktail || (n == nblk - 1 && last_partial))
-        body(F0{}, F1{}, n, cur, nxt, fcur, fprev);
+        body(F0{}, F1{}, n, cur, nxt);
       else
-        body(F0{}, F0{}, n, cur, nxt, fcur, fprev);
+        body(F0{}, F0{}, n, cur, nxt);
     };
-    edge(0, tA, tB, fA, fB);
+    edge(0, tA, tB);
     int n = 1;
     if (ktail) {
       for (; n + 3 < nblk; n += 2) {
-        body(F1{}, F1{}, n, tB, tA, fB, fA);
-        body(F1{}, F1{}, n + 1, tA, tB, fA, fB);
+        body(F1{}, F1{}, n, tB, tA);
+        body(F1{}, F1{}, n + 1, tA, tB);
       }
     } else {
       for (; n + 3 < nblk; n += 2) {
-        body(F1{}, F0{}, n, tB, tA, fB, fA);
-        body(F1{}, F0{}, n + 1, tA, tB, fA, fB);
+        body(F1{}, F0{}, n, tB, tA);
+        body(F1{}, F0{}, n + 1, tA, tB);
       }
     }
     for (; n < nblk; ++n) {
       if (n & 1)
-        edge(n, tB, tA, fB, fA);
+        edge(n, tB, tA);
       else
-        edge(n, tA, tB, fA, fB);
-    }
-#pragma unroll
-    for (int cc = 0; cc < 2; ++cc) {
-      if ((nblk - 1) & 1)
-        outputs(nblk - 1, cc, fB);
-      else
-        outputs(nblk - 1, cc, fA);
+        edge(n, tA, tB);
     }
   } else {
     Tiles t;
