@@ -13,14 +13,22 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libflashbob.so")
 
-SOURCES = ["flashbob_api.hip", "bob_query.hip", "bob_key.hip"]
+# (source, extra flags): bob_query.hip is built twice. The pass-1 object keeps
+# MFMA results in VGPRs (its register budget allows it, and its elementwise
+# work then reads them without AGPR copies); the pass-2 object lets the
+# compiler place accumulators in AGPRs.
+OBJECTS = [
+    ("flashbob_api.hip", []),
+    ("bob_query.hip", ["-DFLASHBOB_QUERY_PASS1", "-mllvm", "-amdgpu-mfma-vgpr-form"]),
+    ("bob_query.hip", ["-DFLASHBOB_QUERY_PASS2"]),
+    ("bob_key.hip", []),
+]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",
     "-O3",
     "-std=c++17",
     "-fPIC",
-    "-shared",
     "-munsafe-fp-atomics",
     # no packed fp32 VALU ops (v_pk_*_f32) in device code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
@@ -35,21 +43,32 @@ def hipcc():
     raise RuntimeError("hipcc not found")
 
 
-def build(verbose=False):
-    srcs = [os.path.join(CSRC, s) for s in SOURCES]
-    tmp = LIB + ".tmp"
-    cmd = [hipcc(), *HIPCC_FLAGS, "-I", INCLUDE, "-I", CSRC, *srcs, "-o", tmp]
+def _run(cmd, verbose):
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
     out = "\n".join(
         ln for ln in (res.stdout + res.stderr).splitlines()
-        if "packed-fp32-ops" not in ln  # host pass does not know the device feature
+        if "packed-fp32-ops" not in ln  # the host pass does not know the device feature
     )
     if res.returncode != 0:
         raise RuntimeError(f"hipcc failed ({res.returncode}):\n{out}")
     if verbose and out.strip():
         print(out)
+
+
+def build(verbose=False):
+    """Compile every object and link libflashbob.so (always rebuilds)."""
+    objdir = os.path.join(PKG, "_build")
+    os.makedirs(objdir, exist_ok=True)
+    objs = []
+    for i, (src, extra) in enumerate(OBJECTS):
+        obj = os.path.join(objdir, f"{i}_{os.path.splitext(src)[0]}.o")
+        _run([hipcc(), *HIPCC_FLAGS, *extra, "-I", INCLUDE, "-I", CSRC, "-c", os.path.join(CSRC, src),
+              "-o", obj], verbose)
+        objs.append(obj)
+    tmp = LIB + ".tmp"
+    _run([hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp], verbose)
     os.replace(tmp, LIB)
     return LIB
 

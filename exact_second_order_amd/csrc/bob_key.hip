@@ -32,17 +32,23 @@ struct KeyCfg {
   static constexpr int BQ = 32;                        // queries per LDS stage (one MFMA block)
   static constexpr int LDQ = D + 16 / (int)sizeof(T);  // padded LDS row (elements)
   static constexpr int NCH = D / 16, NDB = D / 32;
-  // same pipelining and staging choices as the query-major kernel
-  static constexpr bool PIPE = sizeof(T) == 2 && D == 64;
-  static constexpr bool SWZ = PIPE;
+  // same staging choices as the query-major kernel; OCC2: two waves per SIMD
+  // (no cross-iteration pipeline)
+  static constexpr bool SWZ = sizeof(T) == 2 && D == 64;
+  static constexpr bool OCC2 = SWZ;
+  static constexpr bool PIPE = SWZ && !OCC2;
+  // SWZ: which of the wave's K, gK, V, gV operand tensors (bits 0..3) live in
+  // LDS instead of registers; K (used by two products) stays in registers
+  static constexpr int KLDS = SWZ ? 0xE : 0;
+  static constexpr int NKLDS = __builtin_popcount(KLDS);
   static constexpr int NBUF = PIPE ? 4 : 2;
   static constexpr int AHEAD = PIPE ? 2 : 1;
   static constexpr int ROWLEN = SWZ ? D : LDQ;
   static constexpr int QSTAGE = 3 * BQ * ROWLEN;       // Q, gQ, dO elements of one stage
   static constexpr int SSTAGE = 4 * BQ;                // row scalars of one stage (floats)
-  // SWZ: each wave's K, gK, V, gV rows live in LDS (4 x 32 x 64 per wave)
-  // instead of registers, after the stage buffers
-  static constexpr size_t KSIDE = SWZ ? 4 * 4 * 32 * D * sizeof(T) : 0;
+  // the LDS-resident key-side tiles (NKLDS per wave, 32 x D each) follow the
+  // stage buffers
+  static constexpr size_t KSIDE = (size_t)4 * NKLDS * 32 * D * sizeof(T);
   static constexpr size_t STAGE_BYTES = NBUF * (QSTAGE * sizeof(T) + SSTAGE * sizeof(float));
   static constexpr size_t LDS_BYTES = STAGE_BYTES + KSIDE;
   static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
@@ -102,7 +108,7 @@ __device__ __forceinline__ void key_chunk(int cc, const f32x16& S, const f32x16&
 }
 
 template <typename T, int D>
-__global__ __launch_bounds__(256, 1) void key_kernel(
+__global__ __launch_bounds__(256, (KeyCfg<T, D>::OCC2 ? 2 : 1)) void key_kernel(
     const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V, const T* __restrict__ dO,
     const T* __restrict__ gQ, const T* __restrict__ gK, const T* __restrict__ gV,
     const float* __restrict__ lse2, const float* __restrict__ Dv, const float* __restrict__ cv,
@@ -140,38 +146,43 @@ __global__ __launch_bounds__(256, 1) void key_kernel(
   const int key = kblk * Cfg::BC + 32 * w + col;  // this lane's key
   const bool kvalid = key < N;
   const bool ktail = kblk * Cfg::BC + Cfg::BC > N;
+  // LDS tile of key-side tensor t (a KLDS member)
   auto ktile = [&](int t) __attribute__((always_inline)) {
-    return reinterpret_cast<T*>(smem + Cfg::STAGE_BYTES) + (w * 4 + t) * 32 * D;
+    const int slot = __builtin_popcount(Cfg::KLDS & ((1 << t) - 1));
+    return reinterpret_cast<T*>(smem + Cfg::STAGE_BYTES) + (w * Cfg::NKLDS + slot) * 32 * D;
   };
 
   // B operands of the wave's 32 keys (lane <-> key, k over d): registers, or
-  // (SWZ) this wave's LDS tiles, which keeps the pipelined loop within the
-  // register file
-  F bK[SWZ ? 1 : NCH], bgK[SWZ ? 1 : NCH], bV[SWZ ? 1 : NCH], bgV[SWZ ? 1 : NCH];
-  if constexpr (SWZ) {
+  // (KLDS members) this wave's LDS tiles, which keeps the kernel within its
+  // register budget
+  constexpr int KLDS = Cfg::KLDS;
+  F bK[(KLDS & 1) ? 1 : NCH], bgK[(KLDS & 2) ? 1 : NCH], bV[(KLDS & 4) ? 1 : NCH], bgV[(KLDS & 8) ? 1 : NCH];
+  {
     const int k0w = kblk * Cfg::BC + 32 * w;
     const int nkw = max(1, min(32, N - k0w));  // waves wholly past the end copy row N-1 (masked)
-    const size_t ro = hoff + (size_t)min(k0w, N - 1) * D;
-    load_tile_sw_wave(ktile(0), K + ro, nkw);
-    load_tile_sw_wave(ktile(1), gK + ro, nkw);
-    load_tile_sw_wave(ktile(2), V + ro, nkw);
-    load_tile_sw_wave(ktile(3), gV + ro, nkw);
-  } else {
+    const size_t rw = hoff + (size_t)min(k0w, N - 1) * D;
     const size_t ro = hoff + (size_t)key * D;
+    const T* const srcs[4] = {K, gK, V, gV};
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      if constexpr (SWZ) {
+        if (KLDS & (1 << t)) load_tile_sw_wave(ktile(t), srcs[t] + rw, nkw);
+      }
+    }
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
-      bK[c] = load_key_frag(K + ro, kvalid, c);
-      bgK[c] = load_key_frag(gK + ro, kvalid, c);
-      bV[c] = load_key_frag(V + ro, kvalid, c);
-      bgV[c] = load_key_frag(gV + ro, kvalid, c);
+      if constexpr (!(KLDS & 1)) bK[c] = load_key_frag(K + ro, kvalid, c);
+      if constexpr (!(KLDS & 2)) bgK[c] = load_key_frag(gK + ro, kvalid, c);
+      if constexpr (!(KLDS & 4)) bV[c] = load_key_frag(V + ro, kvalid, c);
+      if constexpr (!(KLDS & 8)) bgV[c] = load_key_frag(gV + ro, kvalid, c);
     }
   }
   auto keyop = [&](int t, int c) __attribute__((always_inline)) -> F {
     if constexpr (SWZ) {
-      return ld_rows_sw(ktile(t), 0, c);
-    } else {
-      return t == 0 ? bK[c] : t == 1 ? bgK[c] : t == 2 ? bV[c] : bgV[c];
+      if (KLDS & (1 << t)) return ld_rows_sw(ktile(t), 0, c);
     }
+    return t == 0 ? bK[(KLDS & 1) ? 0 : c]
+                  : t == 1 ? bgK[(KLDS & 2) ? 0 : c] : t == 2 ? bV[(KLDS & 4) ? 0 : c] : bgV[(KLDS & 8) ? 0 : c];
   };
   // gradK^T, gradV^T: d rows x the wave's 32 keys
   f32x16 accK[NDB], accV[NDB];

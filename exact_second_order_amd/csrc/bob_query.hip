@@ -47,11 +47,14 @@ struct QueryCfg {
   // does the elementwise work of block n and the output products of block
   // n-1, so MFMA and VALU streams are independent; four stage buffers (n-1
   // .. n+2) are live. Otherwise one block per iteration, two buffers.
-  static constexpr bool PIPE = sizeof(T) == 2 && D == 64;
-  // The pipelined variant stages tiles with direct global->LDS loads into
-  // swizzled unpadded rows (no staging registers); the others stage through
-  // registers into padded rows.
-  static constexpr bool SWZ = PIPE;
+  // bf16 d = 64 stages tiles with direct global->LDS loads into swizzled
+  // unpadded rows (no staging registers); the others stage through registers
+  // into padded rows. OCC2: two waves per SIMD (<= 256 registers, no
+  // cross-iteration pipeline; the second wave hides the first one's
+  // latencies and overlaps its VALU work with the other's MFMAs).
+  static constexpr bool SWZ = sizeof(T) == 2 && D == 64;
+  static constexpr bool OCC2 = SWZ;
+  static constexpr bool PIPE = SWZ && !OCC2;
   static constexpr int NBUF = PIPE ? 4 : 2;
   static constexpr int AHEAD = PIPE ? 2 : 1;           // prefetch distance in stages
   static constexpr int STAGE = 4 * BK * (SWZ ? D : LDK);  // elements of one stage
@@ -109,19 +112,19 @@ constexpr int kFlush = 64;  // blocks per level-1 chain
 // >= nvalid_rel are masked out.
 template <bool TAIL>
 __device__ __forceinline__ void online_chunk(int cc, const f32x16& S, const f32x16& G, const f32x16& dP,
-                                             const f32x16& H, float sl2, bool pos_scale, int nvalid_rel,
-                                             OnlineSums& st, float& mu) {
+                                             const f32x16& H, float sl2, int nvalid_rel, OnlineSums& st,
+                                             float& mu) {
   const int h = lane_id() >> 5;
   if (cc == 0) {
-    // block extreme of the raw score (the max of s*S is s*max S for s >= 0,
-    // s*min S otherwise)
-    float ext = pos_scale ? -INFINITY : INFINITY;
+    // block maximum of x = S * scale * log2(e) (taken on the product, which
+    // is canonical, so max needs no NaN quieting, and which has the right
+    // order for either sign of the scale)
+    float mb = -INFINITY;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const bool ok = !TAIL || acc_row(h, i) < nvalid_rel;
-      if (ok) ext = pos_scale ? fmaxf(ext, S[i]) : fminf(ext, S[i]);
+      if (ok) mb = fmaxf(mb, S[i] * sl2);
     }
-    const float mb = (ext == INFINITY || ext == -INFINITY) ? -INFINITY : ext * sl2;
     const float mn = fmaxf(st.m, mb);
     mu = (mn == -INFINITY) ? 0.f : mn;
     const float alpha = fast_exp2(st.m - mu);
@@ -182,7 +185,7 @@ __device__ __forceinline__ void query_chunk(int cc, const f32x16& S, const f32x1
 }
 
 template <typename T, int D, bool GRADQ>
-__global__ __launch_bounds__(256, 1) void query_kernel(
+__global__ __launch_bounds__(256, (QueryCfg<T, D, GRADQ>::OCC2 ? 2 : 1)) void query_kernel(
     const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V, const T* __restrict__ dO,
     const T* __restrict__ gQ, const T* __restrict__ gK, const T* __restrict__ gV, float* __restrict__ lse,
     float* __restrict__ Dv, float* __restrict__ cv, float* __restrict__ rv, float* __restrict__ gradQ,
@@ -229,7 +232,6 @@ __global__ __launch_bounds__(256, 1) void query_kernel(
   }
 
   const float sl2 = scale * kLog2e;
-  const bool pos_scale = scale >= 0.f;
   OnlineSums st;  // pass 1 state
   int nflush = 0;
   // pass 2q state: the lane's row scalars and the output accumulators
@@ -320,7 +322,7 @@ __global__ __launch_bounds__(256, 1) void query_kernel(
     constexpr bool TAIL = decltype(tail)::value;
     const int nrel = N - n * BK;
     if constexpr (!GRADQ)
-      online_chunk<TAIL>(cc, t.S, t.G, t.dP, t.H, sl2, pos_scale, nrel, st, mu);
+      online_chunk<TAIL>(cc, t.S, t.G, t.dP, t.H, sl2, nrel, st, mu);
     else
       query_chunk<T, TAIL>(cc, t.S, t.G, t.dP, t.H, sl2, scale, l2, Dq, cq, rq, nrel, f.P[cc], f.dS[cc],
                            f.dS2[cc], f.A[cc]);
@@ -502,13 +504,19 @@ hipError_t launch_query(const void* Q, const void* K, const void* V, const void*
                                             const void*, const void*, const void*, float*, float*,      \
                                             float*, float*, float*, float*, int, int, float, int,         \
                                             hipStream_t);
+// Pass 1 and pass 2q instantiations are built as separate objects (pass 1
+// with MFMA results kept in VGPRs, which its register budget allows).
+#ifndef FLASHBOB_QUERY_PASS2
 FLASHBOB_INST_QUERY(bf16, 64, false)
 FLASHBOB_INST_QUERY(bf16, 128, false)
 FLASHBOB_INST_QUERY(float, 64, false)
 FLASHBOB_INST_QUERY(float, 128, false)
+#endif
+#ifndef FLASHBOB_QUERY_PASS1
 FLASHBOB_INST_QUERY(bf16, 64, true)
 FLASHBOB_INST_QUERY(bf16, 128, true)
 FLASHBOB_INST_QUERY(float, 64, true)
 FLASHBOB_INST_QUERY(float, 128, true)
+#endif
 
 }  // namespace flashbob
