@@ -84,7 +84,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", type=int, default=3, help="index into the workload table")
-    ap.add_argument("--cpu-rows", type=int, default=6144, help="oracle sample size (query rows)")
+    ap.add_argument("--cpu-rows", type=int, default=16384, help="oracle sample size (query rows)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-mb", type=int, default=0,
                     help="run one plain device copy of this many MiB first (calibrates HBM byte counters)")

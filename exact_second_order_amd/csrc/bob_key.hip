@@ -10,8 +10,7 @@
 //
 // gfx950 schedule: a workgroup of 4 waves owns 128 keys (32 per wave) and
 // streams the queries (Q, gQ, dO and their row scalars) in 32-row stages
-// through LDS buffers, issuing each stage's global reads one or two stages
-// ahead (software pipelined like the query-major kernel). Per 32-query block a wave builds S, G, dP, H (queries x its keys)
+// through two LDS buffers, issuing each stage's global reads one stage ahead. Per 32-query block a wave builds S, G, dP, H (queries x its keys)
 // with MFMA, so each lane holds one key and 16 queries; the queries' row
 // scalars come from LDS as broadcast reads. P, dS, dS2, A then feed the next
 // MFMAs straight from the accumulator registers as B operands (k = queries in
@@ -32,17 +31,14 @@ struct KeyCfg {
   static constexpr int BQ = 32;                        // queries per LDS stage (one MFMA block)
   static constexpr int LDQ = D + 16 / (int)sizeof(T);  // padded LDS row (elements)
   static constexpr int NCH = D / 16, NDB = D / 32;
-  // same staging choices as the query-major kernel; OCC2: two waves per SIMD
-  // (no cross-iteration pipeline)
+  // same staging and occupancy choices as the query-major kernel
   static constexpr bool SWZ = sizeof(T) == 2 && D == 64;
   static constexpr bool OCC2 = SWZ;
-  static constexpr bool PIPE = SWZ && !OCC2;
+  static constexpr int NBUF = 2;                       // stage n in use, stage n+1 arriving
   // SWZ: which of the wave's K, gK, V, gV operand tensors (bits 0..3) live in
   // LDS instead of registers; K (used by two products) stays in registers
   static constexpr int KLDS = SWZ ? 0xE : 0;
   static constexpr int NKLDS = __builtin_popcount(KLDS);
-  static constexpr int NBUF = PIPE ? 4 : 2;
-  static constexpr int AHEAD = PIPE ? 2 : 1;
   static constexpr int ROWLEN = SWZ ? D : LDQ;
   static constexpr int QSTAGE = 3 * BQ * ROWLEN;       // Q, gQ, dO elements of one stage
   static constexpr int SSTAGE = 4 * BQ;                // row scalars of one stage (floats)
@@ -119,7 +115,7 @@ __global__ __launch_bounds__(256, (KeyCfg<T, D>::OCC2 ? 2 : 1)) void key_kernel(
   using F = typename E::frag;
   constexpr int BQ = Cfg::BQ, LDQ = Cfg::LDQ, NCH = Cfg::NCH, NDB = Cfg::NDB, NBUF = Cfg::NBUF;
   constexpr int ROWLEN = Cfg::ROWLEN;
-  constexpr bool PIPE = Cfg::PIPE, SWZ = Cfg::SWZ;
+  constexpr bool SWZ = Cfg::SWZ;
   // [NBUF][3][BQ][ROWLEN] Q, gQ, dO rows, then [NBUF][4][BQ] row scalars.
   // (Addresses are always formed from the __shared__ array itself so that
   // they stay LDS addresses.)
@@ -292,86 +288,29 @@ __global__ __launch_bounds__(256, (KeyCfg<T, D>::OCC2 ? 2 : 1)) void key_kernel(
     }
   };
 
-#pragma unroll
-  for (int n = 0; n < Cfg::AHEAD; ++n) {
-    if (n < nblk) {
-      prefetch(n);
-      commit(n);
-    }
-  }
+  prefetch(0);  // nblk >= 1
+  commit(0);
   __syncthreads();
 
   using F0 = std::integral_constant<bool, false>;
   using F1 = std::integral_constant<bool, true>;
   const bool last_partial = N % BQ != 0;
-  if constexpr (PIPE) {
-    Tiles tA, tB;
-    Frags fr;
-    recompute(0, tA, 0, NCH);
-    // Iteration n, three fenced phases: [recompute n+1 first half |
-    // elementwise n chunk 0], [recompute n+1 second half, outputs n chunk 0 |
-    // elementwise n chunk 1], [outputs n chunk 1]. MFMA and VALU work in a
-    // phase are independent; only one set of operand fragments is live.
-    // Branch-free in the steady state (1 <= n <= nblk-3).
-    auto body = [&](auto steady, auto tail, int n, Tiles& cur, Tiles& nxt) __attribute__((always_inline)) {
-      constexpr bool STEADY = decltype(steady)::value;
-      const bool pf = STEADY || n + 2 < nblk;
-      const bool rec = STEADY || n + 1 < nblk;
-      if (pf) prefetch(n + 2);  // its buffer last held stage n-2, read in iteration n-1
-      if (rec) recompute(n + 1, nxt, 0, NCH / 2);
-      elementwise(tail, n, 0, cur, fr);
-      __builtin_amdgcn_sched_barrier(0);
-      if (rec) recompute(n + 1, nxt, NCH / 2, NCH);
-      outputs(n, 0, fr);
-      elementwise(tail, n, 1, cur, fr);
-      __builtin_amdgcn_sched_barrier(0);
-      outputs(n, 1, fr);
-      if (pf) commit(n + 2);
-      __syncthreads();
-    };
-    auto edge = [&](int n, Tiles& cur, Tiles& nxt) __attribute__((always_inline)) {
-      if (ktail || (n == nblk - 1 && last_partial))
-        body(F0{}, F1{}, n, cur, nxt);
-      else
-        body(F0{}, F0{}, n, cur, nxt);
-    };
-    edge(0, tA, tB);
-    int n = 1;
-    if (ktail) {
-      for (; n + 3 < nblk; n += 2) {
-        body(F1{}, F1{}, n, tB, tA);
-        body(F1{}, F1{}, n + 1, tA, tB);
-      }
-    } else {
-      for (; n + 3 < nblk; n += 2) {
-        body(F1{}, F0{}, n, tB, tA);
-        body(F1{}, F0{}, n + 1, tA, tB);
-      }
-    }
-    for (; n < nblk; ++n) {
-      if (n & 1)
-        edge(n, tB, tA);
-      else
-        edge(n, tA, tB);
-    }
-  } else {
-    Tiles t;
-    Frags f;
-    for (int n = 0; n < nblk; ++n) {
-      const bool pf = n + 1 < nblk;
-      if (pf) prefetch(n + 1);
-      recompute(n, t, 0, NCH);
+  Tiles t;
+  Frags f;
+  for (int n = 0; n < nblk; ++n) {
+    const bool pf = n + 1 < nblk;
+    if (pf) prefetch(n + 1);
+    recompute(n, t, 0, NCH);
 #pragma unroll
-      for (int cc = 0; cc < 2; ++cc) {
-        if (ktail || (n == nblk - 1 && last_partial))
-          elementwise(F1{}, n, cc, t, f);
-        else
-          elementwise(F0{}, n, cc, t, f);
-        outputs(n, cc, f);
-      }
-      if (pf) commit(n + 1);  // its buffer last held stage n-1, read in iteration n-1
-      __syncthreads();
+    for (int cc = 0; cc < 2; ++cc) {
+      if (ktail || (n == nblk - 1 && last_partial))
+        elementwise(F1{}, n, cc, t, f);
+      else
+        elementwise(F0{}, n, cc, t, f);
+      outputs(n, cc, f);
     }
+    if (pf) commit(n + 1);  // its buffer last held stage n-1, read in iteration n-1
+    __syncthreads();
   }
 
   // accK[j] slot i holds d = 32 j + acc_row(h, i) of this lane's key

@@ -19,8 +19,8 @@
 //            gradQ = s (dS2 K + dS gK),  graddO = A V + P gV.
 //
 // gfx950 schedule: a workgroup of 4 waves owns 128 queries (32 per wave) and
-// streams the keys in 32-row stages (K, gK, V, gV) through LDS buffers, with
-// each stage's global reads issued into registers one or two stages ahead. Per 32-key block a wave builds the transposed tiles S^T, G^T,
+// streams the keys in 32-row stages (K, gK, V, gV) through two LDS buffers,
+// issuing each stage's global reads one stage ahead. Per 32-key block a wave builds the transposed tiles S^T, G^T,
 // dP^T, H^T (keys x its queries) with MFMA; the accumulator layout then puts
 // one query per lane, so the row scalars are per-lane registers. In pass 2q
 // the elementwise results (P, dS, dS2, A) go straight from the accumulator
@@ -43,20 +43,14 @@ struct QueryCfg {
   static constexpr int LDK = D + 16 / (int)sizeof(T);  // padded LDS row (elements)
   static constexpr int NCH = D / 16;                   // 16-wide k chunks over d
   static constexpr int NDB = D / 32;                   // 32-row blocks of d
-  // Software pipelining (bf16, d = 64): iteration n recomputes block n+1,
-  // does the elementwise work of block n and the output products of block
-  // n-1, so MFMA and VALU streams are independent; four stage buffers (n-1
-  // .. n+2) are live. Otherwise one block per iteration, two buffers.
   // bf16 d = 64 stages tiles with direct global->LDS loads into swizzled
-  // unpadded rows (no staging registers); the others stage through registers
-  // into padded rows. OCC2: two waves per SIMD (<= 256 registers, no
-  // cross-iteration pipeline; the second wave hides the first one's
-  // latencies and overlaps its VALU work with the other's MFMAs).
+  // unpadded rows (no staging registers) and runs two waves per SIMD (<= 256
+  // registers: the second wave hides the first one's latencies and overlaps
+  // its VALU work with the other's MFMAs). The other variants stage through
+  // registers into padded rows at one wave per SIMD.
   static constexpr bool SWZ = sizeof(T) == 2 && D == 64;
   static constexpr bool OCC2 = SWZ;
-  static constexpr bool PIPE = SWZ && !OCC2;
-  static constexpr int NBUF = PIPE ? 4 : 2;
-  static constexpr int AHEAD = PIPE ? 2 : 1;           // prefetch distance in stages
+  static constexpr int NBUF = 2;                       // stage n in use, stage n+1 arriving
   static constexpr int STAGE = 4 * BK * (SWZ ? D : LDK);  // elements of one stage
   static constexpr size_t LDS_BYTES = NBUF * STAGE * sizeof(T);
   static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
@@ -84,9 +78,8 @@ __device__ __forceinline__ f32x8 load_row_frag(const float* row, bool valid, int
 // pass 1 running sums of one lane (one query, the keys of its half-wave).
 // Level-1 sums are scaled to the current running max m and absorb one 32-key
 // block at a time (block sums first); every kFlush blocks they move into
-// level-2 sums kept at their own max m2 (every two blocks in the pipelined
-// loop, every kFlush blocks otherwise). At 262144 keys this keeps every fp32
-// chain at a few thousand additions at most instead of 131072.
+// level-2 sums kept at their own max m2 every kFlush blocks. At 262144 keys
+// this keeps every fp32 chain at a few hundred additions instead of 131072.
 struct OnlineSums {
   float m = -INFINITY, l = 0.f, aD = 0.f, ac = 0.f, ae = 0.f, ah = 0.f;
   float m2 = -INFINITY, l2 = 0.f, aD2 = 0.f, ac2 = 0.f, ae2 = 0.f, ah2 = 0.f;
@@ -194,7 +187,6 @@ __global__ __launch_bounds__(256, (QueryCfg<T, D, GRADQ>::OCC2 ? 2 : 1)) void qu
   using E = Elem<T>;
   using F = typename E::frag;
   constexpr int BK = Cfg::BK, LDK = Cfg::LDK, NCH = Cfg::NCH, NDB = Cfg::NDB, NBUF = Cfg::NBUF;
-  constexpr bool PIPE = Cfg::PIPE;
   constexpr bool SWZ = Cfg::SWZ;
   constexpr int ROWLEN = SWZ ? D : LDK;
   // [NBUF][4][BK][ROWLEN]: K, gK, V, gV of a stage
@@ -346,96 +338,35 @@ __global__ __launch_bounds__(256, (QueryCfg<T, D, GRADQ>::OCC2 ? 2 : 1)) void qu
     }
   };
 
-  // prologue: stages 0 .. AHEAD-1 in LDS
-#pragma unroll
-  for (int n = 0; n < Cfg::AHEAD; ++n) {
-    if (n < nblk) {
-      prefetch(n);
-      commit(n);
-    }
-  }
+  prefetch(0);  // nblk >= 1
+  commit(0);
   __syncthreads();
 
   using F0 = std::integral_constant<bool, false>;
   using F1 = std::integral_constant<bool, true>;
   const bool last_partial = N % BK != 0;
-  if constexpr (PIPE) {
-    Tiles tA, tB;
-    Frags fA, fB;
-    recompute(0, tA, 0, NCH);
-    // Iteration n: recompute n+1 (MFMA), elementwise n (VALU), outputs n-1
-    // (MFMA). The three are independent. The body runs as two phases (fenced
-    // with sched_barrier so the scheduler cannot hoist every LDS read), each
-    // pairing half the MFMAs with half the VALU work; in the steady state
-    // (1 <= n <= nblk-3, no tail) a phase is branch-free, so the MFMA and
-    // VALU streams interleave.
-    auto body = [&](auto steady, auto tail, int n, Tiles& cur, Tiles& nxt, Frags& fcur, Frags& fprev) __attribute__((always_inline)) {
-      constexpr bool STEADY = decltype(steady)::value;
-      const bool pf = STEADY || n + 2 < nblk;
-      const bool rec = STEADY || n + 1 < nblk;
-      const bool out = STEADY || n >= 1;
-      if (pf) prefetch(n + 2);  // its buffer last held stage n-2, read in iteration n-1
-#pragma unroll
-      for (int ph = 0; ph < 2; ++ph) {
-        if (rec) recompute(n + 1, nxt, ph * NCH / 2, (ph + 1) * NCH / 2);
-        elementwise(tail, n, ph, cur, fcur);
-        if (out) outputs(n - 1, ph, fprev);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-      if (pf) commit(n + 2);
-      __syncthreads();
-    };
-    auto edge = [&](int n, Tiles& cur, Tiles& nxt, Frags& fcur, Frags& fprev) __attribute__((always_inline)) {
-      if (n == nblk - 1 && last_partial)
-        body(F0{}, F1{}, n, cur, nxt, fcur, fprev);
-      else
-        body(F0{}, F0{}, n, cur, nxt, fcur, fprev);
-      if constexpr (!GRADQ) st.flush();
-    };
-    edge(0, tA, tB, fA, fB);
-    int n = 1;
-    for (; n + 3 < nblk; n += 2) {
-      body(F1{}, F0{}, n, tB, tA, fB, fA);
-      body(F1{}, F0{}, n + 1, tA, tB, fA, fB);
-      if constexpr (!GRADQ) st.flush();  // level-1 chains of two blocks
-    }
-    for (; n < nblk; ++n) {
-      if (n & 1)
-        edge(n, tB, tA, fB, fA);
-      else
-        edge(n, tA, tB, fA, fB);
-    }
+  Tiles t;
+  Frags f;
+  for (int n = 0; n < nblk; ++n) {
+    const bool pf = n + 1 < nblk;
+    if (pf) prefetch(n + 1);
+    recompute(n, t, 0, NCH);
 #pragma unroll
     for (int cc = 0; cc < 2; ++cc) {
-      if ((nblk - 1) & 1)
-        outputs(nblk - 1, cc, fB);
+      if (n == nblk - 1 && last_partial)
+        elementwise(F1{}, n, cc, t, f);
       else
-        outputs(nblk - 1, cc, fA);
+        elementwise(F0{}, n, cc, t, f);
+      outputs(n, cc, f);
     }
-  } else {
-    Tiles t;
-    Frags f;
-    for (int n = 0; n < nblk; ++n) {
-      const bool pf = n + 1 < nblk;
-      if (pf) prefetch(n + 1);
-      recompute(n, t, 0, NCH);
-#pragma unroll
-      for (int cc = 0; cc < 2; ++cc) {
-        if (n == nblk - 1 && last_partial)
-          elementwise(F1{}, n, cc, t, f);
-        else
-          elementwise(F0{}, n, cc, t, f);
-        outputs(n, cc, f);
+    if constexpr (!GRADQ) {
+      if (++nflush == kFlush) {
+        st.flush();
+        nflush = 0;
       }
-      if constexpr (!GRADQ) {
-        if (++nflush == kFlush) {
-          st.flush();
-          nflush = 0;
-        }
-      }
-      if (pf) commit(n + 1);  // its buffer last held stage n-1, read in iteration n-1
-      __syncthreads();
     }
+    if (pf) commit(n + 1);  // its buffer last held stage n-1, read in iteration n-1
+    __syncthreads();
   }
 
   if constexpr (!GRADQ) {
