@@ -225,7 +225,6 @@ __global__ __launch_bounds__(256, (QueryCfg<T, D, GRADQ>::OCC2 ? 2 : 1)) void qu
 
   const float sl2 = scale * kLog2e;
   OnlineSums st;  // pass 1 state
-  int nflush = 0;
   // pass 2q state: the lane's row scalars and the output accumulators
   // (gradQ^T, graddO^T: d rows x the wave's 32 queries)
   float l2 = INFINITY, Dq = 0.f, cq = 0.f, rq = 0.f;
@@ -347,27 +346,32 @@ __global__ __launch_bounds__(256, (QueryCfg<T, D, GRADQ>::OCC2 ? 2 : 1)) void qu
   const bool last_partial = N % BK != 0;
   Tiles t;
   Frags f;
-  for (int n = 0; n < nblk; ++n) {
-    const bool pf = n + 1 < nblk;
-    if (pf) prefetch(n + 1);
+  // one iteration per 32-key block; all but the last are branch-free (every
+  // key valid, next stage exists), so each is one straight-line block the
+  // scheduler can interleave freely
+  auto iteration = [&](auto last, auto tail, int n) __attribute__((always_inline)) {
+    constexpr bool LAST = decltype(last)::value;
+    if constexpr (!LAST) prefetch(n + 1);  // its buffer last held stage n-1, read in iteration n-1
     recompute(n, t, 0, NCH);
 #pragma unroll
     for (int cc = 0; cc < 2; ++cc) {
-      if (n == nblk - 1 && last_partial)
-        elementwise(F1{}, n, cc, t, f);
-      else
-        elementwise(F0{}, n, cc, t, f);
+      elementwise(tail, n, cc, t, f);
       outputs(n, cc, f);
     }
-    if constexpr (!GRADQ) {
-      if (++nflush == kFlush) {
-        st.flush();
-        nflush = 0;
-      }
-    }
-    if (pf) commit(n + 1);  // its buffer last held stage n-1, read in iteration n-1
+    if constexpr (!LAST) commit(n + 1);
     __syncthreads();
+  };
+  // pass 1 flushes its level-1 sums every kFlush blocks (outside the
+  // branch-free inner loop)
+  for (int n0 = 0; n0 < nblk - 1; n0 += kFlush) {
+    const int n1 = min(n0 + kFlush, nblk - 1);
+    for (int n = n0; n < n1; ++n) iteration(F0{}, F0{}, n);
+    if constexpr (!GRADQ) st.flush();
   }
+  if (last_partial)
+    iteration(F1{}, F1{}, nblk - 1);
+  else
+    iteration(F1{}, F0{}, nblk - 1);
 
   if constexpr (!GRADQ) {
     st.flush();
