@@ -10,9 +10,13 @@
 //
 // gfx950 schedule: a workgroup of 4 waves owns 128 keys (32 per wave) and
 // streams the queries (Q, gQ, dO and their row scalars) in 32-row stages
-// through two LDS buffers, issuing each stage's global reads one stage ahead. Per 32-query block a wave builds S, G, dP, H (queries x its keys)
-// with MFMA, so each lane holds one key and 16 queries; the queries' row
-// scalars come from LDS as broadcast reads. P, dS, dS2, A then feed the next
+// through two LDS buffers, issuing each stage's global reads one stage ahead.
+// Per 32-query block a wave builds S, G, dP, H (queries x its keys) with
+// MFMA, so each lane holds one key and 16 queries. The dP, G and H
+// accumulators start from the queries' row scalars (-D, -c/s, -r, read from
+// LDS as broadcast reads), so the MFMAs deliver dP - D, G/s - c/s and H - r
+// and the elementwise step has no per-element subtractions left; LSE enters
+// the exponent. P, dS, dS2, A then feed the next
 // MFMAs straight from the accumulator registers as B operands (k = queries in
 // accumulator row order), against Q^T, gQ^T, dO^T read from the LDS stage with
 // transpose loads in the same order. gradK^T and gradV^T stay in registers for
@@ -66,15 +70,29 @@ __device__ __forceinline__ f32x8 load_key_frag(const float* row, bool valid, int
   return f;
 }
 
+// A per-query-row vector of the stage (LDS) laid out as an accumulator: slot
+// i holds row acc_row(h, i), i.e. four broadcast reads of 4 consecutive rows.
+__device__ __forceinline__ f32x16 rows_as_acc(const float* v) {
+  const int h = lane_id() >> 5;
+  f32x16 a;
+#pragma unroll
+  for (int g = 0; g < 4; ++g) {
+    const f32x4 x = *reinterpret_cast<const f32x4*>(v + 8 * g + 4 * h);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) a[4 * g + e] = x[e];
+  }
+  return a;
+}
+
 // Elementwise step of 16-query chunk cc of a 32-query block (slot i <-> query
 // row acc_row(h, i), lane <-> key), turned into B operands with k = queries.
-// TAIL zeroes P for keys past the sequence end and for query rows at or past
-// nq_rel.
+// dP, G, H arrive already shifted by their row scalars (the accumulators
+// start at -D, -c/s, -r): dP - D, G/s - c/s, H - r. TAIL zeroes P for keys
+// past the sequence end and for query rows at or past nq_rel.
 template <typename T, bool TAIL>
 __device__ __forceinline__ void key_chunk(int cc, const f32x16& S, const f32x16& G, const f32x16& dP,
-                                          const f32x16& H, const float* sl, const float* sd, const float* sc,
-                                          const float* sr, float sl2, float scale, bool kvalid, int nq_rel,
-                                          typename Elem<T>::frag& fdS, typename Elem<T>::frag& fdS2,
+                                          const f32x16& H, const float* sl, float sl2, float scale, bool kvalid,
+                                          int nq_rel, typename Elem<T>::frag& fdS, typename Elem<T>::frag& fdS2,
                                           typename Elem<T>::frag& fA) {
   const int h = lane_id() >> 5;
   f32x8 dS, dS2, A;
@@ -83,19 +101,16 @@ __device__ __forceinline__ void key_chunk(int cc, const f32x16& S, const f32x16&
     const int g = 2 * cc + gg;
     const int r0 = 8 * g + 4 * h;  // this lane-half's 4 consecutive query rows
     const f32x4 L4 = *reinterpret_cast<const f32x4*>(sl + r0);
-    const f32x4 D4 = *reinterpret_cast<const f32x4*>(sd + r0);
-    const f32x4 C4 = *reinterpret_cast<const f32x4*>(sc + r0);
-    const f32x4 R4 = *reinterpret_cast<const f32x4*>(sr + r0);
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int i = 4 * g + e, s = 4 * gg + e;
       float p = fast_exp2(fmaf(S[i], sl2, -L4[e]));
       if (TAIL && (!kvalid || r0 + e >= nq_rel)) p = 0.f;
-      const float ds = p * (dP[i] - D4[e]);
-      const float gv = fmaf(G[i], scale, -C4[e]);
+      const float ds = p * dP[i];
+      const float gv = G[i] * scale;
       dS[s] = ds;
       A[s] = p * gv;
-      dS2[s] = fmaf(ds, gv, p * (H[i] - R4[e]));
+      dS2[s] = fmaf(ds, gv, p * H[i]);
     }
   }
   to_frag(fdS, dS);
@@ -241,14 +256,16 @@ __global__ __launch_bounds__(256, (KeyCfg<T, D>::OCC2 ? 2 : 1)) void key_kernel(
   struct Tiles {
     f32x16 S, G, dP, H;
   };
-  // d-chunks [c0, c1) of S, G, dP, H of query block n (queries x this wave's keys)
+  // d-chunks [c0, c1) of S, G/s - c/s, dP - D, H - r of query block n
+  // (queries x this wave's keys): the accumulators start from the stage's row
+  // scalars
   auto recompute = [&](int n, Tiles& t, int c0, int c1) __attribute__((always_inline)) {
     const int b = n % NBUF;
     if (c0 == 0) {
       t.S = f32x16{};
-      t.G = f32x16{};
-      t.dP = f32x16{};
-      t.H = f32x16{};
+      t.dP = rows_as_acc(sS(b, 1));
+      t.G = rows_as_acc(sS(b, 2));
+      t.H = rows_as_acc(sS(b, 3));
     }
 #pragma unroll
     for (int c = c0; c < c1; ++c) {
@@ -271,8 +288,8 @@ __global__ __launch_bounds__(256, (KeyCfg<T, D>::OCC2 ? 2 : 1)) void key_kernel(
   auto elementwise = [&](auto tail, int n, int cc, const Tiles& t, Frags& f) __attribute__((always_inline)) {
     constexpr bool TAIL = decltype(tail)::value;
     const int b = n % NBUF;
-    key_chunk<T, TAIL>(cc, t.S, t.G, t.dP, t.H, sS(b, 0), sS(b, 1), sS(b, 2), sS(b, 3), sl2, scale, kvalid,
-                       N - n * BQ, f.dS[cc], f.dS2[cc], f.A[cc]);
+    key_chunk<T, TAIL>(cc, t.S, t.G, t.dP, t.H, sS(b, 0), sl2, scale, kvalid, N - n * BQ, f.dS[cc], f.dS2[cc],
+                       f.A[cc]);
   };
   auto outputs = [&](int n, int cc, const Frags& f) __attribute__((always_inline)) {
     const int b = n % NBUF;

@@ -17,6 +17,8 @@
 //            r = ae/l - D c + ah/l, LSE = m + ln l.
 //   pass 2q: dS  = P (dP - D),  A = P (G - c),  dS2 = dS (G - c) + P (H - r),
 //            gradQ = s (dS2 K + dS gK),  graddO = A V + P gV.
+//            Pass 1 hands the scalars over as LSE log2(e), -D, -c/s and -r
+//            (the key-major kernel starts its dP, G, H accumulators from them).
 //
 // gfx950 schedule: a workgroup of 4 waves owns 128 queries (32 per wave) and
 // streams the keys in 32-row stages (K, gK, V, gV) through two LDS buffers,
@@ -149,8 +151,8 @@ __device__ __forceinline__ void online_chunk(int cc, const f32x16& S, const f32x
 }
 
 // pass 2q elementwise step of one 16-key chunk cc of a 32-key block, turned
-// into B operands (k = keys in accumulator row order). TAIL masks keys at
-// relative index >= nvalid_rel.
+// into B operands (k = keys in accumulator row order). Dq, cq, rq are -D, -c,
+// -r of the lane's query. TAIL masks keys at relative index >= nvalid_rel.
 template <typename T, bool TAIL>
 __device__ __forceinline__ void query_chunk(int cc, const f32x16& S, const f32x16& G, const f32x16& dP,
                                             const f32x16& H, float sl2, float scale, float l2, float Dq,
@@ -164,12 +166,12 @@ __device__ __forceinline__ void query_chunk(int cc, const f32x16& S, const f32x1
     const int i = 8 * cc + s;
     float p = fast_exp2(fmaf(S[i], sl2, -l2));
     if (TAIL && acc_row(h, i) >= nvalid_rel) p = 0.f;
-    const float ds = p * (dP[i] - Dq);
-    const float g = fmaf(G[i], scale, -cq);
+    const float ds = p * (dP[i] + Dq);
+    const float g = fmaf(G[i], scale, cq);
     P[s] = p;
     dS[s] = ds;
     A[s] = p * g;
-    dS2[s] = fmaf(ds, g, p * (H[i] - rq));
+    dS2[s] = fmaf(ds, g, p * (H[i] + rq));
   }
   to_frag(fP, P);
   to_frag(fdS, dS);
@@ -227,14 +229,15 @@ __global__ __launch_bounds__(256, (QueryCfg<T, D, GRADQ>::OCC2 ? 2 : 1)) void qu
   OnlineSums st;  // pass 1 state
   // pass 2q state: the lane's row scalars and the output accumulators
   // (gradQ^T, graddO^T: d rows x the wave's 32 queries)
+  // (pass-2 form: LSE * log2(e), -D, -c, -r)
   float l2 = INFINITY, Dq = 0.f, cq = 0.f, rq = 0.f;
   f32x16 accQ[GRADQ ? NDB : 1], accO[GRADQ ? NDB : 1];
   if constexpr (GRADQ) {
     if (qvalid) {
       const size_t o = (size_t)head * N + q;
-      l2 = lse[o];  // row scalars carry LSE * log2(e)
+      l2 = lse[o];
       Dq = Dv[o];
-      cq = cv[o];
+      cq = scale * cv[o];
       rq = rv[o];
     }
 #pragma unroll
@@ -389,14 +392,22 @@ __global__ __launch_bounds__(256, (QueryCfg<T, D, GRADQ>::OCC2 ? 2 : 1)) void qu
     if (h == 0 && qvalid) {
       const float inv = 1.f / L;
       const float Dr = AD * inv;
-      const float cr = scale * AC * inv;
+      const float cbar = AC * inv;  // c / s
+      const float cr = scale * cbar;
       const float rr = scale * AE * inv - Dr * cr + AH * inv;
       const size_t o = (size_t)head * N + q;
       const float lse2 = mm + log2f(L);
-      lse[o] = lse_natural ? lse2 * kLn2 : lse2;
-      Dv[o] = Dr;
-      cv[o] = cr;
-      rv[o] = rr;
+      if (lse_natural) {  // the row statistics themselves
+        lse[o] = lse2 * kLn2;
+        Dv[o] = Dr;
+        cv[o] = cr;
+        rv[o] = rr;
+      } else {  // pass-2 form: LSE * log2(e), -D, -c/s, -r
+        lse[o] = lse2;
+        Dv[o] = -Dr;
+        cv[o] = -cbar;
+        rv[o] = -rr;
+      }
     }
   } else {
     // accQ[j] slot i holds d = 32 j + acc_row(h, i) of this lane's query

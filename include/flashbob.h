@@ -78,8 +78,9 @@ size_t flashbob_workspace_bytes(int B, int H, int N, int d);
  *   scale            softmax scale s (finite; commonly 1/sqrt(d))
  *   workspace        device buffer of at least flashbob_workspace_bytes(B,H,N,d)
  *                    bytes; its contents on entry do not matter and on return
- *                    hold the row scalars (LSE * log2(e), D, c, r) as
- *                    [4][B][H][N] float32.
+ *                    hold the row scalars in the form pass 2 consumes,
+ *                    (LSE * log2(e), -D, -c/s, -r) as [4][B][H][N] float32
+ *                    (flashbob_rowstats returns them plainly).
  * Pass 1 (one kernel) computes the row scalars of every query. Pass 2
  * recomputes the score tiles and contracts them into the outputs in two
  * kernels: a query-major sweep producing gradQ and graddO and a key-major
@@ -96,7 +97,7 @@ int flashbob_bob(const void* Q, const void* K, const void* V, const void* dO,
  * calling pass1, pass2_query and pass2_key in this order on one stream with
  * the same buffers is exactly flashbob_bob (the two pass-2 calls are
  * independent of each other).
- *   pass1:       writes the row scalars (LSE, D, c, r) into `workspace`;
+ *   pass1:       writes the row scalars (pass-2 form, see above) into `workspace`;
  *                touches no output.
  *   pass2_query: reads the row scalars from `workspace`, writes gradQ and
  *                graddO (query-major sweep over the keys).
