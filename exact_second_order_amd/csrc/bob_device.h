@@ -235,6 +235,16 @@ __device__ __forceinline__ void load_tile_sw_wave(bf16* t, const bf16* src, int 
   }
 }
 
+// Negate an operand fragment in place (sign bits only, exact).
+__device__ __forceinline__ void negate(bf16x8& f) {
+  typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+  f = __builtin_bit_cast(bf16x8, __builtin_bit_cast(u32x4, f) ^ 0x80008000u);
+}
+__device__ __forceinline__ void negate(f32x8& f) {
+  typedef unsigned u32x8 __attribute__((ext_vector_type(8)));
+  f = __builtin_bit_cast(f32x8, __builtin_bit_cast(u32x8, f) ^ 0x80000000u);
+}
+
 // Wait for this wave's outstanding global loads, including direct-to-LDS ones.
 __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 

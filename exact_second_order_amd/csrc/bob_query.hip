@@ -111,15 +111,15 @@ __device__ __forceinline__ void online_chunk(int cc, const f32x16& S, const f32x
                                              float& mu) {
   const int h = lane_id() >> 5;
   if (cc == 0) {
-    // block maximum of x = S * scale * log2(e) (taken on the product, which
-    // is canonical, so max needs no NaN quieting, and which has the right
-    // order for either sign of the scale)
+    // block maximum of x = S * scale * log2(e); the caller makes the scale
+    // non-negative (sl2 >= 0), so it is the maximum of S times sl2
     float mb = -INFINITY;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const bool ok = !TAIL || acc_row(h, i) < nvalid_rel;
-      if (ok) mb = fmaxf(mb, S[i] * sl2);
+      if (ok) mb = fmaxf(mb, S[i]);
     }
+    mb *= sl2;
     const float mn = fmaxf(st.m, mb);
     mu = (mn == -INFINITY) ? 0.f : mn;
     const float alpha = fast_exp2(st.m - mu);
@@ -225,6 +225,17 @@ __global__ __launch_bounds__(256, (QueryCfg<T, D, GRADQ>::OCC2 ? 2 : 1)) void qu
     }
   }
 
+  // Pass 1 works with |scale|: for a negative scale it negates Q and gQ, which
+  // leaves s S and s G unchanged and lets the online maximum be taken on S.
+  const float sgn = (!GRADQ && scale < 0.f) ? -1.f : 1.f;
+  if (sgn < 0.f) {
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+      negate(fQ[c]);
+      negate(fgQ[c]);
+    }
+  }
+  scale *= sgn;
   const float sl2 = scale * kLog2e;
   OnlineSums st;  // pass 1 state
   // pass 2q state: the lane's row scalars and the output accumulators
@@ -392,8 +403,10 @@ __global__ __launch_bounds__(256, (QueryCfg<T, D, GRADQ>::OCC2 ? 2 : 1)) void qu
     if (h == 0 && qvalid) {
       const float inv = 1.f / L;
       const float Dr = AD * inv;
-      const float cbar = AC * inv;  // c / s
-      const float cr = scale * cbar;
+      // scale is |s| here and G carried the sign of s, so c = |s| AC / L and
+      // c / s = sgn AC / L
+      const float cr = scale * AC * inv;
+      const float cbar = sgn * AC * inv;
       const float rr = scale * AE * inv - Dr * cr + AH * inv;
       const size_t o = (size_t)head * N + q;
       const float lse2 = mm + log2f(L);
