@@ -30,7 +30,9 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
-__device__ __forceinline__ int wave_id() { return threadIdx.x >> 6; }
+// (read from the first lane, so that it and everything derived from it stays
+// in scalar registers)
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
 
 // Row of the accumulator layout held by (lane half h, slot i).
 __device__ __forceinline__ constexpr int acc_row(int h, int i) { return 8 * (i >> 2) + 4 * h + (i & 3); }
@@ -205,20 +207,25 @@ __device__ __forceinline__ bf16x8 ld_cols_perm_sw(const bf16* t, int krow0, int 
   return __builtin_bit_cast(bf16x8, v);
 }
 
+// Raw buffer resource over `bytes` bytes at p: loads at byte offsets past the
+// end return zero. (Word 3 is the gfx9-family raw-buffer format.)
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* p, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, bytes, 0x00020000);
+}
+
 // Direct global -> LDS copy of a 32 x 64 bf16 tile into swizzled layout, one
-// global_load_lds_dwordx4 per wave: wave w fills rows 8w .. 8w+7 (the
+// buffer_load_dwordx4 ... lds per wave: wave w fills rows 8w .. 8w+7 (the
 // hardware writes lane L's 16 bytes at LDS chunk L of the wave's window, so
-// lane L fetches the global chunk that belongs there). Rows at or past
-// `nvalid` (>= 1) re-read row nvalid-1: every address stays inside the source,
-// and callers mask those rows.
+// lane L fetches the global chunk that belongs there). The source is a buffer
+// of `nvalid` rows, so rows at or past nvalid arrive as zeros (callers mask
+// them); the per-lane offset is loop-invariant and the rest is scalar.
 __device__ __forceinline__ void load_tile_sw(bf16* t, const bf16* src, int nvalid) {
   const int l = lane_id(), w = wave_id();
   const int row = 8 * w + (l >> 3);
   const int c = (l & 7) ^ swz(row);
-  const int srow = row < nvalid ? row : nvalid - 1;
   typedef __attribute__((address_space(3))) void lds_void;
-  __builtin_amdgcn_global_load_lds((const void*)(src + srow * 64 + 8 * c), (lds_void*)(t + 8 * w * 64), 16, 0,
-                                   0);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(buffer_rsrc(src, nvalid * 128), (lds_void*)(t + 8 * w * 64), 16,
+                                           row * 128 + 16 * c, 0, 0, 0);
 }
 
 // The same copy of a 32 x 64 tile done by one wave alone (4 loads).

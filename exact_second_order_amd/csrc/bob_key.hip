@@ -212,18 +212,18 @@ __global__ __launch_bounds__(256, (KeyCfg<T, D>::OCC2 ? 2 : 1)) void key_kernel(
     const int q0 = n * BQ;
     const int nq = min(BQ, N - q0);
     if constexpr (SWZ) {
-      const int b = n % NBUF;
+      const int b = n & (NBUF - 1);
       load_tile_sw(tile(b, 0), Q + hoff + (size_t)q0 * D, nq);
       load_tile_sw(tile(b, 1), gQ + hoff + (size_t)q0 * D, nq);
       load_tile_sw(tile(b, 2), dO + hoff + (size_t)q0 * D, nq);
-      if (w < 2) {
-        // waves 0 and 1 fetch (LSE*log2e, D) and (c, r): lane L -> array
-        // 2w + L/32, row L%32, written at LDS float L of the wave's window
-        const int a = 2 * w + (l >> 5), i = l & 31;
-        const float* arr = a == 0 ? lse2 : a == 1 ? Dv : a == 2 ? cv : rv;
-        const size_t o = soff + q0 + (i < nq ? i : nq - 1);
+      // wave w fetches row scalar w (LSE*log2e, -D, -c/s, -r) of the stage's
+      // queries: lane L < 32 -> row L, written at LDS float L of sS(b, w);
+      // rows past the end read as zero
+      if (l < 32) {
+        const float* arr = w == 0 ? lse2 : w == 1 ? Dv : w == 2 ? cv : rv;
         typedef __attribute__((address_space(3))) void lds_void;
-        __builtin_amdgcn_global_load_lds((const void*)(arr + o), (lds_void*)(sS(b, 0) + 64 * w), 4, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(buffer_rsrc(arr + soff + q0, nq * 4), (lds_void*)sS(b, w), 4,
+                                                 4 * l, 0, 0, 0);
       }
     } else {
       pq.load(Q + hoff + (size_t)q0 * D, nq);
@@ -245,7 +245,7 @@ __global__ __launch_bounds__(256, (KeyCfg<T, D>::OCC2 ? 2 : 1)) void key_kernel(
     if constexpr (SWZ) {
       wait_vmem();
     } else {
-      const int b = n % NBUF;
+      const int b = n & (NBUF - 1);
       pq.store(sQ(b, 0, 0, 0), LDQ);
       pg.store(sQ(b, 1, 0, 0), LDQ);
       pd.store(sQ(b, 2, 0, 0), LDQ);
@@ -260,7 +260,7 @@ __global__ __launch_bounds__(256, (KeyCfg<T, D>::OCC2 ? 2 : 1)) void key_kernel(
   // (queries x this wave's keys): the accumulators start from the stage's row
   // scalars
   auto recompute = [&](int n, Tiles& t, int c0, int c1) __attribute__((always_inline)) {
-    const int b = n % NBUF;
+    const int b = n & (NBUF - 1);
     if (c0 == 0) {
       t.S = f32x16{};
       t.dP = rows_as_acc(sS(b, 1));
@@ -287,12 +287,12 @@ __global__ __launch_bounds__(256, (KeyCfg<T, D>::OCC2 ? 2 : 1)) void key_kernel(
   // and query rows past the end (last query block)
   auto elementwise = [&](auto tail, int n, int cc, const Tiles& t, Frags& f) __attribute__((always_inline)) {
     constexpr bool TAIL = decltype(tail)::value;
-    const int b = n % NBUF;
+    const int b = n & (NBUF - 1);
     key_chunk<T, TAIL>(cc, t.S, t.G, t.dP, t.H, sS(b, 0), sl2, scale, kvalid, N - n * BQ, f.dS[cc], f.dS2[cc],
                        f.A[cc]);
   };
   auto outputs = [&](int n, int cc, const Frags& f) __attribute__((always_inline)) {
-    const int b = n % NBUF;
+    const int b = n & (NBUF - 1);
 #pragma unroll
     for (int j = 0; j < NDB; ++j) {
       // lane <-> d, k over this chunk's queries (accumulator row order)
@@ -314,6 +314,9 @@ __global__ __launch_bounds__(256, (KeyCfg<T, D>::OCC2 ? 2 : 1)) void key_kernel(
   const bool last_partial = N % BQ != 0;
   Tiles t;
   Frags f;
+  // unrolled by two from n = 0, so that the stage buffer index is a
+  // compile-time constant in the unrolled body
+#pragma unroll 2
   for (int n = 0; n < nblk; ++n) {
     const bool pf = n + 1 < nblk;
     if (pf) prefetch(n + 1);

@@ -267,7 +267,7 @@ __global__ __launch_bounds__(256, (QueryCfg<T, D, GRADQ>::OCC2 ? 2 : 1)) void qu
     const int k0 = n * BK;
     const int nk = min(BK, N - k0);
     if constexpr (SWZ) {
-      const int b = n % NBUF;
+      const int b = n & (NBUF - 1);
       load_tile_sw(tile(b, 0), K + hoff + (size_t)k0 * D, nk);
       load_tile_sw(tile(b, 1), gK + hoff + (size_t)k0 * D, nk);
       load_tile_sw(tile(b, 2), V + hoff + (size_t)k0 * D, nk);
@@ -283,7 +283,7 @@ __global__ __launch_bounds__(256, (QueryCfg<T, D, GRADQ>::OCC2 ? 2 : 1)) void qu
     if constexpr (SWZ) {
       wait_vmem();
     } else {
-      const int b = n % NBUF;
+      const int b = n & (NBUF - 1);
       pk.store(sK(b, 0, 0, 0), LDK);
       pgk.store(sK(b, 1, 0, 0), LDK);
       pv.store(sK(b, 2, 0, 0), LDK);
@@ -297,7 +297,7 @@ __global__ __launch_bounds__(256, (QueryCfg<T, D, GRADQ>::OCC2 ? 2 : 1)) void qu
   };
   // d-chunks [c0, c1) of the recompute products of block n
   auto recompute = [&](int n, Tiles& t, int c0, int c1) __attribute__((always_inline)) {
-    const int b = n % NBUF;
+    const int b = n & (NBUF - 1);
     if (c0 == 0) {
       t.S = f32x16{};
       t.G = f32x16{};
@@ -335,7 +335,7 @@ __global__ __launch_bounds__(256, (QueryCfg<T, D, GRADQ>::OCC2 ? 2 : 1)) void qu
   // output products of 16-key chunk cc of block n (pass 2q)
   auto outputs = [&](int n, int cc, const Frags& f) __attribute__((always_inline)) {
     if constexpr (GRADQ) {
-      const int b = n % NBUF;
+      const int b = n & (NBUF - 1);
 #pragma unroll
       for (int j = 0; j < NDB; ++j) {
         // lane <-> d, k over this chunk's keys (accumulator row order)
@@ -377,9 +377,16 @@ __global__ __launch_bounds__(256, (QueryCfg<T, D, GRADQ>::OCC2 ? 2 : 1)) void qu
   };
   // pass 1 flushes its level-1 sums every kFlush blocks (outside the
   // branch-free inner loop)
+  // (n0 is a multiple of kFlush and the steady iterations go in pairs from
+  // it, so every stage buffer index below is a compile-time constant)
   for (int n0 = 0; n0 < nblk - 1; n0 += kFlush) {
     const int n1 = min(n0 + kFlush, nblk - 1);
-    for (int n = n0; n < n1; ++n) iteration(F0{}, F0{}, n);
+    const int npairs = (n1 - n0) >> 1;
+    for (int i = 0; i < npairs; ++i) {
+      iteration(F0{}, F0{}, n0 + 2 * i);
+      iteration(F0{}, F0{}, n0 + 2 * i + 1);
+    }
+    if ((n1 - n0) & 1) iteration(F0{}, F0{}, n1 - 1);
     if constexpr (!GRADQ) st.flush();
   }
   if (last_partial)
