@@ -314,23 +314,27 @@ __global__ __launch_bounds__(256, (KeyCfg<T, D>::OCC2 ? 2 : 1)) void key_kernel(
   const bool last_partial = N % BQ != 0;
   Tiles t;
   Frags f;
-  // unrolled by two from n = 0, so that the stage buffer index is a
-  // compile-time constant in the unrolled body
-#pragma unroll 2
-  for (int n = 0; n < nblk; ++n) {
-    const bool pf = n + 1 < nblk;
-    if (pf) prefetch(n + 1);
-    recompute(n, t, 0, NCH);
+  // iterations in pairs from n = 0, so that the stage buffer index is a
+  // compile-time constant in both halves
+  for (int i = 0; 2 * i < nblk; ++i) {
 #pragma unroll
-    for (int cc = 0; cc < 2; ++cc) {
-      if (ktail || (n == nblk - 1 && last_partial))
-        elementwise(F1{}, n, cc, t, f);
-      else
-        elementwise(F0{}, n, cc, t, f);
-      outputs(n, cc, f);
+    for (int u = 0; u < 2; ++u) {
+      const int n = 2 * i + u;
+      if (u == 1 && n >= nblk) break;  // odd block count: the last pair is a single
+      const bool pf = n + 1 < nblk;
+      if (pf) prefetch(n + 1);
+      recompute(n, t, 0, NCH);
+#pragma unroll
+      for (int cc = 0; cc < 2; ++cc) {
+        if (ktail || (n == nblk - 1 && last_partial))
+          elementwise(F1{}, n, cc, t, f);
+        else
+          elementwise(F0{}, n, cc, t, f);
+        outputs(n, cc, f);
+      }
+      if (pf) commit(n + 1);  // its buffer last held stage n-1, read in iteration n-1
+      __syncthreads();
     }
-    if (pf) commit(n + 1);  // its buffer last held stage n-1, read in iteration n-1
-    __syncthreads();
   }
 
   // accK[j] slot i holds d = 32 j + acc_row(h, i) of this lane's key
