@@ -40,8 +40,9 @@ struct KeyCfg {
   static constexpr bool OCC2 = SWZ;
   static constexpr int NBUF = 2;                       // stage n in use, stage n+1 arriving
   // SWZ: which of the wave's K, gK, V, gV operand tensors (bits 0..3) live in
-  // LDS instead of registers; K (used by two products) stays in registers
-  static constexpr int KLDS = SWZ ? 0xE : 0;
+  // LDS instead of registers: gV only, which is what the register budget of two
+  // waves per SIMD leaves over (every per-block LDS read costs time)
+  static constexpr int KLDS = SWZ ? 0x8 : 0;
   static constexpr int NKLDS = __builtin_popcount(KLDS);
   static constexpr int ROWLEN = SWZ ? D : LDQ;
   static constexpr int QSTAGE = 3 * BQ * ROWLEN;       // Q, gQ, dO elements of one stage
