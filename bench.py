@@ -139,6 +139,8 @@ def main():
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)] for _ in range(args.steps)]
     log(f"[bench] timing {args.steps} steps")
     torch.cuda.synchronize()
+    mem0 = torch.cuda.memory_allocated(dev)
+    torch.cuda.reset_peak_memory_stats(dev)
     t0 = time.perf_counter()
     for i in range(args.steps):
         step(evs[i])
@@ -146,6 +148,12 @@ def main():
     wall = time.perf_counter() - t0
 
     ms_step = wall * 1e3 / args.steps
+    # device memory the timed calls added on top of inputs, outputs and
+    # workspace (the library allocates nothing: expected 0)
+    peak_mem_delta = torch.cuda.max_memory_allocated(dev) - mem0
+    step_ms = sorted(e[0].elapsed_time(e[len(stages)]) for e in evs)
+    ms_median = step_ms[len(step_ms) // 2] if len(step_ms) % 2 else 0.5 * (
+        step_ms[len(step_ms) // 2 - 1] + step_ms[len(step_ms) // 2])
     flops = w.flops
     tflops = flops / (ms_step * 1e-3) / 1e12
     peak = PEAK_TFLOPS[w.dtype_name]
@@ -184,7 +192,8 @@ def main():
         "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d, "dtype": w.dtype_name,
                    "scale": w.scale, "causal": False, "seed": WORKLOADS.index(w),
                    "flops_per_step": flops, "frac_of_peak": round(tflops / peak, 4),
-                   "kernels": per_kernel},
+                   "ms_median_events": round(ms_median, 4), "ms_min_events": round(step_ms[0], 4),
+                   "peak_mem_delta_bytes": int(peak_mem_delta), "kernels": per_kernel},
         "roofline": roofline,
         "cpu_baseline": cpu,
     }
