@@ -26,6 +26,11 @@ readings taken here (listed with the others in the design notes):
 
 Every function works per head on 2-D arrays [N, d] in float64 and
 materialises the N x N quantities; the batched wrappers loop over [B, H].
+
+Causal masking (a reading beyond the abstract, which does not treat masks):
+with causal=True query i attends to keys j <= i only. The masked scores are
+-inf constants, so P, dS, A and dS2 vanish there and no gradient flows
+through them; everything else is unchanged.
 """
 
 import numpy as np
@@ -50,6 +55,15 @@ def _f64(*xs):
     return [np.asarray(x, dtype=np.float64) for x in xs]
 
 
+def _mask_scores(S, qidx, causal):
+    """Scores with the causal mask applied: -inf where key j > query qidx[i]."""
+    if not causal:
+        return S
+    qidx = np.asarray(qidx).reshape(-1, 1)
+    keys = np.arange(S.shape[1]).reshape(1, -1)
+    return np.where(keys > qidx, -np.inf, S)
+
+
 def softmax_rows(S):
     """Row-wise softmax, stabilised by the row maximum (exact in real arithmetic)."""
     S = np.asarray(S, dtype=np.float64)
@@ -58,17 +72,17 @@ def softmax_rows(S):
     return E / E.sum(axis=-1, keepdims=True)
 
 
-def attention_forward(Q, K, V, scale):
+def attention_forward(Q, K, V, scale, causal=False):
     """Softmax attention forward of one head, O = softmax(scale Q K^T) V.
 
     The function whose first and second derivatives the abstract is about.
     """
     Q, K, V = _f64(Q, K, V)
-    P = softmax_rows(scale * (Q @ K.T))
+    P = softmax_rows(_mask_scores(scale * (Q @ K.T), np.arange(Q.shape[0]), causal))
     return P @ V
 
 
-def attention_backward(Q, K, V, dO, scale):
+def attention_backward(Q, K, V, dO, scale, causal=False):
     """Textbook first backward of one attention head (the pass BoB goes through).
 
     Abstract: FlashAttention covers the forward and this first backward; BoB
@@ -77,7 +91,7 @@ def attention_backward(Q, K, V, dO, scale):
       dQ = scale dS K,  dK = scale dS^T Q,  dV = P^T dO.
     """
     Q, K, V, dO = _f64(Q, K, V, dO)
-    P = softmax_rows(scale * (Q @ K.T))
+    P = softmax_rows(_mask_scores(scale * (Q @ K.T), np.arange(Q.shape[0]), causal))
     O = P @ V
     dP = dO @ V.T
     D = np.sum(dO * O, axis=1, keepdims=True)
@@ -85,20 +99,23 @@ def attention_backward(Q, K, V, dO, scale):
     return scale * (dS @ K), scale * (dS.T @ Q), P.T @ dO
 
 
-def bob_objective(Q, K, V, dO, gQ, gK, gV, scale):
+def bob_objective(Q, K, V, dO, gQ, gK, gV, scale, causal=False):
     """Scalar L = <gQ, dQ> + <gK, dK> + <gV, dV> whose gradient BoB returns."""
-    dQ, dK, dV = attention_backward(Q, K, V, dO, scale)
+    dQ, dK, dV = attention_backward(Q, K, V, dO, scale, causal)
     gQ, gK, gV = _f64(gQ, gK, gV)
     return float(np.sum(gQ * dQ) + np.sum(gK * dK) + np.sum(gV * dV))
 
 
-def _tiles(Q, K, V, dO, gQ, gK, gV, scale):
+def _tiles(Q, K, V, dO, gQ, gK, gV, scale, qidx=None, causal=False):
     """All N x N quantities of one head, for the query rows held in Q/dO/gQ.
 
-    Q, dO, gQ may be a block of rows; K, V, gK, gV are always all keys.
-    Every quantity below is row-local, so a row block gives exact rows.
+    Q, dO, gQ may be a block of rows (qidx: their positions in the sequence,
+    default 0..); K, V, gK, gV are always all keys. Every quantity below is
+    row-local, so a row block gives exact rows.
     """
-    S = scale * (Q @ K.T)                       # scores
+    if qidx is None:
+        qidx = np.arange(Q.shape[0])
+    S = _mask_scores(scale * (Q @ K.T), qidx, causal)  # scores
     P = softmax_rows(S)                         # probabilities
     O = P @ V                                   # forward output rows
     D = np.sum(dO * O, axis=1, keepdims=True)   # first-backward row scalar
@@ -114,7 +131,7 @@ def _tiles(Q, K, V, dO, gQ, gK, gV, scale):
     return dict(S=S, P=P, O=O, D=D, dP=dP, dS=dS, G=G, H=H, c=c, r=r, A=A, dS2=dS2)
 
 
-def bob_head(Q, K, V, dO, gQ, gK, gV, scale):
+def bob_head(Q, K, V, dO, gQ, gK, gV, scale, causal=False):
     """Exact BoB of one head: (dL/dQ, dL/dK, dL/dV, dL/ddO), each [N, d].
 
     Abstract: exact BoB of softmax attention; all outputs are affine in the
@@ -130,7 +147,7 @@ def bob_head(Q, K, V, dO, gQ, gK, gV, scale):
       S  = scale Q K^T    -> Q-bar gets scale dS2 K,  K-bar gets scale dS2^T Q
     """
     Q, K, V, dO, gQ, gK, gV = _f64(Q, K, V, dO, gQ, gK, gV)
-    t = _tiles(Q, K, V, dO, gQ, gK, gV, scale)
+    t = _tiles(Q, K, V, dO, gQ, gK, gV, scale, causal=causal)
     gradQ = scale * (t["dS2"] @ K + t["dS"] @ gK)
     gradK = scale * (t["dS2"].T @ Q + t["dS"].T @ gQ)
     gradV = t["A"].T @ dO
@@ -138,33 +155,33 @@ def bob_head(Q, K, V, dO, gQ, gK, gV, scale):
     return gradQ, gradK, gradV, graddO
 
 
-def bob(Q, K, V, dO, gQ, gK, gV, scale):
+def bob(Q, K, V, dO, gQ, gK, gV, scale, causal=False):
     """Batched BoB over leading dims [..., N, d]; each (b, h) slice independently."""
     Q, K, V, dO, gQ, gK, gV = _f64(Q, K, V, dO, gQ, gK, gV)
     lead = Q.shape[:-2]
     outs = [np.empty_like(Q), np.empty_like(K), np.empty_like(V), np.empty_like(dO)]
     for idx in np.ndindex(*lead):
-        res = bob_head(Q[idx], K[idx], V[idx], dO[idx], gQ[idx], gK[idx], gV[idx], scale)
+        res = bob_head(Q[idx], K[idx], V[idx], dO[idx], gQ[idx], gK[idx], gV[idx], scale, causal)
         for o, x in zip(outs, res):
             o[idx] = x
     return tuple(outs)
 
 
-def row_stats_head(Q, K, V, dO, gQ, gK, gV, scale):
+def row_stats_head(Q, K, V, dO, gQ, gK, gV, scale, causal=False):
     """Per-row scalars of one head by their direct definitions: (LSE, D, c, r), each [N].
 
     LSE is the log of the softmax normaliser of scale Q K^T; D is the
     first-backward row scalar; c and r are the two BoB row scalars.
     """
     Q, K, V, dO, gQ, gK, gV = _f64(Q, K, V, dO, gQ, gK, gV)
-    t = _tiles(Q, K, V, dO, gQ, gK, gV, scale)
+    t = _tiles(Q, K, V, dO, gQ, gK, gV, scale, causal=causal)
     S = t["S"]
     m = S.max(axis=1)
     lse = m + np.log(np.exp(S - m[:, None]).sum(axis=1))
     return lse, t["D"][:, 0], t["c"][:, 0], t["r"][:, 0]
 
 
-def row_stats_closed_forms_head(Q, K, V, dO, gQ, gK, gV, scale):
+def row_stats_closed_forms_head(Q, K, V, dO, gQ, gK, gV, scale, causal=False):
     """(D, c, r) of one head through d-vector contractions instead of N x N rowsums.
 
     D = dO . (P V),   c = scale (gQ . (P K) + Q . (P gK)),
@@ -172,7 +189,7 @@ def row_stats_closed_forms_head(Q, K, V, dO, gQ, gK, gV, scale):
     A second route to the row scalars, used to cross-check the first.
     """
     Q, K, V, dO, gQ, gK, gV = _f64(Q, K, V, dO, gQ, gK, gV)
-    P = softmax_rows(scale * (Q @ K.T))
+    P = softmax_rows(_mask_scores(scale * (Q @ K.T), np.arange(Q.shape[0]), causal))
     D = np.sum(dO * (P @ V), axis=1)
     c = scale * (np.sum(gQ * (P @ K), axis=1) + np.sum(Q * (P @ gK), axis=1))
     dS = P * (dO @ V.T - D[:, None])
@@ -182,7 +199,7 @@ def row_stats_closed_forms_head(Q, K, V, dO, gQ, gK, gV, scale):
     return D, c, r
 
 
-def row_stats_online_head(Q, K, V, dO, gQ, gK, gV, scale, block):
+def row_stats_online_head(Q, K, V, dO, gQ, gK, gV, scale, block, causal=False):
     """(LSE, D, c, r) of one head in one sweep over key blocks (online softmax).
 
     The row scalars only need running sums weighted by exp(S - m): l, and the
@@ -201,10 +218,15 @@ def row_stats_online_head(Q, K, V, dO, gQ, gK, gV, scale, block):
     for j0 in range(0, K.shape[0], block):
         j1 = min(j0 + block, K.shape[0])
         S = scale * (Q @ K[j0:j1].T)
+        if causal:  # key j0 + k is masked for query i when j0 + k > i
+            S = np.where(np.arange(j0, j1)[None, :] > np.arange(N)[:, None], -np.inf, S)
         G = scale * (gQ @ K[j0:j1].T + Q @ gK[j0:j1].T)
         dP = dO @ V[j0:j1].T
         H = dO @ gV[j0:j1].T
         m_new = np.maximum(m, S.max(axis=1))
+        # (a block masked for a whole row leaves m at -inf only while every
+        # earlier block was masked too, which never happens: key 0 is always
+        # visible)
         alpha = np.exp(m - m_new)
         Pt = np.exp(S - m_new[:, None])
         l = alpha * l + Pt.sum(axis=1)
@@ -219,7 +241,7 @@ def row_stats_online_head(Q, K, V, dO, gQ, gK, gV, scale, block):
     return m + np.log(l), D, c, r
 
 
-def bob_rows_head(Q, K, V, dO, gQ, gK, gV, scale, rows):
+def bob_rows_head(Q, K, V, dO, gQ, gK, gV, scale, rows, causal=False):
     """gradQ and graddO of one head for the query rows `rows` only (exact).
 
     Both are row-local: every N x N quantity of a query row depends on that
@@ -227,13 +249,13 @@ def bob_rows_head(Q, K, V, dO, gQ, gK, gV, scale, rows):
     """
     Q, K, V, dO, gQ, gK, gV = _f64(Q, K, V, dO, gQ, gK, gV)
     rows = np.asarray(rows)
-    t = _tiles(Q[rows], K, V, dO[rows], gQ[rows], gK, gV, scale)
+    t = _tiles(Q[rows], K, V, dO[rows], gQ[rows], gK, gV, scale, qidx=rows, causal=causal)
     gradQ = scale * (t["dS2"] @ K + t["dS"] @ gK)
     graddO = t["A"] @ V + t["P"] @ gV
     return gradQ, graddO
 
 
-def bob_blocked_head(Q, K, V, dO, gQ, gK, gV, scale, block=1024):
+def bob_blocked_head(Q, K, V, dO, gQ, gK, gV, scale, block=1024, causal=False):
     """bob_head computed over blocks of query rows to bound host memory.
 
     Rows of gradQ and graddO are final per block; gradK and gradV are sums of
@@ -247,7 +269,7 @@ def bob_blocked_head(Q, K, V, dO, gQ, gK, gV, scale, block=1024):
     gradV = np.zeros_like(V)
     for i0 in range(0, N, block):
         I = slice(i0, min(i0 + block, N))
-        t = _tiles(Q[I], K, V, dO[I], gQ[I], gK, gV, scale)
+        t = _tiles(Q[I], K, V, dO[I], gQ[I], gK, gV, scale, qidx=np.arange(N)[I], causal=causal)
         gradQ[I] = scale * (t["dS2"] @ K + t["dS"] @ gK)
         graddO[I] = t["A"] @ V + t["P"] @ gV
         gradK += scale * (t["dS2"].T @ Q[I] + t["dS"].T @ gQ[I])
@@ -255,14 +277,14 @@ def bob_blocked_head(Q, K, V, dO, gQ, gK, gV, scale, block=1024):
     return gradQ, gradK, gradV, graddO
 
 
-def bob_blocked(Q, K, V, dO, gQ, gK, gV, scale, block=1024):
+def bob_blocked(Q, K, V, dO, gQ, gK, gV, scale, block=1024, causal=False):
     """Batched row-blocked BoB over leading dims [..., N, d]."""
     Q, K, V, dO, gQ, gK, gV = _f64(Q, K, V, dO, gQ, gK, gV)
     lead = Q.shape[:-2]
     outs = [np.empty_like(Q), np.empty_like(K), np.empty_like(V), np.empty_like(dO)]
     for idx in np.ndindex(*lead):
         res = bob_blocked_head(Q[idx], K[idx], V[idx], dO[idx], gQ[idx], gK[idx],
-                               gV[idx], scale, block)
+                               gV[idx], scale, block, causal)
         for o, x in zip(outs, res):
             o[idx] = x
     return tuple(outs)

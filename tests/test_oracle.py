@@ -306,3 +306,132 @@ def test_pins_catch_planted_mistakes(name, monkeypatch):
     ref = torch_bob(xs, s)
     worst = max(rel(g, r) for g, r in zip(got, ref))
     assert worst > 1e-3, f"mutation {name} not caught (worst rel {worst})"
+
+
+# ----------------------------------------------------------------------------
+# causal masking: query i attends to keys j <= i (a reading beyond the
+# abstract). Independent routes: torch autograd through a masked torch
+# attention, finite differences, and rows whose result is fixed in closed form.
+
+
+def torch_attn_causal(Q, K, V, scale):
+    N = Q.shape[0]
+    mask = torch.ones(N, K.shape[0], dtype=torch.bool).triu(1)  # key j > query i
+    S = (scale * Q @ K.T).masked_fill(mask, float("-inf"))
+    return torch.softmax(S, dim=-1) @ V
+
+
+def torch_bob_causal(xs, scale):
+    Q, K, V, dO, gQ, gK, gV = [torch.tensor(x, requires_grad=True) for x in xs]
+    f = torch.sum(dO * torch_attn_causal(Q, K, V, scale))
+    dQ, dK, dV = torch.autograd.grad(f, (Q, K, V), create_graph=True)
+    L = torch.sum(gQ * dQ) + torch.sum(gK * dK) + torch.sum(gV * dV)
+    grads = torch.autograd.grad(L, (Q, K, V, dO), allow_unused=True)
+    return [np.zeros(x.shape) if g is None else g.detach().numpy() for g, x in zip(grads, xs[:4])]
+
+
+def L_value_causal(xs, scale):
+    Q, K, V, dO = [torch.tensor(x, requires_grad=True) for x in xs[:4]]
+    f = torch.sum(dO * torch_attn_causal(Q, K, V, scale))
+    dQ, dK, dV = torch.autograd.grad(f, (Q, K, V))
+    gQ, gK, gV = [torch.tensor(x) for x in xs[4:]]
+    return float(torch.sum(gQ * dQ) + torch.sum(gK * dK) + torch.sum(gV * dV))
+
+
+@pytest.mark.parametrize("N,d", [(1, 3), (5, 4), (33, 8), (64, 16)])
+def test_causal_matches_autograd_double_backward(N, d):
+    xs = rand_inputs(N, d, seed=17 * N + d)
+    s = 1.0 / math.sqrt(d)
+    got = oracle.bob_head(*xs, s, causal=True)
+    ref = torch_bob_causal(xs, s)
+    for g, r in zip(got, ref):
+        if np.linalg.norm(r) == 0:
+            assert np.abs(g).max() < 1e-12
+        else:
+            assert rel(g, r) < 1e-12
+
+
+def test_causal_central_finite_differences():
+    N, d = 17, 6
+    xs = rand_inputs(N, d, seed=71)
+    s = 0.4
+    got = oracle.bob_head(*xs, s, causal=True)
+    rng = np.random.default_rng(5)
+    h = 1e-5
+    for k in range(4):
+        u = rng.standard_normal(xs[k].shape)
+        xp, xm = list(xs), list(xs)
+        xp[k] = xs[k] + h * u
+        xm[k] = xs[k] - h * u
+        fd = (L_value_causal(xp, s) - L_value_causal(xm, s)) / (2 * h)
+        an = float(np.sum(got[k] * u))
+        assert abs(fd - an) <= 1e-7 * max(1.0, abs(an)), (k, fd, an)
+
+
+def test_causal_first_and_last_rows():
+    # row 0 sees key 0 alone: P = 1, so dS = A = dS2 = 0 on that row and
+    # gradQ_0 = 0, graddO_0 = gV_0 exactly; the last row sees every key, so
+    # its gradQ and graddO equal the unmasked ones
+    N, d = 29, 8
+    xs = rand_inputs(N, d, seed=8)
+    s = 0.3
+    gq, gk, gv, gdo = oracle.bob_head(*xs, s, causal=True)
+    assert np.abs(gq[0]).max() < 1e-14
+    assert np.abs(gdo[0] - xs[6][0]).max() < 1e-14
+    fq, fk, fv, fdo = oracle.bob_head(*xs, s)
+    assert rel(gq[N - 1], fq[N - 1]) < 1e-13
+    assert rel(gdo[N - 1], fdo[N - 1]) < 1e-13
+    # the last key is seen by the last query only, so its gradK / gradV rows
+    # come from that single (P = softmax weight) entry and differ from the
+    # unmasked ones
+    assert rel(gk[N - 1], fk[N - 1]) > 1e-3
+
+
+def test_causal_hessian_symmetry_and_forms():
+    N, d = 33, 8
+    xs = rand_inputs(N, d, seed=41)
+    hs = rand_inputs(N, d, seed=42)[4:]
+    s = 1.0 / math.sqrt(d)
+    bg = oracle.bob_head(*xs, s, causal=True)
+    bh = oracle.bob_head(*xs[:4], *hs, s, causal=True)
+    lhs = sum(np.sum(h * b) for h, b in zip(hs, bg[:3]))
+    rhs = sum(np.sum(g * b) for g, b in zip(xs[4:], bh[:3]))
+    assert abs(lhs - rhs) <= 1e-12 * max(1.0, abs(lhs))
+    # row-blocked, row-sampled and online forms are exact restrictions
+    bb = oracle.bob_blocked_head(*xs, s, block=10, causal=True)
+    assert max(rel(a, b) for a, b in zip(bb, bg)) < 1e-13
+    rows = np.array([0, 7, 32])
+    rq, rdo = oracle.bob_rows_head(*xs, s, rows, causal=True)
+    assert rel(rq, bg[0][rows]) < 1e-13 and rel(rdo, bg[3][rows]) < 1e-13
+    direct = oracle.row_stats_head(*xs, s, causal=True)
+    online = oracle.row_stats_online_head(*xs, s, block=8, causal=True)
+    closed = oracle.row_stats_closed_forms_head(*xs, s, causal=True)
+    for a, b in zip(direct, online):
+        assert rel(a, b) < 1e-12
+    for a, b in zip(direct[1:], closed):
+        assert rel(a, b) < 1e-12
+
+
+@pytest.mark.parametrize("variant", ["diagonal_masked", "transposed_mask"])
+def test_causal_pins_catch_planted_mask_mistakes(variant, monkeypatch):
+    N, d = 16, 4
+    xs = rand_inputs(N, d, seed=321)
+    s = 0.5
+
+    def mask(S, qidx, causal):
+        if not causal:
+            return S
+        q = np.asarray(qidx).reshape(-1, 1)
+        k = np.arange(S.shape[1]).reshape(1, -1)
+        bad = (k >= q) if variant == "diagonal_masked" else (k < q)
+        # keep at least one key per row so the softmax stays finite
+        bad[:, 0] = bad[:, 0] & (q[:, 0] > 0) if variant == "diagonal_masked" else bad[:, 0]
+        if variant == "diagonal_masked":
+            bad[0, 0] = False
+        return np.where(bad, -np.inf, S)
+
+    monkeypatch.setattr(bob_oracle, "_mask_scores", mask)
+    got = oracle.bob_head(*xs, s, causal=True)
+    ref = torch_bob_causal(xs, s)
+    worst = max(rel(g, r) for g, r in zip(got, ref))
+    assert worst > 1e-3, f"planted {variant} not caught (worst rel {worst})"
