@@ -40,9 +40,10 @@ def kernel_source_hash():
     return h.hexdigest()[:16]
 
 
-def measured_traffic(stage):
+def measured_traffic(stage, causal=False):
     """HBM bytes per launch of `stage` from committed rocprofv3 counters, if
-    they were taken on the current kernel sources; else None."""
+    they were taken on the current kernel sources (and with the same mask);
+    else None."""
     try:
         with open(TRAFFIC_FILE) as f:
             t = json.load(f)
@@ -50,12 +51,14 @@ def measured_traffic(stage):
         return None
     if t.get("kernel_source_sha256_16") != kernel_source_hash():
         return None
-    return t.get("bytes_per_launch", {}).get(stage)
+    return t.get("bytes_per_launch_causal" if causal else "bytes_per_launch", {}).get(stage)
 
 
-def cpu_baseline(w, rows, block=512):
+def cpu_baseline(w, rows, block=512, causal=False):
     """fp64 oracle on `rows` query rows against all keys of head 0 (a bounded
-    sample of the workload), scaled to TFLOP/s with the same flop convention."""
+    sample of the workload), scaled to TFLOP/s with the same flop convention
+    (causal: the sampled rows are the first ones, credited with the key pairs
+    they see)."""
     import numpy as np
     import oracle
     from exact_second_order_amd.inputs import workload_inputs
@@ -67,15 +70,20 @@ def cpu_baseline(w, rows, block=512):
     ins = workload_inputs(w)
     xs = [ins[k][0, 0].to(dtype=__import__("torch").float64).numpy() for k in
           ("Q", "K", "V", "dO", "gQ", "gK", "gV")]
-    for i in (0, 3, 4):  # query-side inputs restricted to the sampled rows
+    # query-side inputs restricted to the sampled rows; causal: the first
+    # `rows` queries see only the first `rows` keys, so that prefix is an exact
+    # causal problem of its own
+    for i in (range(7) if causal else (0, 3, 4)):
         xs[i] = np.ascontiguousarray(xs[i][:rows])
     t0 = time.perf_counter()
-    oracle.bob_blocked_head(*xs, w.scale, block=block)
+    oracle.bob_blocked_head(*xs, w.scale, block=block, causal=causal)
     dt = time.perf_counter() - t0
-    flops = 34.0 * rows * w.N * w.d
+    pairs = rows * (rows + 1) / 2 if causal else rows * w.N
+    flops = 34.0 * pairs * w.d
+    what = f"the first {rows} query rows (causal)" if causal else f"{rows} query rows x all {w.N} keys"
     return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
-            "sample": f"{rows} query rows x all {w.N} keys of one head (d={w.d}), fp64 row-blocked oracle, "
-                      f"{dt:.2f} s; flops counted as 34*rows*N*d"}
+            "sample": f"{what} of one head (d={w.d}), fp64 row-blocked oracle, {dt:.2f} s; "
+                      f"flops counted as 34*d per visible (query, key) pair"}
 
 
 def main():
@@ -84,8 +92,11 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", type=int, default=3, help="index into the workload table")
-    ap.add_argument("--cpu-rows", type=int, default=16384, help="oracle sample size (query rows)")
+    ap.add_argument("--cpu-rows", type=int, default=0,
+                    help="oracle sample size in query rows (default 16384; 32768 with --causal)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--causal", action="store_true",
+                    help="causal masking (not the headline); flops credited for the N(N+1)/2 visible pairs")
     ap.add_argument("--copy-mb", type=int, default=0,
                     help="run one plain device copy of this many MiB first (calibrates HBM byte counters)")
     args = ap.parse_args()
@@ -127,7 +138,7 @@ def main():
         for i, st in enumerate(stages):
             if ev is not None:
                 ev[i].record(stream)
-            fb.bob_stage(st, *x, out=out, workspace=ws, scale=w.scale)
+            fb.bob_stage(st, *x, out=out, workspace=ws, scale=w.scale, causal=args.causal)
         if ev is not None:
             ev[len(stages)].record(stream)
 
@@ -154,26 +165,28 @@ def main():
     step_ms = sorted(e[0].elapsed_time(e[len(stages)]) for e in evs)
     ms_median = step_ms[len(step_ms) // 2] if len(step_ms) % 2 else 0.5 * (
         step_ms[len(step_ms) // 2 - 1] + step_ms[len(step_ms) // 2])
-    flops = w.flops
+    frac_pairs = (w.N + 1) / (2.0 * w.N) if args.causal else 1.0  # visible (query, key) pairs
+    flops = w.flops * frac_pairs
     tflops = flops / (ms_step * 1e-3) / 1e12
     peak = PEAK_TFLOPS[w.dtype_name]
     per_kernel = {}
     for i, st in enumerate(stages):
         ms = sum(e[i].elapsed_time(e[i + 1]) for e in evs) / args.steps
-        kf = 2.0 * units[st] * w.B * w.H * w.N * w.N * w.d
+        kf = 2.0 * units[st] * w.B * w.H * w.N * w.N * w.d * frac_pairs
         per_kernel[st] = {"ms": round(ms, 4), "tflops": round(kf / (ms * 1e-3) / 1e12, 2),
                           "frac": round(kf / (ms * 1e-3) / 1e12 / peak, 4), "units": units[st]}
     log(f"[bench] ms/step {ms_step:.3f}; {tflops:.1f} TFLOP/s = {100 * tflops / peak:.1f}% of {peak} peak; "
         f"kernels {per_kernel}")
     dom = max(stages, key=lambda st: per_kernel[st]["ms"])
     roofline = {"bound": "mfma", "achieved": per_kernel[dom]["tflops"], "peak": peak, "unit": "TFLOP/s",
-                "frac": per_kernel[dom]["frac"], "traffic": measured_traffic(dom),
+                "frac": per_kernel[dom]["frac"], "traffic": measured_traffic(dom, args.causal),
                 "kernel": kernel_names[dom], "launch_ms": per_kernel[dom]["ms"]}
 
     cpu = None
     if not args.no_cpu_baseline:
-        log(f"[bench] cpu baseline: oracle on {args.cpu_rows} query rows")
-        cpu = cpu_baseline(w, args.cpu_rows)
+        rows = args.cpu_rows or (32768 if args.causal else 16384)
+        log(f"[bench] cpu baseline: oracle on {rows} query rows")
+        cpu = cpu_baseline(w, min(rows, w.N), causal=args.causal)
         log(f"[bench] cpu baseline {cpu['value']} TFLOP/s on {cpu['cores']} threads")
 
     res = {
@@ -189,8 +202,9 @@ def main():
         "vs_baseline": None,
         "dtype": w.dtype_name,
         "data": "synthetic",
-        "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d, "dtype": w.dtype_name,
-                   "scale": w.scale, "causal": False, "seed": WORKLOADS.index(w),
+        "config": {"workload": w.name + ("_causal" if args.causal else ""), "B": w.B, "H": w.H, "N": w.N,
+                   "d": w.d, "dtype": w.dtype_name, "scale": w.scale, "causal": bool(args.causal),
+                   "seed": WORKLOADS.index(w),
                    "flops_per_step": flops, "frac_of_peak": round(tflops / peak, 4),
                    "ms_median_events": round(ms_median, 4), "ms_min_events": round(step_ms[0], 4),
                    "peak_mem_delta_bytes": int(peak_mem_delta), "kernels": per_kernel},

@@ -89,12 +89,13 @@ __device__ __forceinline__ f32x16 rows_as_acc(const float* v) {
 // row acc_row(h, i), lane <-> key), turned into B operands with k = queries.
 // dP, G, H arrive already shifted by their row scalars (the accumulators
 // start at -D, -c/s, -r): dP - D, G/s - c/s, H - r. TAIL zeroes P for keys
-// past the sequence end and for query rows at or past nq_rel.
+// past the sequence end and for query rows outside [q_lo, nq_rel) (q_lo: the
+// causal mask, query row >= this lane's key; otherwise <= 0).
 template <typename T, bool TAIL>
 __device__ __forceinline__ void key_chunk(int cc, const f32x16& S, const f32x16& G, const f32x16& dP,
                                           const f32x16& H, const float* sl, float sl2, float scale, bool kvalid,
-                                          int nq_rel, typename Elem<T>::frag& fdS, typename Elem<T>::frag& fdS2,
-                                          typename Elem<T>::frag& fA) {
+                                          int q_lo, int nq_rel, typename Elem<T>::frag& fdS,
+                                          typename Elem<T>::frag& fdS2, typename Elem<T>::frag& fA) {
   const int h = lane_id() >> 5;
   f32x8 dS, dS2, A;
 #pragma unroll
@@ -106,7 +107,7 @@ __device__ __forceinline__ void key_chunk(int cc, const f32x16& S, const f32x16&
     for (int e = 0; e < 4; ++e) {
       const int i = 4 * g + e, s = 4 * gg + e;
       float p = fast_exp2(fmaf(S[i], sl2, -L4[e]));
-      if (TAIL && (!kvalid || r0 + e >= nq_rel)) p = 0.f;
+      if (TAIL && (!kvalid || r0 + e >= nq_rel || r0 + e < q_lo)) p = 0.f;
       const float ds = p * dP[i];
       const float gv = G[i] * scale;
       dS[s] = ds;
@@ -125,7 +126,7 @@ __global__ __launch_bounds__(256, (KeyCfg<T, D>::OCC2 ? 2 : 1)) void key_kernel(
     const T* __restrict__ gQ, const T* __restrict__ gK, const T* __restrict__ gV,
     const float* __restrict__ lse2, const float* __restrict__ Dv, const float* __restrict__ cv,
     const float* __restrict__ rv, float* __restrict__ gradK, float* __restrict__ gradV, int N, int nkblk,
-    float scale) {
+    float scale, int causal) {
   using Cfg = KeyCfg<T, D>;
   using E = Elem<T>;
   using F = typename E::frag;
@@ -289,8 +290,8 @@ __global__ __launch_bounds__(256, (KeyCfg<T, D>::OCC2 ? 2 : 1)) void key_kernel(
   auto elementwise = [&](auto tail, int n, int cc, const Tiles& t, Frags& f) __attribute__((always_inline)) {
     constexpr bool TAIL = decltype(tail)::value;
     const int b = n & (NBUF - 1);
-    key_chunk<T, TAIL>(cc, t.S, t.G, t.dP, t.H, sS(b, 0), sl2, scale, kvalid, N - n * BQ, f.dS[cc], f.dS2[cc],
-                       f.A[cc]);
+    key_chunk<T, TAIL>(cc, t.S, t.G, t.dP, t.H, sS(b, 0), sl2, scale, kvalid, causal ? key - n * BQ : 0,
+                       N - n * BQ, f.dS[cc], f.dS2[cc], f.A[cc]);
   };
   auto outputs = [&](int n, int cc, const Frags& f) __attribute__((always_inline)) {
     const int b = n & (NBUF - 1);
@@ -306,8 +307,13 @@ __global__ __launch_bounds__(256, (KeyCfg<T, D>::OCC2 ? 2 : 1)) void key_kernel(
     }
   };
 
-  prefetch(0);  // nblk >= 1
-  commit(0);
+  // Query blocks visited: causal starts at the block of the workgroup's
+  // first key (queries before it see none of these keys) and masks the
+  // BC / BQ blocks across the diagonal; the rest see every key.
+  const int nstart = causal ? kblk * (Cfg::BC / BQ) : 0;  // even
+  const int ndiag = causal ? min(nblk, nstart + Cfg::BC / BQ) : 0;
+  prefetch(nstart);  // nstart < nblk
+  commit(nstart);
   __syncthreads();
 
   using F0 = std::integral_constant<bool, false>;
@@ -315,9 +321,9 @@ __global__ __launch_bounds__(256, (KeyCfg<T, D>::OCC2 ? 2 : 1)) void key_kernel(
   const bool last_partial = N % BQ != 0;
   Tiles t;
   Frags f;
-  // iterations in pairs from n = 0, so that the stage buffer index is a
-  // compile-time constant in both halves
-  for (int i = 0; 2 * i < nblk; ++i) {
+  // iterations in pairs from the even nstart, so that the stage buffer index
+  // is a compile-time constant in both halves
+  for (int i = nstart >> 1; 2 * i < nblk; ++i) {
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       const int n = 2 * i + u;
@@ -327,7 +333,7 @@ __global__ __launch_bounds__(256, (KeyCfg<T, D>::OCC2 ? 2 : 1)) void key_kernel(
       recompute(n, t, 0, NCH);
 #pragma unroll
       for (int cc = 0; cc < 2; ++cc) {
-        if (ktail || (n == nblk - 1 && last_partial))
+        if (ktail || n < ndiag || (n == nblk - 1 && last_partial))
           elementwise(F1{}, n, cc, t, f);
         else
           elementwise(F0{}, n, cc, t, f);
@@ -359,21 +365,21 @@ __global__ __launch_bounds__(256, (KeyCfg<T, D>::OCC2 ? 2 : 1)) void key_kernel(
 template <typename T, int D>
 hipError_t launch_key(const void* Q, const void* K, const void* V, const void* dO, const void* gQ, const void* gK,
                       const void* gV, const float* lse2, const float* Dv, const float* cv, const float* rv,
-                      float* gradK, float* gradV, int BH, int N, float scale, hipStream_t stream) {
+                      float* gradK, float* gradV, int BH, int N, float scale, int causal, hipStream_t stream) {
   using Cfg = KeyCfg<T, D>;
   const int nkblk = (N + Cfg::BC - 1) / Cfg::BC;
   const long long nblocks = (long long)nkblk * BH;
   if (nblocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   key_kernel<T, D><<<dim3((unsigned)nblocks), dim3(256), 0, stream>>>(
       (const T*)Q, (const T*)K, (const T*)V, (const T*)dO, (const T*)gQ, (const T*)gK, (const T*)gV, lse2, Dv, cv,
-      rv, gradK, gradV, N, nkblk, scale);
+      rv, gradK, gradV, N, nkblk, scale, causal);
   return hipGetLastError();
 }
 
 #define FLASHBOB_INST_KEY(T, D)                                                                            \
   template hipError_t launch_key<T, D>(const void*, const void*, const void*, const void*, const void*,   \
                                        const void*, const void*, const float*, const float*, const float*, \
-                                       const float*, float*, float*, int, int, float, hipStream_t);
+                                       const float*, float*, float*, int, int, float, int, hipStream_t);
 FLASHBOB_INST_KEY(bf16, 64)
 FLASHBOB_INST_KEY(bf16, 128)
 FLASHBOB_INST_KEY(float, 64)

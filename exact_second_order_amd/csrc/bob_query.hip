@@ -184,7 +184,7 @@ __global__ __launch_bounds__(256, (QueryCfg<T, D, GRADQ>::OCC2 ? 2 : 1)) void qu
     const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V, const T* __restrict__ dO,
     const T* __restrict__ gQ, const T* __restrict__ gK, const T* __restrict__ gV, float* __restrict__ lse,
     float* __restrict__ Dv, float* __restrict__ cv, float* __restrict__ rv, float* __restrict__ gradQ,
-    float* __restrict__ graddO, int N, int nqblk, float scale, int lse_natural) {
+    float* __restrict__ graddO, int N, int nqblk, float scale, int lse_natural, int causal) {
   using Cfg = QueryCfg<T, D, GRADQ>;
   using E = Elem<T>;
   using F = typename E::frag;
@@ -205,11 +205,13 @@ __global__ __launch_bounds__(256, (QueryCfg<T, D, GRADQ>::OCC2 ? 2 : 1)) void qu
   };
 
   const int head = blockIdx.x / nqblk;
-  const int qblk = blockIdx.x % nqblk;
+  // (causal: the longest sweeps, the last query blocks, start first)
+  const int qblk = causal ? nqblk - 1 - (int)(blockIdx.x % nqblk) : (int)(blockIdx.x % nqblk);
   const size_t hoff = (size_t)head * N * D;
   const int w = wave_id(), l = lane_id(), h = l >> 5, col = l & 31;
   const int q = qblk * Cfg::BQ + 32 * w + col;  // this lane's query
   const bool qvalid = q < N;
+  const int qlim = causal ? min(N, q + 1) : N;    // keys [0, qlim) are visible to it
 
   // B operands of the wave's 32 queries (lane <-> query, k over d)
   F fQ[NCH], fgQ[NCH], fdO[NCH];
@@ -325,7 +327,7 @@ __global__ __launch_bounds__(256, (QueryCfg<T, D, GRADQ>::OCC2 ? 2 : 1)) void qu
   // operand fragments (pass 2q); TAIL masks keys past the sequence end
   auto elementwise = [&](auto tail, int n, int cc, const Tiles& t, Frags& f) __attribute__((always_inline)) {
     constexpr bool TAIL = decltype(tail)::value;
-    const int nrel = N - n * BK;
+    const int nrel = qlim - n * BK;
     if constexpr (!GRADQ)
       online_chunk<TAIL>(cc, t.S, t.G, t.dP, t.H, sl2, nrel, st, mu);
     else
@@ -358,6 +360,15 @@ __global__ __launch_bounds__(256, (QueryCfg<T, D, GRADQ>::OCC2 ? 2 : 1)) void qu
   using F0 = std::integral_constant<bool, false>;
   using F1 = std::integral_constant<bool, true>;
   const bool last_partial = N % BK != 0;
+  // Key blocks visited and how many of them need no mask. Causal: the
+  // workgroup's queries q0 .. q0+BQ-1 see keys 0 .. q0+BQ-1, and blocks
+  // wholly below q0 are visible to all of them; the blocks across the
+  // diagonal mask per lane at the key limit qlim = q + 1 (the masked path
+  // also covers a partial last block).
+  const int q0 = qblk * Cfg::BQ;
+  const int nvis = causal ? min(nblk, (q0 + Cfg::BQ + BK - 1) / BK) : nblk;
+  const int nfull = causal ? min(nvis, q0 / BK) : (last_partial ? nblk - 1 : nblk);
+  const int nsteady = min(nfull, nvis - 1);
   Tiles t;
   Frags f;
   // one iteration per 32-key block; all but the last are branch-free (every
@@ -379,8 +390,8 @@ __global__ __launch_bounds__(256, (QueryCfg<T, D, GRADQ>::OCC2 ? 2 : 1)) void qu
   // branch-free inner loop)
   // (n0 is a multiple of kFlush and the steady iterations go in pairs from
   // it, so every stage buffer index below is a compile-time constant)
-  for (int n0 = 0; n0 < nblk - 1; n0 += kFlush) {
-    const int n1 = min(n0 + kFlush, nblk - 1);
+  for (int n0 = 0; n0 < nsteady; n0 += kFlush) {
+    const int n1 = min(n0 + kFlush, nsteady);
     const int npairs = (n1 - n0) >> 1;
     for (int i = 0; i < npairs; ++i) {
       iteration(F0{}, F0{}, n0 + 2 * i);
@@ -389,10 +400,12 @@ __global__ __launch_bounds__(256, (QueryCfg<T, D, GRADQ>::OCC2 ? 2 : 1)) void qu
     if ((n1 - n0) & 1) iteration(F0{}, F0{}, n1 - 1);
     if constexpr (!GRADQ) st.flush();
   }
-  if (last_partial)
-    iteration(F1{}, F1{}, nblk - 1);
+  // masked blocks before the last (causal diagonal only; at most BQ/BK - 1)
+  for (int n = nsteady; n < nvis - 1; ++n) iteration(F0{}, F1{}, n);
+  if (nvis - 1 >= nfull)
+    iteration(F1{}, F1{}, nvis - 1);
   else
-    iteration(F1{}, F0{}, nblk - 1);
+    iteration(F1{}, F0{}, nvis - 1);
 
   if constexpr (!GRADQ) {
     st.flush();
@@ -454,21 +467,21 @@ template <typename T, int D, bool GRADQ>
 hipError_t launch_query(const void* Q, const void* K, const void* V, const void* dO, const void* gQ,
                         const void* gK, const void* gV, float* lse, float* Dv, float* cv, float* rv,
                         float* gradQ, float* graddO, int BH, int N, float scale, int lse_natural,
-                        hipStream_t stream) {
+                        int causal, hipStream_t stream) {
   using Cfg = QueryCfg<T, D, GRADQ>;
   const int nqblk = (N + Cfg::BQ - 1) / Cfg::BQ;
   const long long nblocks = (long long)nqblk * BH;
   if (nblocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   query_kernel<T, D, GRADQ><<<dim3((unsigned)nblocks), dim3(256), 0, stream>>>(
       (const T*)Q, (const T*)K, (const T*)V, (const T*)dO, (const T*)gQ, (const T*)gK, (const T*)gV, lse, Dv,
-      cv, rv, gradQ, graddO, N, nqblk, scale, lse_natural);
+      cv, rv, gradQ, graddO, N, nqblk, scale, lse_natural, causal);
   return hipGetLastError();
 }
 
 #define FLASHBOB_INST_QUERY(T, D, G)                                                                      \
   template hipError_t launch_query<T, D, G>(const void*, const void*, const void*, const void*,         \
                                             const void*, const void*, const void*, float*, float*,      \
-                                            float*, float*, float*, float*, int, int, float, int,         \
+                                            float*, float*, float*, float*, int, int, float, int, int,    \
                                             hipStream_t);
 // Pass 1 and pass 2q instantiations are built as separate objects (pass 1
 // with MFMA results kept in VGPRs, which its register budget allows).

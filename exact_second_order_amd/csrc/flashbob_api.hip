@@ -18,11 +18,11 @@ template <typename T, int D, bool GRADQ>
 hipError_t launch_query(const void* Q, const void* K, const void* V, const void* dO, const void* gQ,
                         const void* gK, const void* gV, float* lse, float* Dv, float* cv, float* rv,
                         float* gradQ, float* graddO, int BH, int N, float scale, int lse_natural,
-                        hipStream_t stream);
+                        int causal, hipStream_t stream);
 template <typename T, int D>
 hipError_t launch_key(const void* Q, const void* K, const void* V, const void* dO, const void* gQ, const void* gK,
                       const void* gV, const float* lse2, const float* Dv, const float* cv, const float* rv,
-                      float* gradK, float* gradV, int BH, int N, float scale, hipStream_t stream);
+                      float* gradK, float* gradV, int BH, int N, float scale, int causal, hipStream_t stream);
 }  // namespace flashbob
 
 namespace {
@@ -80,52 +80,59 @@ int check_outputs(const void* const* ins, size_t in_bytes, void* const* outs, co
 }
 
 // The three kernels of the schedule, dispatched on (element type, d).
-enum Stage { kPass1 = 1, kPass2Query = 2, kPass2Key = 4, kAll = 7 };
+enum Stage {
+  kPass1 = FLASHBOB_STAGE_PASS1,
+  kPass2Query = FLASHBOB_STAGE_PASS2_QUERY,
+  kPass2Key = FLASHBOB_STAGE_PASS2_KEY,
+};
 
 template <typename T, int D>
-hipError_t run_stages(int stages, const void* const* in, float* stats, float* gQo, float* gKo, float* gVo,
-                      float* gdOo, int BH, int N, float scale, hipStream_t st) {
+hipError_t run_stages(int stages, int causal, const void* const* in, float* stats, float* gQo, float* gKo,
+                      float* gVo, float* gdOo, int BH, int N, float scale, hipStream_t st) {
   const size_t BHN = (size_t)BH * N;
   // workspace row scalars: LSE * log2(e), D, c, r
   float *lse = stats, *Dv = stats + BHN, *cv = stats + 2 * BHN, *rv = stats + 3 * BHN;
   hipError_t e = hipSuccess;
   if (stages & kPass1) {
     e = flashbob::launch_query<T, D, false>(in[0], in[1], in[2], in[3], in[4], in[5], in[6], lse, Dv, cv, rv,
-                                            nullptr, nullptr, BH, N, scale, 0, st);
+                                            nullptr, nullptr, BH, N, scale, 0, causal, st);
     if (e != hipSuccess) return e;
   }
   if (stages & kPass2Query) {
     e = flashbob::launch_query<T, D, true>(in[0], in[1], in[2], in[3], in[4], in[5], in[6], lse, Dv, cv, rv,
-                                           gQo, gdOo, BH, N, scale, 0, st);
+                                           gQo, gdOo, BH, N, scale, 0, causal, st);
     if (e != hipSuccess) return e;
   }
   if (stages & kPass2Key) {
     e = flashbob::launch_key<T, D>(in[0], in[1], in[2], in[3], in[4], in[5], in[6], lse, Dv, cv, rv, gKo, gVo,
-                                   BH, N, scale, st);
+                                   BH, N, scale, causal, st);
   }
   return e;
 }
 
-hipError_t dispatch(int dtype, int d, int stages, const void* const* in, float* stats, float* gQo, float* gKo,
-                    float* gVo, float* gdOo, int BH, int N, float scale, hipStream_t st) {
+hipError_t dispatch(int dtype, int d, int stages, int causal, const void* const* in, float* stats, float* gQo,
+                    float* gKo, float* gVo, float* gdOo, int BH, int N, float scale, hipStream_t st) {
   if (dtype == FLASHBOB_BF16)
-    return d == 64 ? run_stages<__bf16, 64>(stages, in, stats, gQo, gKo, gVo, gdOo, BH, N, scale, st)
-                   : run_stages<__bf16, 128>(stages, in, stats, gQo, gKo, gVo, gdOo, BH, N, scale, st);
-  return d == 64 ? run_stages<float, 64>(stages, in, stats, gQo, gKo, gVo, gdOo, BH, N, scale, st)
-                 : run_stages<float, 128>(stages, in, stats, gQo, gKo, gVo, gdOo, BH, N, scale, st);
+    return d == 64 ? run_stages<__bf16, 64>(stages, causal, in, stats, gQo, gKo, gVo, gdOo, BH, N, scale, st)
+                   : run_stages<__bf16, 128>(stages, causal, in, stats, gQo, gKo, gVo, gdOo, BH, N, scale, st);
+  return d == 64 ? run_stages<float, 64>(stages, causal, in, stats, gQo, gKo, gVo, gdOo, BH, N, scale, st)
+                 : run_stages<float, 128>(stages, causal, in, stats, gQo, gKo, gVo, gdOo, BH, N, scale, st);
 }
 
-hipError_t dispatch_rowstats(int dtype, int d, const void* const* in, float* lse, float* Dv, float* cv, float* rv,
-                             int BH, int N, float scale, hipStream_t st) {
+template <typename T, int D>
+hipError_t rowstats_launch(const void* const* in, float* lse, float* Dv, float* cv, float* rv, int BH, int N,
+                           float scale, int causal, hipStream_t st) {
+  return flashbob::launch_query<T, D, false>(in[0], in[1], in[2], in[3], in[4], in[5], in[6], lse, Dv, cv, rv,
+                                             nullptr, nullptr, BH, N, scale, 1, causal, st);
+}
+
+hipError_t dispatch_rowstats(int dtype, int d, int causal, const void* const* in, float* lse, float* Dv, float* cv,
+                             float* rv, int BH, int N, float scale, hipStream_t st) {
   if (dtype == FLASHBOB_BF16)
-    return d == 64 ? flashbob::launch_query<__bf16, 64, false>(in[0], in[1], in[2], in[3], in[4], in[5], in[6], lse,
-                                                              Dv, cv, rv, nullptr, nullptr, BH, N, scale, 1, st)
-                   : flashbob::launch_query<__bf16, 128, false>(in[0], in[1], in[2], in[3], in[4], in[5], in[6],
-                                                               lse, Dv, cv, rv, nullptr, nullptr, BH, N, scale, 1, st);
-  return d == 64 ? flashbob::launch_query<float, 64, false>(in[0], in[1], in[2], in[3], in[4], in[5], in[6], lse, Dv,
-                                                           cv, rv, nullptr, nullptr, BH, N, scale, 1, st)
-                 : flashbob::launch_query<float, 128, false>(in[0], in[1], in[2], in[3], in[4], in[5], in[6], lse,
-                                                            Dv, cv, rv, nullptr, nullptr, BH, N, scale, 1, st);
+    return d == 64 ? rowstats_launch<__bf16, 64>(in, lse, Dv, cv, rv, BH, N, scale, causal, st)
+                   : rowstats_launch<__bf16, 128>(in, lse, Dv, cv, rv, BH, N, scale, causal, st);
+  return d == 64 ? rowstats_launch<float, 64>(in, lse, Dv, cv, rv, BH, N, scale, causal, st)
+                 : rowstats_launch<float, 128>(in, lse, Dv, cv, rv, BH, N, scale, causal, st);
 }
 
 size_t stats_bytes(int B, int H, int N) {
@@ -143,10 +150,12 @@ size_t flashbob_workspace_bytes(int B, int H, int N, int d) {
   return stats_bytes(B, H, N);
 }
 
-static int bob_stages(const void* Q, const void* K, const void* V, const void* dO, const void* gQ,
-                      const void* gK, const void* gV, float* gradQ, float* gradK, float* gradV, float* graddO,
-                      int B, int H, int N, int d, float scale, int dtype, void* workspace,
-                      size_t workspace_bytes, void* stream, int stages) {
+int flashbob_bob_ex(const void* Q, const void* K, const void* V, const void* dO, const void* gQ, const void* gK,
+                    const void* gV, float* gradQ, float* gradK, float* gradV, float* graddO, int B, int H, int N,
+                    int d, float scale, int dtype, int flags, int stages, void* workspace, size_t workspace_bytes,
+                    void* stream) {
+  if ((flags & ~FLASHBOB_CAUSAL) != 0 || stages <= 0 || (stages & ~FLASHBOB_STAGES_ALL) != 0)
+    return FLASHBOB_ERR_FLAGS;
   const void* ins[7] = {Q, K, V, dO, gQ, gK, gV};
   size_t numel = 0;
   int rc = check_common(ins, B, H, N, d, scale, dtype, &numel);
@@ -159,45 +168,47 @@ static int bob_stages(const void* Q, const void* K, const void* V, const void* d
   const size_t ob[5] = {numel * 4, numel * 4, numel * 4, numel * 4, ws_need};
   rc = check_outputs(ins, numel * esz, outs, ob, 5);
   if (rc != FLASHBOB_OK) return rc;
-  const hipError_t e = dispatch(dtype, d, stages, ins, static_cast<float*>(workspace), gradQ, gradK, gradV,
-                                graddO, B * H, N, scale, static_cast<hipStream_t>(stream));
+  const hipError_t e = dispatch(dtype, d, stages, (flags & FLASHBOB_CAUSAL) ? 1 : 0, ins,
+                                static_cast<float*>(workspace), gradQ, gradK, gradV, graddO, B * H, N, scale,
+                                static_cast<hipStream_t>(stream));
   return e == hipSuccess ? FLASHBOB_OK : hip_fail(e);
 }
 
 int flashbob_bob(const void* Q, const void* K, const void* V, const void* dO, const void* gQ, const void* gK,
                  const void* gV, float* gradQ, float* gradK, float* gradV, float* graddO, int B, int H, int N,
                  int d, float scale, int dtype, void* workspace, size_t workspace_bytes, void* stream) {
-  return bob_stages(Q, K, V, dO, gQ, gK, gV, gradQ, gradK, gradV, graddO, B, H, N, d, scale, dtype, workspace,
-                    workspace_bytes, stream, kAll);
+  return flashbob_bob_ex(Q, K, V, dO, gQ, gK, gV, gradQ, gradK, gradV, graddO, B, H, N, d, scale, dtype, 0,
+                         FLASHBOB_STAGES_ALL, workspace, workspace_bytes, stream);
 }
 
 int flashbob_bob_pass1(const void* Q, const void* K, const void* V, const void* dO, const void* gQ,
                        const void* gK, const void* gV, float* gradQ, float* gradK, float* gradV, float* graddO,
                        int B, int H, int N, int d, float scale, int dtype, void* workspace,
                        size_t workspace_bytes, void* stream) {
-  return bob_stages(Q, K, V, dO, gQ, gK, gV, gradQ, gradK, gradV, graddO, B, H, N, d, scale, dtype, workspace,
-                    workspace_bytes, stream, kPass1);
+  return flashbob_bob_ex(Q, K, V, dO, gQ, gK, gV, gradQ, gradK, gradV, graddO, B, H, N, d, scale, dtype, 0,
+                         FLASHBOB_STAGE_PASS1, workspace, workspace_bytes, stream);
 }
 
 int flashbob_bob_pass2_query(const void* Q, const void* K, const void* V, const void* dO, const void* gQ,
                              const void* gK, const void* gV, float* gradQ, float* gradK, float* gradV,
                              float* graddO, int B, int H, int N, int d, float scale, int dtype, void* workspace,
                              size_t workspace_bytes, void* stream) {
-  return bob_stages(Q, K, V, dO, gQ, gK, gV, gradQ, gradK, gradV, graddO, B, H, N, d, scale, dtype, workspace,
-                    workspace_bytes, stream, kPass2Query);
+  return flashbob_bob_ex(Q, K, V, dO, gQ, gK, gV, gradQ, gradK, gradV, graddO, B, H, N, d, scale, dtype, 0,
+                         FLASHBOB_STAGE_PASS2_QUERY, workspace, workspace_bytes, stream);
 }
 
 int flashbob_bob_pass2_key(const void* Q, const void* K, const void* V, const void* dO, const void* gQ,
                            const void* gK, const void* gV, float* gradQ, float* gradK, float* gradV,
                            float* graddO, int B, int H, int N, int d, float scale, int dtype, void* workspace,
                            size_t workspace_bytes, void* stream) {
-  return bob_stages(Q, K, V, dO, gQ, gK, gV, gradQ, gradK, gradV, graddO, B, H, N, d, scale, dtype, workspace,
-                    workspace_bytes, stream, kPass2Key);
+  return flashbob_bob_ex(Q, K, V, dO, gQ, gK, gV, gradQ, gradK, gradV, graddO, B, H, N, d, scale, dtype, 0,
+                         FLASHBOB_STAGE_PASS2_KEY, workspace, workspace_bytes, stream);
 }
 
-int flashbob_rowstats(const void* Q, const void* K, const void* V, const void* dO, const void* gQ,
-                      const void* gK, const void* gV, float* lse, float* Dv, float* cv, float* rv, int B, int H,
-                      int N, int d, float scale, int dtype, void* stream) {
+int flashbob_rowstats_ex(const void* Q, const void* K, const void* V, const void* dO, const void* gQ,
+                         const void* gK, const void* gV, float* lse, float* Dv, float* cv, float* rv, int B, int H,
+                         int N, int d, float scale, int dtype, int flags, void* stream) {
+  if ((flags & ~FLASHBOB_CAUSAL) != 0) return FLASHBOB_ERR_FLAGS;
   const void* ins[7] = {Q, K, V, dO, gQ, gK, gV};
   size_t numel = 0;
   int rc = check_common(ins, B, H, N, d, scale, dtype, &numel);
@@ -208,11 +219,16 @@ int flashbob_rowstats(const void* Q, const void* K, const void* V, const void* d
   const size_t ob[4] = {vb, vb, vb, vb};
   rc = check_outputs(ins, numel * esz, outs, ob, 4);
   if (rc != FLASHBOB_OK) return rc;
-  // the row scalars go to the caller's four vectors: they are laid out as
-  // the stats workspace expects only if contiguous, so launch pass 1 per vector set
-  const hipError_t e = dispatch_rowstats(dtype, d, ins, lse, Dv, cv, rv, B * H, N, scale,
-                                         static_cast<hipStream_t>(stream));
+  // pass 1 writing the plain row scalars into the caller's four vectors
+  const hipError_t e = dispatch_rowstats(dtype, d, (flags & FLASHBOB_CAUSAL) ? 1 : 0, ins, lse, Dv, cv, rv, B * H,
+                                         N, scale, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? FLASHBOB_OK : hip_fail(e);
+}
+
+int flashbob_rowstats(const void* Q, const void* K, const void* V, const void* dO, const void* gQ,
+                      const void* gK, const void* gV, float* lse, float* Dv, float* cv, float* rv, int B, int H,
+                      int N, int d, float scale, int dtype, void* stream) {
+  return flashbob_rowstats_ex(Q, K, V, dO, gQ, gK, gV, lse, Dv, cv, rv, B, H, N, d, scale, dtype, 0, stream);
 }
 
 const char* flashbob_strerror(int code) {
@@ -227,11 +243,12 @@ const char* flashbob_strerror(int code) {
     case FLASHBOB_ERR_WORKSPACE: return "workspace too small";
     case FLASHBOB_ERR_ALIAS: return "an output overlaps an input, the workspace or another output";
     case FLASHBOB_ERR_SCALE: return "scale is not finite";
+    case FLASHBOB_ERR_FLAGS: return "unknown flag bits or an empty or unknown stage set";
     case FLASHBOB_ERR_HIP: return g_last_hip_error.c_str();
     default: return "unknown error code";
   }
 }
 
-int flashbob_version(void) { return 100; }
+int flashbob_version(void) { return 101; }
 
 }  // extern "C"

@@ -15,6 +15,8 @@ LIB_PATH = os.path.join(_PKG, "libflashbob.so")
 
 FLASHBOB_F32 = 0
 FLASHBOB_BF16 = 1
+FLASHBOB_CAUSAL = 1
+STAGE_BITS = {"pass1": 1, "pass2_query": 2, "pass2_key": 4}
 
 ERRORS = {
     0: "OK",
@@ -27,6 +29,7 @@ ERRORS = {
     -7: "ERR_WORKSPACE",
     -8: "ERR_ALIAS",
     -9: "ERR_SCALE",
+    -10: "ERR_FLAGS",
     -100: "ERR_HIP",
 }
 
@@ -37,6 +40,8 @@ EXPORTS = (
     "flashbob_bob_pass2_query",
     "flashbob_bob_pass2_key",
     "flashbob_rowstats",
+    "flashbob_bob_ex",
+    "flashbob_rowstats_ex",
     "flashbob_strerror",
     "flashbob_version",
 )
@@ -74,6 +79,10 @@ def load_library(path=LIB_PATH):
         fn.restype = i
     lib.flashbob_rowstats.argtypes = [vp] * 7 + [vp] * 4 + [i, i, i, i, f, i, vp]
     lib.flashbob_rowstats.restype = i
+    lib.flashbob_bob_ex.argtypes = [vp] * 7 + [vp] * 4 + [i, i, i, i, f, i, i, i, vp, sz, vp]
+    lib.flashbob_bob_ex.restype = i
+    lib.flashbob_rowstats_ex.argtypes = [vp] * 7 + [vp] * 4 + [i, i, i, i, f, i, i, vp]
+    lib.flashbob_rowstats_ex.restype = i
     lib.flashbob_strerror.argtypes = [i]
     lib.flashbob_strerror.restype = ctypes.c_char_p
     lib.flashbob_version.argtypes = []
@@ -125,27 +134,34 @@ def workspace_bytes(B, H, N, d):
     return int(load_library().flashbob_workspace_bytes(B, H, N, d))
 
 
-def bob_stage(stage, Q, K, V, dO, gQ, gK, gV, out, workspace, scale=None, stream=None):
+def bob_stage(stage, Q, K, V, dO, gQ, gK, gV, out, workspace, scale=None, stream=None, causal=False):
     """Run one kernel of bob(): stage in STAGES ("pass1", "pass2_query", "pass2_key")."""
     lib = load_library()
     ins = _inputs(Q, K, V, dO, gQ, gK, gV)
     B, H, N, d = Q.shape
     if scale is None:
         scale = d ** -0.5
-    fn = getattr(lib, STAGES[stage])
-    rc = fn(*[_ptr(t) for t in ins], *[_ptr(t) for t in out], B, H, N, d, ctypes.c_float(scale),
-            _dtype_code(Q.dtype), _ptr(workspace),
-            ctypes.c_size_t(workspace.numel() * workspace.element_size()),
-            _stream_handle(Q.device, stream))
+    if causal:
+        rc = lib.flashbob_bob_ex(*[_ptr(t) for t in ins], *[_ptr(t) for t in out], B, H, N, d,
+                                 ctypes.c_float(scale), _dtype_code(Q.dtype), FLASHBOB_CAUSAL, STAGE_BITS[stage],
+                                 _ptr(workspace), ctypes.c_size_t(workspace.numel() * workspace.element_size()),
+                                 _stream_handle(Q.device, stream))
+    else:
+        fn = getattr(lib, STAGES[stage])
+        rc = fn(*[_ptr(t) for t in ins], *[_ptr(t) for t in out], B, H, N, d, ctypes.c_float(scale),
+                _dtype_code(Q.dtype), _ptr(workspace),
+                ctypes.c_size_t(workspace.numel() * workspace.element_size()),
+                _stream_handle(Q.device, stream))
     _check(rc)
 
 
-def bob(Q, K, V, dO, gQ, gK, gV, scale=None, out=None, workspace=None, stream=None):
+def bob(Q, K, V, dO, gQ, gK, gV, scale=None, out=None, workspace=None, stream=None, causal=False):
     """Exact BoB of softmax attention: (gradQ, gradK, gradV, graddO), float32.
 
     Inputs [B, H, N, d] bf16 or fp32 device tensors; `scale` defaults to
     1/sqrt(d). `out` (four float32 tensors) and `workspace` (uint8 tensor of
     at least workspace_bytes(B, H, N, d)) may be given to avoid allocation.
+    causal=True masks key j > query i (flashbob_bob_ex with FLASHBOB_CAUSAL).
     """
     lib = load_library()
     ins = _inputs(Q, K, V, dO, gQ, gK, gV)
@@ -157,15 +173,21 @@ def bob(Q, K, V, dO, gQ, gK, gV, scale=None, out=None, workspace=None, stream=No
     nws = lib.flashbob_workspace_bytes(B, H, N, d)
     if workspace is None:
         workspace = torch.empty(max(nws, 1), dtype=torch.uint8, device=Q.device)
-    rc = lib.flashbob_bob(*[_ptr(t) for t in ins], *[_ptr(t) for t in out], B, H, N, d,
-                          ctypes.c_float(scale), _dtype_code(Q.dtype), _ptr(workspace),
-                          ctypes.c_size_t(workspace.numel() * workspace.element_size()),
-                          _stream_handle(Q.device, stream))
+    if causal:
+        rc = lib.flashbob_bob_ex(*[_ptr(t) for t in ins], *[_ptr(t) for t in out], B, H, N, d,
+                                 ctypes.c_float(scale), _dtype_code(Q.dtype), FLASHBOB_CAUSAL, 7, _ptr(workspace),
+                                 ctypes.c_size_t(workspace.numel() * workspace.element_size()),
+                                 _stream_handle(Q.device, stream))
+    else:
+        rc = lib.flashbob_bob(*[_ptr(t) for t in ins], *[_ptr(t) for t in out], B, H, N, d,
+                              ctypes.c_float(scale), _dtype_code(Q.dtype), _ptr(workspace),
+                              ctypes.c_size_t(workspace.numel() * workspace.element_size()),
+                              _stream_handle(Q.device, stream))
     _check(rc)
     return tuple(out)
 
 
-def rowstats(Q, K, V, dO, gQ, gK, gV, scale=None, stream=None):
+def rowstats(Q, K, V, dO, gQ, gK, gV, scale=None, stream=None, causal=False):
     """Pass 1 alone: (LSE, D, c, r) per query row, each [B, H, N] float32."""
     lib = load_library()
     ins = _inputs(Q, K, V, dO, gQ, gK, gV)
@@ -173,9 +195,9 @@ def rowstats(Q, K, V, dO, gQ, gK, gV, scale=None, stream=None):
     if scale is None:
         scale = d ** -0.5
     outs = tuple(torch.empty((B, H, N), dtype=torch.float32, device=Q.device) for _ in range(4))
-    rc = lib.flashbob_rowstats(*[_ptr(t) for t in ins], *[_ptr(t) for t in outs], B, H, N, d,
-                               ctypes.c_float(scale), _dtype_code(Q.dtype),
-                               _stream_handle(Q.device, stream))
+    rc = lib.flashbob_rowstats_ex(*[_ptr(t) for t in ins], *[_ptr(t) for t in outs], B, H, N, d,
+                                  ctypes.c_float(scale), _dtype_code(Q.dtype),
+                                  FLASHBOB_CAUSAL if causal else 0, _stream_handle(Q.device, stream))
     _check(rc)
     return outs
 

@@ -15,8 +15,10 @@
  * the library returns the gradients of the scalar
  *     L = <gQ, dQ> + <gK, dK> + <gV, dV>
  * with respect to Q, K, V and dO. LSE and D are differentiated through (they
- * are functions of the inputs). Non-causal, no dropout, no bias, no gradient
- * for `scale`.
+ * are functions of the inputs). No dropout, no bias, no gradient for `scale`.
+ * Attention is non-causal unless FLASHBOB_CAUSAL is passed to the *_ex entry
+ * points (then query i attends to keys j <= i; the masked scores are -inf
+ * constants, a reading beyond the abstract, which does not treat masks).
  *
  * Conventions shared by every entry point
  *   - Tensors are contiguous [B, H, N, d] arrays, d fastest, in device memory
@@ -61,7 +63,21 @@ enum {
   FLASHBOB_ERR_WORKSPACE = -7,      /* workspace smaller than flashbob_workspace_bytes */
   FLASHBOB_ERR_ALIAS = -8,          /* an output overlaps an input, the workspace or another output */
   FLASHBOB_ERR_SCALE = -9,          /* scale is not finite */
+  FLASHBOB_ERR_FLAGS = -10,         /* unknown flag bits, or an empty or unknown stage set */
   FLASHBOB_ERR_HIP = -100           /* a HIP call failed; see flashbob_strerror */
+};
+
+/* Flags of the *_ex entry points. */
+enum {
+  FLASHBOB_CAUSAL = 1  /* query i attends to keys j <= i */
+};
+
+/* Stage sets of flashbob_bob_ex (the three kernels of the schedule). */
+enum {
+  FLASHBOB_STAGE_PASS1 = 1,        /* row scalars into the workspace */
+  FLASHBOB_STAGE_PASS2_QUERY = 2,  /* gradQ, graddO from the workspace's row scalars */
+  FLASHBOB_STAGE_PASS2_KEY = 4,    /* gradK, gradV from the workspace's row scalars */
+  FLASHBOB_STAGES_ALL = 7
 };
 
 /* Bytes of device workspace flashbob_bob needs: four float32 row-scalar
@@ -119,6 +135,22 @@ int flashbob_bob_pass2_key(const void* Q, const void* K, const void* V, const vo
                            int B, int H, int N, int d, float scale, int dtype,
                            void* workspace, size_t workspace_bytes, void* stream);
 
+/* General form of flashbob_bob and of the three stage calls below:
+ *   flags   0 or FLASHBOB_CAUSAL. Causal: per head, each query row i uses
+ *           keys 0..i only; key blocks wholly above the diagonal are skipped,
+ *           so the work is about half.
+ *   stages  a non-empty subset of FLASHBOB_STAGES_ALL, run in the order
+ *           pass 1, pass 2 query side, pass 2 key side. Pass 2 stages read the
+ *           row scalars pass 1 left in `workspace` (computed with the same
+ *           flags and inputs).
+ * Other arguments, checks and return codes as flashbob_bob; unknown flag
+ * bits or stage sets return FLASHBOB_ERR_FLAGS. */
+int flashbob_bob_ex(const void* Q, const void* K, const void* V, const void* dO,
+                    const void* gQ, const void* gK, const void* gV,
+                    float* gradQ, float* gradK, float* gradV, float* graddO,
+                    int B, int H, int N, int d, float scale, int dtype, int flags, int stages,
+                    void* workspace, size_t workspace_bytes, void* stream);
+
 /* Pass 1 alone (row statistics), exported for testing the first pass.
  * Writes, per query row, LSE (natural-log log-sum-exp of s Q K^T), the
  * first-backward scalar D = rowsum(dO o O) and the two BoB row scalars
@@ -130,6 +162,14 @@ int flashbob_rowstats(const void* Q, const void* K, const void* V, const void* d
                       float* lse, float* D, float* c, float* r,
                       int B, int H, int N, int d, float scale, int dtype,
                       void* stream);
+
+/* flashbob_rowstats with flags (0 or FLASHBOB_CAUSAL; with the mask, the
+ * row scalars are those of the causal attention). */
+int flashbob_rowstats_ex(const void* Q, const void* K, const void* V, const void* dO,
+                         const void* gQ, const void* gK, const void* gV,
+                         float* lse, float* D, float* c, float* r,
+                         int B, int H, int N, int d, float scale, int dtype, int flags,
+                         void* stream);
 
 /* Static description of an error code; for FLASHBOB_ERR_HIP, the HIP error
  * text of the calling thread's last failure. Never NULL. */

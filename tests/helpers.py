@@ -35,10 +35,10 @@ def to_f64(t):
     return t.detach().to("cpu", torch.float64).numpy()
 
 
-def gpu_bob(ins, scale=None, dtype=None):
+def gpu_bob(ins, scale=None, dtype=None, causal=False):
     """Run flashbob.bob on the device; `ins` is the dict of CPU tensors."""
     dev = [ins[k].to("cuda") if dtype is None else ins[k].to(dtype).to("cuda") for k in NAMES]
-    out = fb.bob(*dev, scale=scale)
+    out = fb.bob(*dev, scale=scale, causal=causal)
     torch.cuda.synchronize()
     return [o.cpu() for o in out]
 

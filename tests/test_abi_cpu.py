@@ -37,8 +37,8 @@ def test_library_exports_every_declared_symbol():
 
 def test_version_and_strerror():
     lib = fb.load_library()
-    assert lib.flashbob_version() == 100
-    for code in (0, -1, -2, -3, -4, -5, -6, -7, -8, -9, -100, 12345):
+    assert lib.flashbob_version() == 101
+    for code in (0, -1, -2, -3, -4, -5, -6, -7, -8, -9, -10, -100, 12345):
         s = lib.flashbob_strerror(code)
         assert isinstance(s, bytes) and len(s) > 0
 
@@ -175,3 +175,33 @@ def test_rowstats_validation():
     bad = list(outs)
     bad[1] = vp(BASE + 7 * STRIDE + 4)
     assert lib.flashbob_rowstats(*ins, *bad, 1, 1, 128, 64, ctypes.c_float(0.1), F32, vp(0)) == ALIGN
+
+
+def call_ex(ins, outs, B, H, N, d, scale, dtype, wsp, nws, flags=0, stages=7):
+    lib = fb.load_library()
+    vp = ctypes.c_void_p
+    return lib.flashbob_bob_ex(*[vp(p) for p in ins], *[vp(p) for p in outs], B, H, N, d, ctypes.c_float(scale),
+                               dtype, flags, stages, vp(wsp), ctypes.c_size_t(nws), vp(0))
+
+
+def test_ex_rejects_unknown_flags_and_stage_sets():
+    FLAGS = -10
+    for flags in (2, 4, -1, 1 << 20):
+        assert call_ex(*fake_args(), flags=flags) == FLAGS
+    for stages in (0, 8, 9, -1, 16):
+        assert call_ex(*fake_args(), stages=stages) == FLAGS
+    # the flags check comes first, the shape checks still apply after it
+    a = list(fake_args())
+    a[5] = 96
+    assert call_ex(*a, flags=1, stages=7) == UD
+    lib = fb.load_library()
+    vp = ctypes.c_void_p
+    ins = [vp(BASE + i * STRIDE) for i in range(7)]
+    outs = [vp(BASE + (7 + i) * STRIDE) for i in range(4)]
+    assert lib.flashbob_rowstats_ex(*ins, *outs, 1, 1, 128, 64, ctypes.c_float(0.1), F32, 2, vp(0)) == FLAGS
+
+
+def test_ex_empty_problem_is_a_noop():
+    # B*H*N == 0 returns OK before any HIP call, with or without the mask
+    for flags in (0, 1):
+        assert call_ex(*fake_args(B=0), flags=flags) == 0
