@@ -48,6 +48,7 @@ __all__ = [
     "bob_rows_head",
     "bob_blocked_head",
     "bob_blocked",
+    "bob_gqa",
 ]
 
 
@@ -288,3 +289,39 @@ def bob_blocked(Q, K, V, dO, gQ, gK, gV, scale, block=1024, causal=False):
         for o, x in zip(outs, res):
             o[idx] = x
     return tuple(outs)
+
+
+def bob_gqa(Q, K, V, dO, gQ, gK, gV, scale, causal=False, block=None):
+    """Batched BoB with grouped key/value heads (GQA / MQA).
+
+    Q, dO, gQ are [B, H, N, d]; K, V, gK, gV are [B, Hkv, N, d] with H a
+    multiple of Hkv, and query head h uses key/value head h // (H / Hkv) (a
+    reading beyond the pages). The first backward of such attention gives the
+    shared K and V the sum of their per-head gradients, so L = <gQ, dQ> +
+    <gK, dK> + <gV, dV> is the multi-head objective with K, V, gK, gV repeated
+    over each group: gradQ, graddO are per query head, gradK, gradV are the
+    sums over the group's query heads. `block` selects the row-blocked form.
+    """
+    Q, K, V, dO, gQ, gK, gV = _f64(Q, K, V, dO, gQ, gK, gV)
+    B, H = Q.shape[:2]
+    Hkv = K.shape[1]
+    if H % Hkv:
+        raise ValueError("query heads must be a multiple of key/value heads")
+    G = H // Hkv
+    gradQ = np.empty_like(Q)
+    graddO = np.empty_like(dO)
+    gradK = np.zeros_like(K)
+    gradV = np.zeros_like(V)
+    for b in range(B):
+        for h in range(H):
+            j = h // G
+            args = (Q[b, h], K[b, j], V[b, j], dO[b, h], gQ[b, h], gK[b, j], gV[b, j], scale)
+            if block is None:
+                gq, gk, gv, gdo = bob_head(*args, causal=causal)
+            else:
+                gq, gk, gv, gdo = bob_blocked_head(*args, block=block, causal=causal)
+            gradQ[b, h] = gq
+            graddO[b, h] = gdo
+            gradK[b, j] += gk
+            gradV[b, j] += gv
+    return gradQ, gradK, gradV, graddO

@@ -435,3 +435,64 @@ def test_causal_pins_catch_planted_mask_mistakes(variant, monkeypatch):
     ref = torch_bob_causal(xs, s)
     worst = max(rel(g, r) for g, r in zip(got, ref))
     assert worst > 1e-3, f"planted {variant} not caught (worst rel {worst})"
+
+
+# ----------------------------------------------------------------------------
+# grouped key/value heads (GQA / MQA): query head h uses key/value head
+# h // (H / Hkv). Independent route: torch autograd through a torch attention
+# whose K, V are expanded with repeat_interleave (gradients flow back to the
+# shared heads).
+
+
+def torch_bob_gqa(xs, scale, causal):
+    Q, K, V, dO, gQ, gK, gV = [torch.tensor(x, requires_grad=True) for x in xs]
+    G = Q.shape[1] // K.shape[1]
+    Ke, Ve = K.repeat_interleave(G, dim=1), V.repeat_interleave(G, dim=1)
+    S = scale * Q @ Ke.transpose(-1, -2)
+    if causal:
+        N = Q.shape[2]
+        S = S.masked_fill(torch.ones(N, N, dtype=torch.bool).triu(1), float("-inf"))
+    f = torch.sum(dO * (torch.softmax(S, dim=-1) @ Ve))
+    dQ, dK, dV = torch.autograd.grad(f, (Q, K, V), create_graph=True)
+    L = torch.sum(gQ * dQ) + torch.sum(gK * dK) + torch.sum(gV * dV)
+    grads = torch.autograd.grad(L, (Q, K, V, dO))
+    return [g.detach().numpy() for g in grads]
+
+
+@pytest.mark.parametrize("H,Hkv", [(4, 2), (3, 1), (2, 2)])
+@pytest.mark.parametrize("causal", [False, True])
+def test_gqa_matches_autograd(H, Hkv, causal):
+    rng = np.random.default_rng(H * 10 + Hkv + causal)
+    B, N, d = 2, 9, 4
+    q_shape, kv_shape = (B, H, N, d), (B, Hkv, N, d)
+    xs = [rng.standard_normal(s) for s in (q_shape, kv_shape, kv_shape, q_shape, q_shape, kv_shape, kv_shape)]
+    got = oracle.bob_gqa(*xs, 0.45, causal=causal)
+    ref = torch_bob_gqa(xs, 0.45, causal)
+    for g, r in zip(got, ref):
+        assert rel(g, r) < 1e-12
+    blocked = oracle.bob_gqa(*xs, 0.45, causal=causal, block=4)
+    for g, r in zip(blocked, got):
+        assert rel(g, r) < 1e-13
+
+
+def test_gqa_planted_mistake_is_caught(monkeypatch):
+    # taking only the group's first query head for gradK, gradV (instead of
+    # the sum over the group) must fail the autograd pin
+    rng = np.random.default_rng(3)
+    B, H, Hkv, N, d = 1, 4, 2, 7, 4
+    q_shape, kv_shape = (B, H, N, d), (B, Hkv, N, d)
+    xs = [rng.standard_normal(s) for s in (q_shape, kv_shape, kv_shape, q_shape, q_shape, kv_shape, kv_shape)]
+    ref = torch_bob_gqa(xs, 0.5, False)
+    orig = bob_oracle.bob_head
+    calls = {"n": 0}
+
+    def first_only(*a, **k):
+        out = orig(*a, **k)
+        calls["n"] += 1
+        if calls["n"] % 2 == 0:  # the group's second head contributes nothing to gradK, gradV
+            return out[0], np.zeros_like(out[1]), np.zeros_like(out[2]), out[3]
+        return out
+
+    monkeypatch.setattr(bob_oracle, "bob_head", first_only)
+    got = oracle.bob_gqa(*xs, 0.5)
+    assert max(rel(g, r) for g, r in zip(got, ref)) > 1e-3
