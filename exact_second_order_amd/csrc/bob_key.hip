@@ -126,7 +126,7 @@ __global__ __launch_bounds__(256, (KeyCfg<T, D>::OCC2 ? 2 : 1)) void key_kernel(
     const T* __restrict__ gQ, const T* __restrict__ gK, const T* __restrict__ gV,
     const float* __restrict__ lse2, const float* __restrict__ Dv, const float* __restrict__ cv,
     const float* __restrict__ rv, float* __restrict__ gradK, float* __restrict__ gradV, int N, int nkblk,
-    float scale, int causal) {
+    float scale, int causal, int G) {
   using Cfg = KeyCfg<T, D>;
   using E = Elem<T>;
   using F = typename E::frag;
@@ -153,8 +153,9 @@ __global__ __launch_bounds__(256, (KeyCfg<T, D>::OCC2 ? 2 : 1)) void key_kernel(
 
   const int head = blockIdx.x / nkblk;
   const int kblk = blockIdx.x % nkblk;
+  // key/value head `head`; the query heads of its group are head * G + g
   const size_t hoff = (size_t)head * N * D;
-  const size_t soff = (size_t)head * N;
+  size_t qoff = 0, soff = 0;  // query head of the current group member
   const int w = wave_id(), l = lane_id(), h = l >> 5, col = l & 31;
   const int key = kblk * Cfg::BC + 32 * w + col;  // this lane's key
   const bool kvalid = key < N;
@@ -215,9 +216,9 @@ __global__ __launch_bounds__(256, (KeyCfg<T, D>::OCC2 ? 2 : 1)) void key_kernel(
     const int nq = min(BQ, N - q0);
     if constexpr (SWZ) {
       const int b = n & (NBUF - 1);
-      load_tile_sw(tile(b, 0), Q + hoff + (size_t)q0 * D, nq);
-      load_tile_sw(tile(b, 1), gQ + hoff + (size_t)q0 * D, nq);
-      load_tile_sw(tile(b, 2), dO + hoff + (size_t)q0 * D, nq);
+      load_tile_sw(tile(b, 0), Q + qoff + (size_t)q0 * D, nq);
+      load_tile_sw(tile(b, 1), gQ + qoff + (size_t)q0 * D, nq);
+      load_tile_sw(tile(b, 2), dO + qoff + (size_t)q0 * D, nq);
       // wave w fetches row scalar w (LSE*log2e, -D, -c/s, -r) of the stage's
       // queries: lane L < 32 -> row L, written at LDS float L of sS(b, w);
       // rows past the end read as zero
@@ -228,9 +229,9 @@ __global__ __launch_bounds__(256, (KeyCfg<T, D>::OCC2 ? 2 : 1)) void key_kernel(
                                                  4 * l, 0, 0, 0);
       }
     } else {
-      pq.load(Q + hoff + (size_t)q0 * D, nq);
-      pg.load(gQ + hoff + (size_t)q0 * D, nq);
-      pd.load(dO + hoff + (size_t)q0 * D, nq);
+      pq.load(Q + qoff + (size_t)q0 * D, nq);
+      pg.load(gQ + qoff + (size_t)q0 * D, nq);
+      pd.load(dO + qoff + (size_t)q0 * D, nq);
       if ((int)threadIdx.x < 4 * BQ) {
         const int t = threadIdx.x / BQ, i = threadIdx.x % BQ;
         const bool ok = i < nq;
@@ -312,35 +313,41 @@ __global__ __launch_bounds__(256, (KeyCfg<T, D>::OCC2 ? 2 : 1)) void key_kernel(
   // BC / BQ blocks across the diagonal; the rest see every key.
   const int nstart = causal ? kblk * (Cfg::BC / BQ) : 0;  // even
   const int ndiag = causal ? min(nblk, nstart + Cfg::BC / BQ) : 0;
-  prefetch(nstart);  // nstart < nblk
-  commit(nstart);
-  __syncthreads();
 
   using F0 = std::integral_constant<bool, false>;
   using F1 = std::integral_constant<bool, true>;
   const bool last_partial = N % BQ != 0;
   Tiles t;
   Frags f;
-  // iterations in pairs from the even nstart, so that the stage buffer index
-  // is a compile-time constant in both halves
-  for (int i = nstart >> 1; 2 * i < nblk; ++i) {
+  // sweep the queries of each member of the key/value head's group in turn
+  // (gradK, gradV sum over them)
+  for (int g = 0; g < G; ++g) {
+    qoff = (size_t)(head * G + g) * N * D;
+    soff = (size_t)(head * G + g) * N;
+    prefetch(nstart);  // nstart < nblk; the previous member's last barrier freed both buffers
+    commit(nstart);
+    __syncthreads();
+    // iterations in pairs from the even nstart, so that the stage buffer index
+    // is a compile-time constant in both halves
+    for (int i = nstart >> 1; 2 * i < nblk; ++i) {
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int n = 2 * i + u;
-      if (u == 1 && n >= nblk) break;  // odd block count: the last pair is a single
-      const bool pf = n + 1 < nblk;
-      if (pf) prefetch(n + 1);
-      recompute(n, t, 0, NCH);
+      for (int u = 0; u < 2; ++u) {
+        const int n = 2 * i + u;
+        if (u == 1 && n >= nblk) break;  // odd block count: the last pair is a single
+        const bool pf = n + 1 < nblk;
+        if (pf) prefetch(n + 1);
+        recompute(n, t, 0, NCH);
 #pragma unroll
-      for (int cc = 0; cc < 2; ++cc) {
-        if (ktail || n < ndiag || (n == nblk - 1 && last_partial))
-          elementwise(F1{}, n, cc, t, f);
-        else
-          elementwise(F0{}, n, cc, t, f);
-        outputs(n, cc, f);
+        for (int cc = 0; cc < 2; ++cc) {
+          if (ktail || n < ndiag || (n == nblk - 1 && last_partial))
+            elementwise(F1{}, n, cc, t, f);
+          else
+            elementwise(F0{}, n, cc, t, f);
+          outputs(n, cc, f);
+        }
+        if (pf) commit(n + 1);  // its buffer last held stage n-1, read in iteration n-1
+        __syncthreads();
       }
-      if (pf) commit(n + 1);  // its buffer last held stage n-1, read in iteration n-1
-      __syncthreads();
     }
   }
 
@@ -365,21 +372,22 @@ __global__ __launch_bounds__(256, (KeyCfg<T, D>::OCC2 ? 2 : 1)) void key_kernel(
 template <typename T, int D>
 hipError_t launch_key(const void* Q, const void* K, const void* V, const void* dO, const void* gQ, const void* gK,
                       const void* gV, const float* lse2, const float* Dv, const float* cv, const float* rv,
-                      float* gradK, float* gradV, int BH, int N, float scale, int causal, hipStream_t stream) {
+                      float* gradK, float* gradV, int BHkv, int N, float scale, int causal, int G,
+                      hipStream_t stream) {
   using Cfg = KeyCfg<T, D>;
   const int nkblk = (N + Cfg::BC - 1) / Cfg::BC;
-  const long long nblocks = (long long)nkblk * BH;
+  const long long nblocks = (long long)nkblk * BHkv;
   if (nblocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   key_kernel<T, D><<<dim3((unsigned)nblocks), dim3(256), 0, stream>>>(
       (const T*)Q, (const T*)K, (const T*)V, (const T*)dO, (const T*)gQ, (const T*)gK, (const T*)gV, lse2, Dv, cv,
-      rv, gradK, gradV, N, nkblk, scale, causal);
+      rv, gradK, gradV, N, nkblk, scale, causal, G);
   return hipGetLastError();
 }
 
 #define FLASHBOB_INST_KEY(T, D)                                                                            \
   template hipError_t launch_key<T, D>(const void*, const void*, const void*, const void*, const void*,   \
                                        const void*, const void*, const float*, const float*, const float*, \
-                                       const float*, float*, float*, int, int, float, int, hipStream_t);
+                                       const float*, float*, float*, int, int, float, int, int, hipStream_t);
 FLASHBOB_INST_KEY(bf16, 64)
 FLASHBOB_INST_KEY(bf16, 128)
 FLASHBOB_INST_KEY(float, 64)

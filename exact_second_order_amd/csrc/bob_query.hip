@@ -184,7 +184,7 @@ __global__ __launch_bounds__(256, (QueryCfg<T, D, GRADQ>::OCC2 ? 2 : 1)) void qu
     const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V, const T* __restrict__ dO,
     const T* __restrict__ gQ, const T* __restrict__ gK, const T* __restrict__ gV, float* __restrict__ lse,
     float* __restrict__ Dv, float* __restrict__ cv, float* __restrict__ rv, float* __restrict__ gradQ,
-    float* __restrict__ graddO, int N, int nqblk, float scale, int lse_natural, int causal) {
+    float* __restrict__ graddO, int N, int nqblk, float scale, int lse_natural, int causal, int G) {
   using Cfg = QueryCfg<T, D, GRADQ>;
   using E = Elem<T>;
   using F = typename E::frag;
@@ -207,7 +207,8 @@ __global__ __launch_bounds__(256, (QueryCfg<T, D, GRADQ>::OCC2 ? 2 : 1)) void qu
   const int head = blockIdx.x / nqblk;
   // (causal: the longest sweeps, the last query blocks, start first)
   const int qblk = causal ? nqblk - 1 - (int)(blockIdx.x % nqblk) : (int)(blockIdx.x % nqblk);
-  const size_t hoff = (size_t)head * N * D;
+  const size_t hoff = (size_t)head * N * D;         // query head (Q, dO, gQ, outputs)
+  const size_t koff = (size_t)(head / G) * N * D;   // its key/value head (groups of G)
   const int w = wave_id(), l = lane_id(), h = l >> 5, col = l & 31;
   const int q = qblk * Cfg::BQ + 32 * w + col;  // this lane's query
   const bool qvalid = q < N;
@@ -270,15 +271,15 @@ __global__ __launch_bounds__(256, (QueryCfg<T, D, GRADQ>::OCC2 ? 2 : 1)) void qu
     const int nk = min(BK, N - k0);
     if constexpr (SWZ) {
       const int b = n & (NBUF - 1);
-      load_tile_sw(tile(b, 0), K + hoff + (size_t)k0 * D, nk);
-      load_tile_sw(tile(b, 1), gK + hoff + (size_t)k0 * D, nk);
-      load_tile_sw(tile(b, 2), V + hoff + (size_t)k0 * D, nk);
-      load_tile_sw(tile(b, 3), gV + hoff + (size_t)k0 * D, nk);
+      load_tile_sw(tile(b, 0), K + koff + (size_t)k0 * D, nk);
+      load_tile_sw(tile(b, 1), gK + koff + (size_t)k0 * D, nk);
+      load_tile_sw(tile(b, 2), V + koff + (size_t)k0 * D, nk);
+      load_tile_sw(tile(b, 3), gV + koff + (size_t)k0 * D, nk);
     } else {
-      pk.load(K + hoff + (size_t)k0 * D, nk);
-      pgk.load(gK + hoff + (size_t)k0 * D, nk);
-      pv.load(V + hoff + (size_t)k0 * D, nk);
-      pgv.load(gV + hoff + (size_t)k0 * D, nk);
+      pk.load(K + koff + (size_t)k0 * D, nk);
+      pgk.load(gK + koff + (size_t)k0 * D, nk);
+      pv.load(V + koff + (size_t)k0 * D, nk);
+      pgv.load(gV + koff + (size_t)k0 * D, nk);
     }
   };
   auto commit = [&](int n) __attribute__((always_inline)) {
@@ -467,14 +468,14 @@ template <typename T, int D, bool GRADQ>
 hipError_t launch_query(const void* Q, const void* K, const void* V, const void* dO, const void* gQ,
                         const void* gK, const void* gV, float* lse, float* Dv, float* cv, float* rv,
                         float* gradQ, float* graddO, int BH, int N, float scale, int lse_natural,
-                        int causal, hipStream_t stream) {
+                        int causal, int G, hipStream_t stream) {
   using Cfg = QueryCfg<T, D, GRADQ>;
   const int nqblk = (N + Cfg::BQ - 1) / Cfg::BQ;
   const long long nblocks = (long long)nqblk * BH;
   if (nblocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   query_kernel<T, D, GRADQ><<<dim3((unsigned)nblocks), dim3(256), 0, stream>>>(
       (const T*)Q, (const T*)K, (const T*)V, (const T*)dO, (const T*)gQ, (const T*)gK, (const T*)gV, lse, Dv,
-      cv, rv, gradQ, graddO, N, nqblk, scale, lse_natural, causal);
+      cv, rv, gradQ, graddO, N, nqblk, scale, lse_natural, causal, G);
   return hipGetLastError();
 }
 
@@ -482,7 +483,7 @@ hipError_t launch_query(const void* Q, const void* K, const void* V, const void*
   template hipError_t launch_query<T, D, G>(const void*, const void*, const void*, const void*,         \
                                             const void*, const void*, const void*, float*, float*,      \
                                             float*, float*, float*, float*, int, int, float, int, int,    \
-                                            hipStream_t);
+                                            int, hipStream_t);
 // Pass 1 and pass 2q instantiations are built as separate objects (pass 1
 // with MFMA results kept in VGPRs, which its register budget allows).
 #ifndef FLASHBOB_QUERY_PASS2

@@ -18,11 +18,12 @@ template <typename T, int D, bool GRADQ>
 hipError_t launch_query(const void* Q, const void* K, const void* V, const void* dO, const void* gQ,
                         const void* gK, const void* gV, float* lse, float* Dv, float* cv, float* rv,
                         float* gradQ, float* graddO, int BH, int N, float scale, int lse_natural,
-                        int causal, hipStream_t stream);
+                        int causal, int G, hipStream_t stream);
 template <typename T, int D>
 hipError_t launch_key(const void* Q, const void* K, const void* V, const void* dO, const void* gQ, const void* gK,
                       const void* gV, const float* lse2, const float* Dv, const float* cv, const float* rv,
-                      float* gradK, float* gradV, int BH, int N, float scale, int causal, hipStream_t stream);
+                      float* gradK, float* gradV, int BHkv, int N, float scale, int causal, int G,
+                      hipStream_t stream);
 }  // namespace flashbob
 
 namespace {
@@ -60,7 +61,9 @@ int check_common(const void* const* ins, int B, int H, int N, int d, float scale
   return FLASHBOB_OK;
 }
 
-int check_outputs(const void* const* ins, size_t in_bytes, void* const* outs, const size_t* out_bytes, int nout) {
+// ins: the seven inputs with their byte sizes; outs: nout outputs with theirs.
+int check_outputs(const void* const* ins, const size_t* in_bytes, void* const* outs, const size_t* out_bytes,
+                  int nout) {
   for (int i = 0; i < nout; ++i) {
     if (outs[i] == nullptr) return FLASHBOB_ERR_NULL;
     if (reinterpret_cast<uintptr_t>(outs[i]) % 16) return FLASHBOB_ERR_ALIGN;
@@ -68,7 +71,7 @@ int check_outputs(const void* const* ins, size_t in_bytes, void* const* outs, co
   for (int i = 0; i < nout; ++i) {
     const Range ro{reinterpret_cast<uintptr_t>(outs[i]), reinterpret_cast<uintptr_t>(outs[i]) + out_bytes[i]};
     for (int j = 0; j < 7; ++j) {
-      const Range ri{reinterpret_cast<uintptr_t>(ins[j]), reinterpret_cast<uintptr_t>(ins[j]) + in_bytes};
+      const Range ri{reinterpret_cast<uintptr_t>(ins[j]), reinterpret_cast<uintptr_t>(ins[j]) + in_bytes[j]};
       if (overlaps(ro, ri)) return FLASHBOB_ERR_ALIAS;
     }
     for (int j = i + 1; j < nout; ++j) {
@@ -88,51 +91,51 @@ enum Stage {
 
 template <typename T, int D>
 hipError_t run_stages(int stages, int causal, const void* const* in, float* stats, float* gQo, float* gKo,
-                      float* gVo, float* gdOo, int BH, int N, float scale, hipStream_t st) {
+                      float* gVo, float* gdOo, int BH, int G, int N, float scale, hipStream_t st) {
   const size_t BHN = (size_t)BH * N;
   // workspace row scalars: LSE * log2(e), D, c, r
   float *lse = stats, *Dv = stats + BHN, *cv = stats + 2 * BHN, *rv = stats + 3 * BHN;
   hipError_t e = hipSuccess;
   if (stages & kPass1) {
     e = flashbob::launch_query<T, D, false>(in[0], in[1], in[2], in[3], in[4], in[5], in[6], lse, Dv, cv, rv,
-                                            nullptr, nullptr, BH, N, scale, 0, causal, st);
+                                            nullptr, nullptr, BH, N, scale, 0, causal, G, st);
     if (e != hipSuccess) return e;
   }
   if (stages & kPass2Query) {
     e = flashbob::launch_query<T, D, true>(in[0], in[1], in[2], in[3], in[4], in[5], in[6], lse, Dv, cv, rv,
-                                           gQo, gdOo, BH, N, scale, 0, causal, st);
+                                           gQo, gdOo, BH, N, scale, 0, causal, G, st);
     if (e != hipSuccess) return e;
   }
   if (stages & kPass2Key) {
     e = flashbob::launch_key<T, D>(in[0], in[1], in[2], in[3], in[4], in[5], in[6], lse, Dv, cv, rv, gKo, gVo,
-                                   BH, N, scale, causal, st);
+                                   BH / G, N, scale, causal, G, st);
   }
   return e;
 }
 
 hipError_t dispatch(int dtype, int d, int stages, int causal, const void* const* in, float* stats, float* gQo,
-                    float* gKo, float* gVo, float* gdOo, int BH, int N, float scale, hipStream_t st) {
+                    float* gKo, float* gVo, float* gdOo, int BH, int G, int N, float scale, hipStream_t st) {
   if (dtype == FLASHBOB_BF16)
-    return d == 64 ? run_stages<__bf16, 64>(stages, causal, in, stats, gQo, gKo, gVo, gdOo, BH, N, scale, st)
-                   : run_stages<__bf16, 128>(stages, causal, in, stats, gQo, gKo, gVo, gdOo, BH, N, scale, st);
-  return d == 64 ? run_stages<float, 64>(stages, causal, in, stats, gQo, gKo, gVo, gdOo, BH, N, scale, st)
-                 : run_stages<float, 128>(stages, causal, in, stats, gQo, gKo, gVo, gdOo, BH, N, scale, st);
+    return d == 64 ? run_stages<__bf16, 64>(stages, causal, in, stats, gQo, gKo, gVo, gdOo, BH, G, N, scale, st)
+                   : run_stages<__bf16, 128>(stages, causal, in, stats, gQo, gKo, gVo, gdOo, BH, G, N, scale, st);
+  return d == 64 ? run_stages<float, 64>(stages, causal, in, stats, gQo, gKo, gVo, gdOo, BH, G, N, scale, st)
+                 : run_stages<float, 128>(stages, causal, in, stats, gQo, gKo, gVo, gdOo, BH, G, N, scale, st);
 }
 
 template <typename T, int D>
-hipError_t rowstats_launch(const void* const* in, float* lse, float* Dv, float* cv, float* rv, int BH, int N,
-                           float scale, int causal, hipStream_t st) {
+hipError_t rowstats_launch(const void* const* in, float* lse, float* Dv, float* cv, float* rv, int BH, int G,
+                           int N, float scale, int causal, hipStream_t st) {
   return flashbob::launch_query<T, D, false>(in[0], in[1], in[2], in[3], in[4], in[5], in[6], lse, Dv, cv, rv,
-                                             nullptr, nullptr, BH, N, scale, 1, causal, st);
+                                             nullptr, nullptr, BH, N, scale, 1, causal, G, st);
 }
 
 hipError_t dispatch_rowstats(int dtype, int d, int causal, const void* const* in, float* lse, float* Dv, float* cv,
-                             float* rv, int BH, int N, float scale, hipStream_t st) {
+                             float* rv, int BH, int G, int N, float scale, hipStream_t st) {
   if (dtype == FLASHBOB_BF16)
-    return d == 64 ? rowstats_launch<__bf16, 64>(in, lse, Dv, cv, rv, BH, N, scale, causal, st)
-                   : rowstats_launch<__bf16, 128>(in, lse, Dv, cv, rv, BH, N, scale, causal, st);
-  return d == 64 ? rowstats_launch<float, 64>(in, lse, Dv, cv, rv, BH, N, scale, causal, st)
-                 : rowstats_launch<float, 128>(in, lse, Dv, cv, rv, BH, N, scale, causal, st);
+    return d == 64 ? rowstats_launch<__bf16, 64>(in, lse, Dv, cv, rv, BH, G, N, scale, causal, st)
+                   : rowstats_launch<__bf16, 128>(in, lse, Dv, cv, rv, BH, G, N, scale, causal, st);
+  return d == 64 ? rowstats_launch<float, 64>(in, lse, Dv, cv, rv, BH, G, N, scale, causal, st)
+                 : rowstats_launch<float, 128>(in, lse, Dv, cv, rv, BH, G, N, scale, causal, st);
 }
 
 size_t stats_bytes(int B, int H, int N) {
@@ -150,34 +153,51 @@ size_t flashbob_workspace_bytes(int B, int H, int N, int d) {
   return stats_bytes(B, H, N);
 }
 
+// Key/value heads: 1 <= H_kv <= H with H a multiple of H_kv (any H_kv when H
+// is 0). Query-side tensors hold B*H*N*d elements, key/value-side ones
+// B*H_kv*N*d.
+int check_kv_heads(int H, int H_kv) {
+  if (H_kv < 0 || (H > 0 && (H_kv == 0 || H % H_kv != 0))) return FLASHBOB_ERR_SHAPE;
+  return FLASHBOB_OK;
+}
+
+void tensor_bytes(size_t numel_q, size_t numel_kv, size_t esz, size_t* in_bytes) {
+  const bool q_side[7] = {true, false, false, true, true, false, false};  // Q K V dO gQ gK gV
+  for (int i = 0; i < 7; ++i) in_bytes[i] = (q_side[i] ? numel_q : numel_kv) * esz;
+}
+
 int flashbob_bob_ex(const void* Q, const void* K, const void* V, const void* dO, const void* gQ, const void* gK,
-                    const void* gV, float* gradQ, float* gradK, float* gradV, float* graddO, int B, int H, int N,
-                    int d, float scale, int dtype, int flags, int stages, void* workspace, size_t workspace_bytes,
-                    void* stream) {
+                    const void* gV, float* gradQ, float* gradK, float* gradV, float* graddO, int B, int H,
+                    int H_kv, int N, int d, float scale, int dtype, int flags, int stages, void* workspace,
+                    size_t workspace_bytes, void* stream) {
   if ((flags & ~FLASHBOB_CAUSAL) != 0 || stages <= 0 || (stages & ~FLASHBOB_STAGES_ALL) != 0)
     return FLASHBOB_ERR_FLAGS;
   const void* ins[7] = {Q, K, V, dO, gQ, gK, gV};
   size_t numel = 0;
   int rc = check_common(ins, B, H, N, d, scale, dtype, &numel);
+  if (rc == FLASHBOB_OK) rc = check_kv_heads(H, H_kv);
   if (rc != FLASHBOB_OK || numel == 0) return rc;
   const size_t esz = dtype == FLASHBOB_BF16 ? 2 : 4;
+  const size_t numel_kv = numel / (size_t)H * (size_t)H_kv;
   const size_t ws_need = stats_bytes(B, H, N);
   if (workspace == nullptr) return FLASHBOB_ERR_NULL;
   if (workspace_bytes < ws_need) return FLASHBOB_ERR_WORKSPACE;
+  size_t ib[7];
+  tensor_bytes(numel, numel_kv, esz, ib);
   void* outs[5] = {gradQ, gradK, gradV, graddO, workspace};
-  const size_t ob[5] = {numel * 4, numel * 4, numel * 4, numel * 4, ws_need};
-  rc = check_outputs(ins, numel * esz, outs, ob, 5);
+  const size_t ob[5] = {numel * 4, numel_kv * 4, numel_kv * 4, numel * 4, ws_need};
+  rc = check_outputs(ins, ib, outs, ob, 5);
   if (rc != FLASHBOB_OK) return rc;
   const hipError_t e = dispatch(dtype, d, stages, (flags & FLASHBOB_CAUSAL) ? 1 : 0, ins,
-                                static_cast<float*>(workspace), gradQ, gradK, gradV, graddO, B * H, N, scale,
-                                static_cast<hipStream_t>(stream));
+                                static_cast<float*>(workspace), gradQ, gradK, gradV, graddO, B * H, H / H_kv, N,
+                                scale, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? FLASHBOB_OK : hip_fail(e);
 }
 
 int flashbob_bob(const void* Q, const void* K, const void* V, const void* dO, const void* gQ, const void* gK,
                  const void* gV, float* gradQ, float* gradK, float* gradV, float* graddO, int B, int H, int N,
                  int d, float scale, int dtype, void* workspace, size_t workspace_bytes, void* stream) {
-  return flashbob_bob_ex(Q, K, V, dO, gQ, gK, gV, gradQ, gradK, gradV, graddO, B, H, N, d, scale, dtype, 0,
+  return flashbob_bob_ex(Q, K, V, dO, gQ, gK, gV, gradQ, gradK, gradV, graddO, B, H, H, N, d, scale, dtype, 0,
                          FLASHBOB_STAGES_ALL, workspace, workspace_bytes, stream);
 }
 
@@ -185,7 +205,7 @@ int flashbob_bob_pass1(const void* Q, const void* K, const void* V, const void* 
                        const void* gK, const void* gV, float* gradQ, float* gradK, float* gradV, float* graddO,
                        int B, int H, int N, int d, float scale, int dtype, void* workspace,
                        size_t workspace_bytes, void* stream) {
-  return flashbob_bob_ex(Q, K, V, dO, gQ, gK, gV, gradQ, gradK, gradV, graddO, B, H, N, d, scale, dtype, 0,
+  return flashbob_bob_ex(Q, K, V, dO, gQ, gK, gV, gradQ, gradK, gradV, graddO, B, H, H, N, d, scale, dtype, 0,
                          FLASHBOB_STAGE_PASS1, workspace, workspace_bytes, stream);
 }
 
@@ -193,7 +213,7 @@ int flashbob_bob_pass2_query(const void* Q, const void* K, const void* V, const 
                              const void* gK, const void* gV, float* gradQ, float* gradK, float* gradV,
                              float* graddO, int B, int H, int N, int d, float scale, int dtype, void* workspace,
                              size_t workspace_bytes, void* stream) {
-  return flashbob_bob_ex(Q, K, V, dO, gQ, gK, gV, gradQ, gradK, gradV, graddO, B, H, N, d, scale, dtype, 0,
+  return flashbob_bob_ex(Q, K, V, dO, gQ, gK, gV, gradQ, gradK, gradV, graddO, B, H, H, N, d, scale, dtype, 0,
                          FLASHBOB_STAGE_PASS2_QUERY, workspace, workspace_bytes, stream);
 }
 
@@ -201,34 +221,37 @@ int flashbob_bob_pass2_key(const void* Q, const void* K, const void* V, const vo
                            const void* gK, const void* gV, float* gradQ, float* gradK, float* gradV,
                            float* graddO, int B, int H, int N, int d, float scale, int dtype, void* workspace,
                            size_t workspace_bytes, void* stream) {
-  return flashbob_bob_ex(Q, K, V, dO, gQ, gK, gV, gradQ, gradK, gradV, graddO, B, H, N, d, scale, dtype, 0,
+  return flashbob_bob_ex(Q, K, V, dO, gQ, gK, gV, gradQ, gradK, gradV, graddO, B, H, H, N, d, scale, dtype, 0,
                          FLASHBOB_STAGE_PASS2_KEY, workspace, workspace_bytes, stream);
 }
 
 int flashbob_rowstats_ex(const void* Q, const void* K, const void* V, const void* dO, const void* gQ,
                          const void* gK, const void* gV, float* lse, float* Dv, float* cv, float* rv, int B, int H,
-                         int N, int d, float scale, int dtype, int flags, void* stream) {
+                         int H_kv, int N, int d, float scale, int dtype, int flags, void* stream) {
   if ((flags & ~FLASHBOB_CAUSAL) != 0) return FLASHBOB_ERR_FLAGS;
   const void* ins[7] = {Q, K, V, dO, gQ, gK, gV};
   size_t numel = 0;
   int rc = check_common(ins, B, H, N, d, scale, dtype, &numel);
+  if (rc == FLASHBOB_OK) rc = check_kv_heads(H, H_kv);
   if (rc != FLASHBOB_OK || numel == 0) return rc;
   const size_t esz = dtype == FLASHBOB_BF16 ? 2 : 4;
+  size_t ib[7];
+  tensor_bytes(numel, numel / (size_t)H * (size_t)H_kv, esz, ib);
   const size_t vb = (size_t)B * H * N * sizeof(float);
   void* outs[4] = {lse, Dv, cv, rv};
   const size_t ob[4] = {vb, vb, vb, vb};
-  rc = check_outputs(ins, numel * esz, outs, ob, 4);
+  rc = check_outputs(ins, ib, outs, ob, 4);
   if (rc != FLASHBOB_OK) return rc;
   // pass 1 writing the plain row scalars into the caller's four vectors
   const hipError_t e = dispatch_rowstats(dtype, d, (flags & FLASHBOB_CAUSAL) ? 1 : 0, ins, lse, Dv, cv, rv, B * H,
-                                         N, scale, static_cast<hipStream_t>(stream));
+                                         H / H_kv, N, scale, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? FLASHBOB_OK : hip_fail(e);
 }
 
 int flashbob_rowstats(const void* Q, const void* K, const void* V, const void* dO, const void* gQ,
                       const void* gK, const void* gV, float* lse, float* Dv, float* cv, float* rv, int B, int H,
                       int N, int d, float scale, int dtype, void* stream) {
-  return flashbob_rowstats_ex(Q, K, V, dO, gQ, gK, gV, lse, Dv, cv, rv, B, H, N, d, scale, dtype, 0, stream);
+  return flashbob_rowstats_ex(Q, K, V, dO, gQ, gK, gV, lse, Dv, cv, rv, B, H, H, N, d, scale, dtype, 0, stream);
 }
 
 const char* flashbob_strerror(int code) {

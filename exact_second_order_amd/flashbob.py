@@ -79,9 +79,9 @@ def load_library(path=LIB_PATH):
         fn.restype = i
     lib.flashbob_rowstats.argtypes = [vp] * 7 + [vp] * 4 + [i, i, i, i, f, i, vp]
     lib.flashbob_rowstats.restype = i
-    lib.flashbob_bob_ex.argtypes = [vp] * 7 + [vp] * 4 + [i, i, i, i, f, i, i, i, vp, sz, vp]
+    lib.flashbob_bob_ex.argtypes = [vp] * 7 + [vp] * 4 + [i, i, i, i, i, f, i, i, i, vp, sz, vp]
     lib.flashbob_bob_ex.restype = i
-    lib.flashbob_rowstats_ex.argtypes = [vp] * 7 + [vp] * 4 + [i, i, i, i, f, i, i, vp]
+    lib.flashbob_rowstats_ex.argtypes = [vp] * 7 + [vp] * 4 + [i, i, i, i, i, f, i, i, vp]
     lib.flashbob_rowstats_ex.restype = i
     lib.flashbob_strerror.argtypes = [i]
     lib.flashbob_strerror.restype = ctypes.c_char_p
@@ -117,17 +117,24 @@ def _stream_handle(device, stream):
 
 
 def _inputs(Q, K, V, dO, gQ, gK, gV):
+    """Checks shapes; returns the inputs and the key/value head count."""
     ins = (Q, K, V, dO, gQ, gK, gV)
-    for t in ins:
-        if not isinstance(t, torch.Tensor) or not t.is_cuda:
-            raise TypeError("all inputs must be device tensors")
-        if t.shape != Q.shape or t.dtype != Q.dtype or t.device != Q.device:
-            raise ValueError("all inputs need the same shape, dtype and device")
-        if not t.is_contiguous():
-            raise ValueError("inputs must be contiguous [B, H, N, d]")
     if Q.dim() != 4:
         raise ValueError("inputs must be [B, H, N, d]")
-    return ins
+    B, H, N, d = Q.shape
+    for k, t in enumerate(ins):
+        if not isinstance(t, torch.Tensor) or not t.is_cuda:
+            raise TypeError("all inputs must be device tensors")
+        if t.dtype != Q.dtype or t.device != Q.device:
+            raise ValueError("all inputs need the same dtype and device")
+        if not t.is_contiguous():
+            raise ValueError("inputs must be contiguous [B, H, N, d]")
+        want = Q.shape if k in (0, 3, 4) else K.shape  # Q, dO, gQ | K, V, gK, gV
+        if t.shape != want:
+            raise ValueError("Q, dO, gQ need one shape and K, V, gK, gV another")
+    if K.dim() != 4 or K.shape[0] != B or K.shape[2:] != Q.shape[2:] or K.shape[1] < 1 or H % K.shape[1]:
+        raise ValueError("K, V, gK, gV must be [B, H_kv, N, d] with H a multiple of H_kv")
+    return ins, K.shape[1]
 
 
 def workspace_bytes(B, H, N, d):
@@ -137,14 +144,15 @@ def workspace_bytes(B, H, N, d):
 def bob_stage(stage, Q, K, V, dO, gQ, gK, gV, out, workspace, scale=None, stream=None, causal=False):
     """Run one kernel of bob(): stage in STAGES ("pass1", "pass2_query", "pass2_key")."""
     lib = load_library()
-    ins = _inputs(Q, K, V, dO, gQ, gK, gV)
+    ins, Hkv = _inputs(Q, K, V, dO, gQ, gK, gV)
     B, H, N, d = Q.shape
     if scale is None:
         scale = d ** -0.5
-    if causal:
-        rc = lib.flashbob_bob_ex(*[_ptr(t) for t in ins], *[_ptr(t) for t in out], B, H, N, d,
-                                 ctypes.c_float(scale), _dtype_code(Q.dtype), FLASHBOB_CAUSAL, STAGE_BITS[stage],
-                                 _ptr(workspace), ctypes.c_size_t(workspace.numel() * workspace.element_size()),
+    if causal or Hkv != H:
+        rc = lib.flashbob_bob_ex(*[_ptr(t) for t in ins], *[_ptr(t) for t in out], B, H, Hkv, N, d,
+                                 ctypes.c_float(scale), _dtype_code(Q.dtype), FLASHBOB_CAUSAL if causal else 0,
+                                 STAGE_BITS[stage], _ptr(workspace),
+                                 ctypes.c_size_t(workspace.numel() * workspace.element_size()),
                                  _stream_handle(Q.device, stream))
     else:
         fn = getattr(lib, STAGES[stage])
@@ -162,21 +170,24 @@ def bob(Q, K, V, dO, gQ, gK, gV, scale=None, out=None, workspace=None, stream=No
     1/sqrt(d). `out` (four float32 tensors) and `workspace` (uint8 tensor of
     at least workspace_bytes(B, H, N, d)) may be given to avoid allocation.
     causal=True masks key j > query i (flashbob_bob_ex with FLASHBOB_CAUSAL).
+    K, V, gK, gV may have fewer heads than Q (grouped-query attention): then
+    gradK, gradV have their shape and sum over each group's query heads.
     """
     lib = load_library()
-    ins = _inputs(Q, K, V, dO, gQ, gK, gV)
+    ins, Hkv = _inputs(Q, K, V, dO, gQ, gK, gV)
     B, H, N, d = Q.shape
     if scale is None:
         scale = d ** -0.5
     if out is None:
-        out = tuple(torch.empty((B, H, N, d), dtype=torch.float32, device=Q.device) for _ in range(4))
+        shapes = ((B, H, N, d), (B, Hkv, N, d), (B, Hkv, N, d), (B, H, N, d))
+        out = tuple(torch.empty(s, dtype=torch.float32, device=Q.device) for s in shapes)
     nws = lib.flashbob_workspace_bytes(B, H, N, d)
     if workspace is None:
         workspace = torch.empty(max(nws, 1), dtype=torch.uint8, device=Q.device)
-    if causal:
-        rc = lib.flashbob_bob_ex(*[_ptr(t) for t in ins], *[_ptr(t) for t in out], B, H, N, d,
-                                 ctypes.c_float(scale), _dtype_code(Q.dtype), FLASHBOB_CAUSAL, 7, _ptr(workspace),
-                                 ctypes.c_size_t(workspace.numel() * workspace.element_size()),
+    if causal or Hkv != H:
+        rc = lib.flashbob_bob_ex(*[_ptr(t) for t in ins], *[_ptr(t) for t in out], B, H, Hkv, N, d,
+                                 ctypes.c_float(scale), _dtype_code(Q.dtype), FLASHBOB_CAUSAL if causal else 0, 7,
+                                 _ptr(workspace), ctypes.c_size_t(workspace.numel() * workspace.element_size()),
                                  _stream_handle(Q.device, stream))
     else:
         rc = lib.flashbob_bob(*[_ptr(t) for t in ins], *[_ptr(t) for t in out], B, H, N, d,
@@ -190,12 +201,12 @@ def bob(Q, K, V, dO, gQ, gK, gV, scale=None, out=None, workspace=None, stream=No
 def rowstats(Q, K, V, dO, gQ, gK, gV, scale=None, stream=None, causal=False):
     """Pass 1 alone: (LSE, D, c, r) per query row, each [B, H, N] float32."""
     lib = load_library()
-    ins = _inputs(Q, K, V, dO, gQ, gK, gV)
+    ins, Hkv = _inputs(Q, K, V, dO, gQ, gK, gV)
     B, H, N, d = Q.shape
     if scale is None:
         scale = d ** -0.5
     outs = tuple(torch.empty((B, H, N), dtype=torch.float32, device=Q.device) for _ in range(4))
-    rc = lib.flashbob_rowstats_ex(*[_ptr(t) for t in ins], *[_ptr(t) for t in outs], B, H, N, d,
+    rc = lib.flashbob_rowstats_ex(*[_ptr(t) for t in ins], *[_ptr(t) for t in outs], B, H, Hkv, N, d,
                                   ctypes.c_float(scale), _dtype_code(Q.dtype),
                                   FLASHBOB_CAUSAL if causal else 0, _stream_handle(Q.device, stream))
     _check(rc)

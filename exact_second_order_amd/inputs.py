@@ -54,12 +54,18 @@ WORKLOADS = (
 )
 
 
-def make_inputs(B, H, N, d, dtype, seed, qk_factor=1.0):
-    """Return the seven input tensors (CPU, `dtype`) as a dict keyed by NAMES."""
+def make_inputs(B, H, N, d, dtype, seed, qk_factor=1.0, H_kv=None):
+    """Return the seven input tensors (CPU, `dtype`) as a dict keyed by NAMES.
+
+    H_kv (default H) gives K, V, gK, gV that many heads (grouped-query
+    attention); the draw order and distribution are unchanged.
+    """
     g = torch.Generator(device="cpu").manual_seed(int(seed))
+    hkv = H if H_kv is None else H_kv
     out = {}
     for name in NAMES:
-        x = torch.randn((B, H, N, d), generator=g, dtype=torch.float32)
+        heads = hkv if name in ("K", "V", "gK", "gV") else H
+        x = torch.randn((B, heads, N, d), generator=g, dtype=torch.float32)
         if name in ("Q", "K") and qk_factor != 1.0:
             x.mul_(qk_factor)
         out[name] = x.to(dtype)

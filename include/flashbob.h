@@ -136,6 +136,12 @@ int flashbob_bob_pass2_key(const void* Q, const void* K, const void* V, const vo
                            void* workspace, size_t workspace_bytes, void* stream);
 
 /* General form of flashbob_bob and of the three stage calls below:
+ *   H_kv    key/value heads (grouped-query attention; H_kv = H is plain
+ *           multi-head, H_kv = 1 multi-query). 1 <= H_kv <= H, H a multiple
+ *           of H_kv. Q, dO, gQ, gradQ, graddO are [B, H, N, d]; K, V, gK, gV,
+ *           gradK, gradV are [B, H_kv, N, d]; query head h uses key/value head
+ *           h / (H / H_kv), and gradK, gradV sum over each group's query heads
+ *           (the gradients of the shared heads). Otherwise FLASHBOB_ERR_SHAPE.
  *   flags   0 or FLASHBOB_CAUSAL. Causal: per head, each query row i uses
  *           keys 0..i only; key blocks wholly above the diagonal are skipped,
  *           so the work is about half.
@@ -148,7 +154,7 @@ int flashbob_bob_pass2_key(const void* Q, const void* K, const void* V, const vo
 int flashbob_bob_ex(const void* Q, const void* K, const void* V, const void* dO,
                     const void* gQ, const void* gK, const void* gV,
                     float* gradQ, float* gradK, float* gradV, float* graddO,
-                    int B, int H, int N, int d, float scale, int dtype, int flags, int stages,
+                    int B, int H, int H_kv, int N, int d, float scale, int dtype, int flags, int stages,
                     void* workspace, size_t workspace_bytes, void* stream);
 
 /* Pass 1 alone (row statistics), exported for testing the first pass.
@@ -163,12 +169,13 @@ int flashbob_rowstats(const void* Q, const void* K, const void* V, const void* d
                       int B, int H, int N, int d, float scale, int dtype,
                       void* stream);
 
-/* flashbob_rowstats with flags (0 or FLASHBOB_CAUSAL; with the mask, the
- * row scalars are those of the causal attention). */
+/* flashbob_rowstats with key/value heads H_kv (as for flashbob_bob_ex) and
+ * flags (0 or FLASHBOB_CAUSAL; with the mask, the row scalars are those of the
+ * causal attention). */
 int flashbob_rowstats_ex(const void* Q, const void* K, const void* V, const void* dO,
                          const void* gQ, const void* gK, const void* gV,
                          float* lse, float* D, float* c, float* r,
-                         int B, int H, int N, int d, float scale, int dtype, int flags,
+                         int B, int H, int H_kv, int N, int d, float scale, int dtype, int flags,
                          void* stream);
 
 /* Static description of an error code; for FLASHBOB_ERR_HIP, the HIP error

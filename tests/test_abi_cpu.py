@@ -177,11 +177,11 @@ def test_rowstats_validation():
     assert lib.flashbob_rowstats(*ins, *bad, 1, 1, 128, 64, ctypes.c_float(0.1), F32, vp(0)) == ALIGN
 
 
-def call_ex(ins, outs, B, H, N, d, scale, dtype, wsp, nws, flags=0, stages=7):
+def call_ex(ins, outs, B, H, N, d, scale, dtype, wsp, nws, flags=0, stages=7, hkv=None):
     lib = fb.load_library()
     vp = ctypes.c_void_p
-    return lib.flashbob_bob_ex(*[vp(p) for p in ins], *[vp(p) for p in outs], B, H, N, d, ctypes.c_float(scale),
-                               dtype, flags, stages, vp(wsp), ctypes.c_size_t(nws), vp(0))
+    return lib.flashbob_bob_ex(*[vp(p) for p in ins], *[vp(p) for p in outs], B, H, H if hkv is None else hkv, N, d,
+                               ctypes.c_float(scale), dtype, flags, stages, vp(wsp), ctypes.c_size_t(nws), vp(0))
 
 
 def test_ex_rejects_unknown_flags_and_stage_sets():
@@ -198,10 +198,40 @@ def test_ex_rejects_unknown_flags_and_stage_sets():
     vp = ctypes.c_void_p
     ins = [vp(BASE + i * STRIDE) for i in range(7)]
     outs = [vp(BASE + (7 + i) * STRIDE) for i in range(4)]
-    assert lib.flashbob_rowstats_ex(*ins, *outs, 1, 1, 128, 64, ctypes.c_float(0.1), F32, 2, vp(0)) == FLAGS
+    assert lib.flashbob_rowstats_ex(*ins, *outs, 1, 1, 1, 128, 64, ctypes.c_float(0.1), F32, 2, vp(0)) == FLAGS
 
 
 def test_ex_empty_problem_is_a_noop():
     # B*H*N == 0 returns OK before any HIP call, with or without the mask
     for flags in (0, 1):
         assert call_ex(*fake_args(B=0), flags=flags) == 0
+
+
+def test_ex_rejects_bad_kv_head_counts():
+    for H, hkv in ((4, 0), (4, 3), (4, 5), (4, -1), (6, 4)):
+        assert call_ex(*fake_args(H=H), hkv=hkv) == SHAPE, (H, hkv)
+    lib = fb.load_library()
+    vp = ctypes.c_void_p
+    ins = [vp(BASE + i * STRIDE) for i in range(7)]
+    outs = [vp(BASE + (7 + i) * STRIDE) for i in range(4)]
+    assert lib.flashbob_rowstats_ex(*ins, *outs, 1, 4, 3, 128, 64, ctypes.c_float(0.1), F32, 0, vp(0)) == SHAPE
+
+
+def test_ex_alias_check_uses_kv_sizes():
+    # with H = 4, H_kv = 1 the key/value tensors are a quarter of the query
+    # ones: gradK placed right after K's (smaller) extent is legal (the call
+    # then fails only for want of a device: skipped where one exists, as it
+    # would launch on fake pointers), and overlapping it is caught
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("would launch kernels on a real device with fake pointers")
+    B, H, N, d = 1, 4, 128, 64
+    ins, outs, *_ = fake_args(B=B, H=H, N=N, d=d)
+    nws = fb.load_library().flashbob_workspace_bytes(B, H, N, d)
+    kv_bytes = B * 1 * N * d * 4
+    ins = list(ins)
+    outs = list(outs)
+    outs[1] = ins[1] + kv_bytes            # gradK starts where K ends
+    assert call_ex(ins, outs, B, H, N, d, 0.1, F32, BASE + 11 * STRIDE, nws, hkv=1) == -100
+    outs[1] = ins[1] + kv_bytes - 16       # one chunk of overlap
+    assert call_ex(ins, outs, B, H, N, d, 0.1, F32, BASE + 11 * STRIDE, nws, hkv=1) == -8
