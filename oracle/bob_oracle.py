@@ -49,6 +49,7 @@ __all__ = [
     "bob_blocked_head",
     "bob_blocked",
     "bob_gqa",
+    "attention_backward_batched",
 ]
 
 
@@ -325,3 +326,23 @@ def bob_gqa(Q, K, V, dO, gQ, gK, gV, scale, causal=False, block=None):
             gradK[b, j] += gk
             gradV[b, j] += gv
     return gradQ, gradK, gradV, graddO
+
+
+def attention_backward_batched(Q, K, V, dO, scale, causal=False):
+    """First backward (dQ, dK, dV) over [B, H, N, d] queries and [B, Hkv, N, d]
+    keys/values (Hkv divides H; query head h uses key/value head h // (H/Hkv),
+    and the shared heads' dK, dV sum over the group)."""
+    Q, K, V, dO = _f64(Q, K, V, dO)
+    B, H = Q.shape[:2]
+    G = H // K.shape[1]
+    dQ = np.empty_like(Q)
+    dK = np.zeros_like(K)
+    dV = np.zeros_like(V)
+    for b in range(B):
+        for h in range(H):
+            j = h // G
+            q, k, v = attention_backward(Q[b, h], K[b, j], V[b, j], dO[b, h], scale, causal)
+            dQ[b, h] = q
+            dK[b, j] += k
+            dV[b, j] += v
+    return dQ, dK, dV

@@ -496,3 +496,44 @@ def test_gqa_planted_mistake_is_caught(monkeypatch):
     monkeypatch.setattr(bob_oracle, "bob_head", first_only)
     got = oracle.bob_gqa(*xs, 0.5)
     assert max(rel(g, r) for g, r in zip(got, ref)) > 1e-3
+
+
+# ----------------------------------------------------------------------------
+# the first backward itself (returned by the library on request): pinned
+# against torch autograd of <dO, attention(Q, K, V)>, with and without the
+# causal mask
+
+
+@pytest.mark.parametrize("causal", [False, True], ids=["full", "causal"])
+@pytest.mark.parametrize("N,d", [(1, 3), (6, 4), (33, 8)])
+def test_first_backward_matches_autograd(N, d, causal):
+    xs = rand_inputs(N, d, seed=400 + N + d + causal)
+    s = 0.35
+    got = oracle.attention_backward(*xs[:4], s, causal=causal)
+    Q, K, V = [torch.tensor(x, requires_grad=True) for x in xs[:3]]
+    dO = torch.tensor(xs[3])
+    attn = torch_attn_causal(Q, K, V, s) if causal else torch_attn(Q, K, V, s)
+    ref = torch.autograd.grad(torch.sum(dO * attn), (Q, K, V))
+    for g, r in zip(got, ref):
+        r = r.numpy()
+        if np.linalg.norm(r) == 0:
+            assert np.abs(g).max() < 1e-13
+        else:
+            assert rel(g, r) < 1e-12
+
+
+def test_first_backward_batched_gqa_matches_autograd():
+    rng = np.random.default_rng(77)
+    B, H, Hkv, N, d = 2, 4, 2, 7, 4
+    Q, dO = rng.standard_normal((B, H, N, d)), rng.standard_normal((B, H, N, d))
+    K, V = rng.standard_normal((B, Hkv, N, d)), rng.standard_normal((B, Hkv, N, d))
+    for causal in (False, True):
+        got = oracle.attention_backward_batched(Q, K, V, dO, 0.4, causal=causal)
+        tq, tk, tv = [torch.tensor(x, requires_grad=True) for x in (Q, K, V)]
+        S = 0.4 * tq @ tk.repeat_interleave(2, dim=1).transpose(-1, -2)
+        if causal:
+            S = S.masked_fill(torch.ones(N, N, dtype=torch.bool).triu(1), float("-inf"))
+        out = torch.softmax(S, dim=-1) @ tv.repeat_interleave(2, dim=1)
+        ref = torch.autograd.grad(torch.sum(torch.tensor(dO) * out), (tq, tk, tv))
+        for g, r in zip(got, ref):
+            assert rel(g, r.numpy()) < 1e-12
