@@ -50,6 +50,7 @@ __all__ = [
     "bob_blocked",
     "bob_gqa",
     "attention_backward_batched",
+    "attention_backward_rows_head",
 ]
 
 
@@ -346,3 +347,19 @@ def attention_backward_batched(Q, K, V, dO, scale, causal=False):
             dK[b, j] += k
             dV[b, j] += v
     return dQ, dK, dV
+
+
+def attention_backward_rows_head(Q, K, V, dO, scale, rows, causal=False):
+    """First-backward dQ of one head for the query rows `rows` only (exact).
+
+    dQ_i = scale sum_j dS_ij K_j needs, besides row i of Q and dO, only that
+    row's softmax and D_i = dO_i . O_i, so the rows' values equal those of
+    the full first backward (same formulas as attention_backward).
+    """
+    Q, K, V, dO = _f64(Q, K, V, dO)
+    rows = np.asarray(rows)
+    P = softmax_rows(_mask_scores(scale * (Q[rows] @ K.T), rows, causal))
+    dOr = dO[rows]
+    D = np.sum(dOr * (P @ V), axis=1, keepdims=True)
+    dS = P * (dOr @ V.T - D)
+    return scale * (dS @ K)

@@ -537,3 +537,19 @@ def test_first_backward_batched_gqa_matches_autograd():
         ref = torch.autograd.grad(torch.sum(torch.tensor(dO) * out), (tq, tk, tv))
         for g, r in zip(got, ref):
             assert rel(g, r.numpy()) < 1e-12
+
+
+@pytest.mark.parametrize("causal", [False, True], ids=["full", "causal"])
+def test_first_backward_rows_match_autograd(causal):
+    # the row form (for sampled rows of long sequences) against autograd,
+    # on rows that include the first and last (the causal extremes)
+    xs = rand_inputs(40, 6, seed=91 + causal)
+    s = 0.3
+    rows = np.array([0, 1, 17, 38, 39])
+    got = oracle.attention_backward_rows_head(*xs[:4], s, rows, causal=causal)
+    Q, K, V = [torch.tensor(x, requires_grad=True) for x in xs[:3]]
+    attn = torch_attn_causal(Q, K, V, s) if causal else torch_attn(Q, K, V, s)
+    ref = torch.autograd.grad(torch.sum(torch.tensor(xs[3]) * attn), Q)[0].numpy()[rows]
+    assert rel(got, ref) < 1e-12
+    if causal:
+        assert np.abs(got[0]).max() < 1e-14  # one visible key: dS = 0
