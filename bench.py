@@ -97,6 +97,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--causal", action="store_true",
                     help="causal masking (not the headline); flops credited for the N(N+1)/2 visible pairs")
+    ap.add_argument("--first-backward", action="store_true",
+                    help="also return the first backward dQ, dK, dV (not the headline); credited with its "
+                         "three extra products")
     ap.add_argument("--copy-mb", type=int, default=0,
                     help="run one plain device copy of this many MiB first (calibrates HBM byte counters)")
     args = ap.parse_args()
@@ -118,6 +121,8 @@ def main():
     x = [ins[k].to(dev) for k in NAMES]
     out = tuple(torch.empty(x[0].shape, dtype=torch.float32, device=dev) for _ in range(4))
     ws = torch.empty(fb.workspace_bytes(w.B, w.H, w.N, w.d), dtype=torch.uint8, device=dev)
+    first = (tuple(torch.empty(x[0].shape, dtype=torch.float32, device=dev) for _ in range(3))
+             if args.first_backward else None)
     stream = torch.cuda.current_stream(dev)
     if args.copy_mb > 0:
         src = torch.ones(args.copy_mb << 18, dtype=torch.float32, device=dev)
@@ -131,6 +136,8 @@ def main():
     stages = list(fb.STAGES)
     # algorithmic flops of each kernel: its N x N x d products x 2 N^2 d
     units = {"pass1": 5, "pass2_query": 9, "pass2_key": 8}
+    if args.first_backward:  # + dQ = s dS K in pass 2q, dK = s dS^T Q and dV = P^T dO in pass 2k
+        units = {"pass1": 5, "pass2_query": 10, "pass2_key": 10}
     kernel_names = {"pass1": "query_kernel<.., false>", "pass2_query": "query_kernel<.., true>",
                     "pass2_key": "key_kernel"}
 
@@ -138,7 +145,7 @@ def main():
         for i, st in enumerate(stages):
             if ev is not None:
                 ev[i].record(stream)
-            fb.bob_stage(st, *x, out=out, workspace=ws, scale=w.scale, causal=args.causal)
+            fb.bob_stage(st, *x, out=out, workspace=ws, scale=w.scale, causal=args.causal, first=first)
         if ev is not None:
             ev[len(stages)].record(stream)
 
@@ -166,7 +173,9 @@ def main():
     ms_median = step_ms[len(step_ms) // 2] if len(step_ms) % 2 else 0.5 * (
         step_ms[len(step_ms) // 2 - 1] + step_ms[len(step_ms) // 2])
     frac_pairs = (w.N + 1) / (2.0 * w.N) if args.causal else 1.0  # visible (query, key) pairs
-    flops = w.flops * frac_pairs
+    # credited: the 17 products of the method (not the 22 the kernels execute),
+    # plus the first backward's three when it is returned
+    flops = (w.flops + (6.0 * w.B * w.H * w.N * w.N * w.d if args.first_backward else 0.0)) * frac_pairs
     tflops = flops / (ms_step * 1e-3) / 1e12
     peak = PEAK_TFLOPS[w.dtype_name]
     per_kernel = {}
@@ -179,7 +188,8 @@ def main():
         f"kernels {per_kernel}")
     dom = max(stages, key=lambda st: per_kernel[st]["ms"])
     roofline = {"bound": "mfma", "achieved": per_kernel[dom]["tflops"], "peak": peak, "unit": "TFLOP/s",
-                "frac": per_kernel[dom]["frac"], "traffic": measured_traffic(dom, args.causal),
+                "frac": per_kernel[dom]["frac"],
+                "traffic": None if args.first_backward else measured_traffic(dom, args.causal),
                 "kernel": kernel_names[dom], "launch_ms": per_kernel[dom]["ms"]}
 
     cpu = None
@@ -202,9 +212,10 @@ def main():
         "vs_baseline": None,
         "dtype": w.dtype_name,
         "data": "synthetic",
-        "config": {"workload": w.name + ("_causal" if args.causal else ""), "B": w.B, "H": w.H, "N": w.N,
+        "config": {"workload": w.name + ("_causal" if args.causal else "") + ("_first" if args.first_backward else ""),
+                   "B": w.B, "H": w.H, "N": w.N,
                    "d": w.d, "dtype": w.dtype_name, "scale": w.scale, "causal": bool(args.causal),
-                   "seed": WORKLOADS.index(w),
+                   "first_backward": bool(args.first_backward), "seed": WORKLOADS.index(w),
                    "flops_per_step": flops, "frac_of_peak": round(tflops / peak, 4),
                    "ms_median_events": round(ms_median, 4), "ms_min_events": round(step_ms[0], 4),
                    "peak_mem_delta_bytes": int(peak_mem_delta), "kernels": per_kernel},

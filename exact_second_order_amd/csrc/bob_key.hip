@@ -28,7 +28,7 @@
 
 namespace flashbob {
 
-template <typename T, int D_>
+template <typename T, int D_, bool FIRST = false>
 struct KeyCfg {
   static constexpr int D = D_;
   static constexpr int BC = 128;                       // keys per workgroup (4 waves x 32)
@@ -37,12 +37,13 @@ struct KeyCfg {
   static constexpr int NCH = D / 16, NDB = D / 32;
   // same staging and occupancy choices as the query-major kernel
   static constexpr bool SWZ = sizeof(T) == 2 && D == 64;
-  static constexpr bool OCC2 = SWZ;
+  // (FIRST: the first-backward dK, dV accumulators need the one-wave budget)
+  static constexpr bool OCC2 = SWZ && !FIRST;
   static constexpr int NBUF = 2;                       // stage n in use, stage n+1 arriving
   // SWZ: which of the wave's K, gK, V, gV operand tensors (bits 0..3) live in
   // LDS instead of registers: gV only, which is what the register budget of two
   // waves per SIMD leaves over (every per-block LDS read costs time)
-  static constexpr int KLDS = SWZ ? 0x8 : 0;
+  static constexpr int KLDS = OCC2 ? 0x8 : 0;
   static constexpr int NKLDS = __builtin_popcount(KLDS);
   static constexpr int ROWLEN = SWZ ? D : LDQ;
   static constexpr int QSTAGE = 3 * BQ * ROWLEN;       // Q, gQ, dO elements of one stage
@@ -91,13 +92,14 @@ __device__ __forceinline__ f32x16 rows_as_acc(const float* v) {
 // start at -D, -c/s, -r): dP - D, G/s - c/s, H - r. TAIL zeroes P for keys
 // past the sequence end and for query rows outside [q_lo, nq_rel) (q_lo: the
 // causal mask, query row >= this lane's key; otherwise <= 0).
-template <typename T, bool TAIL>
+template <typename T, bool TAIL, bool FIRST>
 __device__ __forceinline__ void key_chunk(int cc, const f32x16& S, const f32x16& G, const f32x16& dP,
                                           const f32x16& H, const float* sl, float sl2, float scale, bool kvalid,
                                           int q_lo, int nq_rel, typename Elem<T>::frag& fdS,
-                                          typename Elem<T>::frag& fdS2, typename Elem<T>::frag& fA) {
+                                          typename Elem<T>::frag& fdS2, typename Elem<T>::frag& fA,
+                                          typename Elem<T>::frag& fP) {
   const int h = lane_id() >> 5;
-  f32x8 dS, dS2, A;
+  f32x8 dS, dS2, A, P;
 #pragma unroll
   for (int gg = 0; gg < 2; ++gg) {
     const int g = 2 * cc + gg;
@@ -113,21 +115,26 @@ __device__ __forceinline__ void key_chunk(int cc, const f32x16& S, const f32x16&
       dS[s] = ds;
       A[s] = p * gv;
       dS2[s] = fmaf(ds, gv, p * H[i]);
+      if constexpr (FIRST) P[s] = p;
     }
   }
   to_frag(fdS, dS);
   to_frag(fdS2, dS2);
   to_frag(fA, A);
+  if constexpr (FIRST) to_frag(fP, P);
 }
 
-template <typename T, int D>
-__global__ __launch_bounds__(256, (KeyCfg<T, D>::OCC2 ? 2 : 1)) void key_kernel(
+// FIRST: also return the first-backward dK = s dS^T Q and dV = P^T dO (two
+// more products per block against operands already read).
+template <typename T, int D, bool FIRST>
+__global__ __launch_bounds__(256, (KeyCfg<T, D, FIRST>::OCC2 ? 2 : 1)) void key_kernel(
     const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V, const T* __restrict__ dO,
     const T* __restrict__ gQ, const T* __restrict__ gK, const T* __restrict__ gV,
     const float* __restrict__ lse2, const float* __restrict__ Dv, const float* __restrict__ cv,
-    const float* __restrict__ rv, float* __restrict__ gradK, float* __restrict__ gradV, int N, int nkblk,
+    const float* __restrict__ rv, float* __restrict__ gradK, float* __restrict__ gradV, float* __restrict__ dKo,
+    float* __restrict__ dVo, int N, int nkblk,
     float scale, int causal, int G) {
-  using Cfg = KeyCfg<T, D>;
+  using Cfg = KeyCfg<T, D, FIRST>;
   using E = Elem<T>;
   using F = typename E::frag;
   constexpr int BQ = Cfg::BQ, LDQ = Cfg::LDQ, NCH = Cfg::NCH, NDB = Cfg::NDB, NBUF = Cfg::NBUF;
@@ -199,11 +206,15 @@ __global__ __launch_bounds__(256, (KeyCfg<T, D>::OCC2 ? 2 : 1)) void key_kernel(
                   : t == 1 ? bgK[(KLDS & 2) ? 0 : c] : t == 2 ? bV[(KLDS & 4) ? 0 : c] : bgV[(KLDS & 8) ? 0 : c];
   };
   // gradK^T, gradV^T: d rows x the wave's 32 keys
-  f32x16 accK[NDB], accV[NDB];
+  f32x16 accK[NDB], accV[NDB], accdK[FIRST ? NDB : 1], accdV[FIRST ? NDB : 1];
 #pragma unroll
   for (int j = 0; j < NDB; ++j) {
     accK[j] = f32x16{};
     accV[j] = f32x16{};
+    if constexpr (FIRST) {
+      accdK[j] = f32x16{};
+      accdV[j] = f32x16{};
+    }
   }
   const float sl2 = scale * kLog2e;
   const int nblk = (N + BQ - 1) / BQ;  // 32-query blocks = stages
@@ -284,15 +295,15 @@ __global__ __launch_bounds__(256, (KeyCfg<T, D>::OCC2 ? 2 : 1)) void key_kernel(
     }
   };
   struct Frags {
-    F dS[2], dS2[2], A[2];
+    F dS[2], dS2[2], A[2], P[FIRST ? 2 : 1];
   };
   // TAIL: masks keys past the end (the whole sweep of the last key block)
   // and query rows past the end (last query block)
   auto elementwise = [&](auto tail, int n, int cc, const Tiles& t, Frags& f) __attribute__((always_inline)) {
     constexpr bool TAIL = decltype(tail)::value;
     const int b = n & (NBUF - 1);
-    key_chunk<T, TAIL>(cc, t.S, t.G, t.dP, t.H, sS(b, 0), sl2, scale, kvalid, causal ? key - n * BQ : 0,
-                       N - n * BQ, f.dS[cc], f.dS2[cc], f.A[cc]);
+    key_chunk<T, TAIL, FIRST>(cc, t.S, t.G, t.dP, t.H, sS(b, 0), sl2, scale, kvalid, causal ? key - n * BQ : 0,
+                       N - n * BQ, f.dS[cc], f.dS2[cc], f.A[cc], f.P[FIRST ? cc : 0]);
   };
   auto outputs = [&](int n, int cc, const Frags& f) __attribute__((always_inline)) {
     const int b = n & (NBUF - 1);
@@ -305,6 +316,10 @@ __global__ __launch_bounds__(256, (KeyCfg<T, D>::OCC2 ? 2 : 1)) void key_kernel(
       E::mma(accK[j], tQ, f.dS2[cc]);
       E::mma(accK[j], tgQ, f.dS[cc]);
       E::mma(accV[j], tdO, f.A[cc]);
+      if constexpr (FIRST) {
+        E::mma(accdK[j], tQ, f.dS[cc]);
+        E::mma(accdV[j], tdO, f.P[cc]);
+      }
     }
   };
 
@@ -364,33 +379,45 @@ __global__ __launch_bounds__(256, (KeyCfg<T, D>::OCC2 ? 2 : 1)) void key_kernel(
                                                           scale * accK[j][4 * g + 2], scale * accK[j][4 * g + 3]);
         *reinterpret_cast<float4*>(gv + d0) =
             make_float4(accV[j][4 * g], accV[j][4 * g + 1], accV[j][4 * g + 2], accV[j][4 * g + 3]);
+        if constexpr (FIRST) {
+          const size_t o = hoff + (size_t)key * D + d0;
+          *reinterpret_cast<float4*>(dKo + o) = make_float4(scale * accdK[j][4 * g], scale * accdK[j][4 * g + 1],
+                                                            scale * accdK[j][4 * g + 2], scale * accdK[j][4 * g + 3]);
+          *reinterpret_cast<float4*>(dVo + o) =
+              make_float4(accdV[j][4 * g], accdV[j][4 * g + 1], accdV[j][4 * g + 2], accdV[j][4 * g + 3]);
+        }
       }
     }
   }
 }
 
-template <typename T, int D>
+template <typename T, int D, bool FIRST>
 hipError_t launch_key(const void* Q, const void* K, const void* V, const void* dO, const void* gQ, const void* gK,
                       const void* gV, const float* lse2, const float* Dv, const float* cv, const float* rv,
-                      float* gradK, float* gradV, int BHkv, int N, float scale, int causal, int G,
-                      hipStream_t stream) {
-  using Cfg = KeyCfg<T, D>;
+                      float* gradK, float* gradV, float* dK, float* dV, int BHkv, int N, float scale, int causal,
+                      int G, hipStream_t stream) {
+  using Cfg = KeyCfg<T, D, FIRST>;
   const int nkblk = (N + Cfg::BC - 1) / Cfg::BC;
   const long long nblocks = (long long)nkblk * BHkv;
   if (nblocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-  key_kernel<T, D><<<dim3((unsigned)nblocks), dim3(256), 0, stream>>>(
+  key_kernel<T, D, FIRST><<<dim3((unsigned)nblocks), dim3(256), 0, stream>>>(
       (const T*)Q, (const T*)K, (const T*)V, (const T*)dO, (const T*)gQ, (const T*)gK, (const T*)gV, lse2, Dv, cv,
-      rv, gradK, gradV, N, nkblk, scale, causal, G);
+      rv, gradK, gradV, dK, dV, N, nkblk, scale, causal, G);
   return hipGetLastError();
 }
 
-#define FLASHBOB_INST_KEY(T, D)                                                                            \
-  template hipError_t launch_key<T, D>(const void*, const void*, const void*, const void*, const void*,   \
-                                       const void*, const void*, const float*, const float*, const float*, \
-                                       const float*, float*, float*, int, int, float, int, int, hipStream_t);
-FLASHBOB_INST_KEY(bf16, 64)
-FLASHBOB_INST_KEY(bf16, 128)
-FLASHBOB_INST_KEY(float, 64)
-FLASHBOB_INST_KEY(float, 128)
+#define FLASHBOB_INST_KEY(T, D, F)                                                                         \
+  template hipError_t launch_key<T, D, F>(const void*, const void*, const void*, const void*, const void*, \
+                                          const void*, const void*, const float*, const float*,             \
+                                          const float*, const float*, float*, float*, float*, float*, int,  \
+                                          int, float, int, int, hipStream_t);
+FLASHBOB_INST_KEY(bf16, 64, false)
+FLASHBOB_INST_KEY(bf16, 128, false)
+FLASHBOB_INST_KEY(float, 64, false)
+FLASHBOB_INST_KEY(float, 128, false)
+FLASHBOB_INST_KEY(bf16, 64, true)
+FLASHBOB_INST_KEY(bf16, 128, true)
+FLASHBOB_INST_KEY(float, 64, true)
+FLASHBOB_INST_KEY(float, 128, true)
 
 }  // namespace flashbob

@@ -179,12 +179,16 @@ __device__ __forceinline__ void query_chunk(int cc, const f32x16& S, const f32x1
   to_frag(fA, A);
 }
 
-template <typename T, int D, bool GRADQ>
-__global__ __launch_bounds__(256, (QueryCfg<T, D, GRADQ>::OCC2 ? 2 : 1)) void query_kernel(
+// FIRST (pass 2q only): also return the first-backward dQ = s dS K (one more
+// product per block against the K^T operand already read; the extra
+// accumulator needs the one-wave-per-SIMD register budget).
+template <typename T, int D, bool GRADQ, bool FIRST>
+__global__ __launch_bounds__(256, (QueryCfg<T, D, GRADQ>::OCC2 && !FIRST ? 2 : 1)) void query_kernel(
     const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V, const T* __restrict__ dO,
     const T* __restrict__ gQ, const T* __restrict__ gK, const T* __restrict__ gV, float* __restrict__ lse,
     float* __restrict__ Dv, float* __restrict__ cv, float* __restrict__ rv, float* __restrict__ gradQ,
-    float* __restrict__ graddO, int N, int nqblk, float scale, int lse_natural, int causal, int G) {
+    float* __restrict__ graddO, float* __restrict__ dQo, int N, int nqblk, float scale, int lse_natural,
+    int causal, int G) {
   using Cfg = QueryCfg<T, D, GRADQ>;
   using E = Elem<T>;
   using F = typename E::frag;
@@ -245,7 +249,7 @@ __global__ __launch_bounds__(256, (QueryCfg<T, D, GRADQ>::OCC2 ? 2 : 1)) void qu
   // (gradQ^T, graddO^T: d rows x the wave's 32 queries)
   // (pass-2 form: LSE * log2(e), -D, -c, -r)
   float l2 = INFINITY, Dq = 0.f, cq = 0.f, rq = 0.f;
-  f32x16 accQ[GRADQ ? NDB : 1], accO[GRADQ ? NDB : 1];
+  f32x16 accQ[GRADQ ? NDB : 1], accO[GRADQ ? NDB : 1], accdQ[FIRST ? NDB : 1];
   if constexpr (GRADQ) {
     if (qvalid) {
       const size_t o = (size_t)head * N + q;
@@ -258,6 +262,7 @@ __global__ __launch_bounds__(256, (QueryCfg<T, D, GRADQ>::OCC2 ? 2 : 1)) void qu
     for (int j = 0; j < NDB; ++j) {
       accQ[j] = f32x16{};
       accO[j] = f32x16{};
+      if constexpr (FIRST) accdQ[j] = f32x16{};
     }
   }
 
@@ -350,6 +355,7 @@ __global__ __launch_bounds__(256, (QueryCfg<T, D, GRADQ>::OCC2 ? 2 : 1)) void qu
         E::mma(accQ[j], tgK, f.dS[cc]);
         E::mma(accO[j], tV, f.A[cc]);
         E::mma(accO[j], tgV, f.P[cc]);
+        if constexpr (FIRST) E::mma(accdQ[j], tK, f.dS[cc]);
       }
     }
   };
@@ -458,45 +464,53 @@ __global__ __launch_bounds__(256, (QueryCfg<T, D, GRADQ>::OCC2 ? 2 : 1)) void qu
                           scale * accQ[j][4 * g + 3]);
           *reinterpret_cast<float4*>(go + d0) =
               make_float4(accO[j][4 * g], accO[j][4 * g + 1], accO[j][4 * g + 2], accO[j][4 * g + 3]);
+          if constexpr (FIRST)
+            *reinterpret_cast<float4*>(dQo + hoff + (size_t)q * D + d0) =
+                make_float4(scale * accdQ[j][4 * g], scale * accdQ[j][4 * g + 1], scale * accdQ[j][4 * g + 2],
+                            scale * accdQ[j][4 * g + 3]);
         }
       }
     }
   }
 }
 
-template <typename T, int D, bool GRADQ>
+template <typename T, int D, bool GRADQ, bool FIRST>
 hipError_t launch_query(const void* Q, const void* K, const void* V, const void* dO, const void* gQ,
                         const void* gK, const void* gV, float* lse, float* Dv, float* cv, float* rv,
-                        float* gradQ, float* graddO, int BH, int N, float scale, int lse_natural,
+                        float* gradQ, float* graddO, float* dQ, int BH, int N, float scale, int lse_natural,
                         int causal, int G, hipStream_t stream) {
   using Cfg = QueryCfg<T, D, GRADQ>;
   const int nqblk = (N + Cfg::BQ - 1) / Cfg::BQ;
   const long long nblocks = (long long)nqblk * BH;
   if (nblocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-  query_kernel<T, D, GRADQ><<<dim3((unsigned)nblocks), dim3(256), 0, stream>>>(
+  query_kernel<T, D, GRADQ, FIRST><<<dim3((unsigned)nblocks), dim3(256), 0, stream>>>(
       (const T*)Q, (const T*)K, (const T*)V, (const T*)dO, (const T*)gQ, (const T*)gK, (const T*)gV, lse, Dv,
-      cv, rv, gradQ, graddO, N, nqblk, scale, lse_natural, causal, G);
+      cv, rv, gradQ, graddO, dQ, N, nqblk, scale, lse_natural, causal, G);
   return hipGetLastError();
 }
 
-#define FLASHBOB_INST_QUERY(T, D, G)                                                                      \
-  template hipError_t launch_query<T, D, G>(const void*, const void*, const void*, const void*,         \
-                                            const void*, const void*, const void*, float*, float*,      \
-                                            float*, float*, float*, float*, int, int, float, int, int,    \
-                                            int, hipStream_t);
+#define FLASHBOB_INST_QUERY(T, D, G, F)                                                                   \
+  template hipError_t launch_query<T, D, G, F>(const void*, const void*, const void*, const void*,      \
+                                               const void*, const void*, const void*, float*, float*,   \
+                                               float*, float*, float*, float*, float*, int, int, float, \
+                                               int, int, int, hipStream_t);
 // Pass 1 and pass 2q instantiations are built as separate objects (pass 1
 // with MFMA results kept in VGPRs, which its register budget allows).
 #ifndef FLASHBOB_QUERY_PASS2
-FLASHBOB_INST_QUERY(bf16, 64, false)
-FLASHBOB_INST_QUERY(bf16, 128, false)
-FLASHBOB_INST_QUERY(float, 64, false)
-FLASHBOB_INST_QUERY(float, 128, false)
+FLASHBOB_INST_QUERY(bf16, 64, false, false)
+FLASHBOB_INST_QUERY(bf16, 128, false, false)
+FLASHBOB_INST_QUERY(float, 64, false, false)
+FLASHBOB_INST_QUERY(float, 128, false, false)
 #endif
 #ifndef FLASHBOB_QUERY_PASS1
-FLASHBOB_INST_QUERY(bf16, 64, true)
-FLASHBOB_INST_QUERY(bf16, 128, true)
-FLASHBOB_INST_QUERY(float, 64, true)
-FLASHBOB_INST_QUERY(float, 128, true)
+FLASHBOB_INST_QUERY(bf16, 64, true, false)
+FLASHBOB_INST_QUERY(bf16, 128, true, false)
+FLASHBOB_INST_QUERY(float, 64, true, false)
+FLASHBOB_INST_QUERY(float, 128, true, false)
+FLASHBOB_INST_QUERY(bf16, 64, true, true)
+FLASHBOB_INST_QUERY(bf16, 128, true, true)
+FLASHBOB_INST_QUERY(float, 64, true, true)
+FLASHBOB_INST_QUERY(float, 128, true, true)
 #endif
 
 }  // namespace flashbob

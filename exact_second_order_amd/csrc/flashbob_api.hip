@@ -14,16 +14,16 @@
 
 namespace flashbob {
 typedef __bf16 bf16;
-template <typename T, int D, bool GRADQ>
+template <typename T, int D, bool GRADQ, bool FIRST>
 hipError_t launch_query(const void* Q, const void* K, const void* V, const void* dO, const void* gQ,
                         const void* gK, const void* gV, float* lse, float* Dv, float* cv, float* rv,
-                        float* gradQ, float* graddO, int BH, int N, float scale, int lse_natural,
+                        float* gradQ, float* graddO, float* dQ, int BH, int N, float scale, int lse_natural,
                         int causal, int G, hipStream_t stream);
-template <typename T, int D>
+template <typename T, int D, bool FIRST>
 hipError_t launch_key(const void* Q, const void* K, const void* V, const void* dO, const void* gQ, const void* gK,
                       const void* gV, const float* lse2, const float* Dv, const float* cv, const float* rv,
-                      float* gradK, float* gradV, int BHkv, int N, float scale, int causal, int G,
-                      hipStream_t stream);
+                      float* gradK, float* gradV, float* dK, float* dV, int BHkv, int N, float scale, int causal,
+                      int G, hipStream_t stream);
 }  // namespace flashbob
 
 namespace {
@@ -89,44 +89,56 @@ enum Stage {
   kPass2Key = FLASHBOB_STAGE_PASS2_KEY,
 };
 
+// first: also the first-backward outputs fb[3] = dQ, dK, dV
 template <typename T, int D>
-hipError_t run_stages(int stages, int causal, const void* const* in, float* stats, float* gQo, float* gKo,
-                      float* gVo, float* gdOo, int BH, int G, int N, float scale, hipStream_t st) {
+hipError_t run_stages(int stages, int causal, bool first, const void* const* in, float* stats, float* gQo,
+                      float* gKo, float* gVo, float* gdOo, float* const* fb, int BH, int G, int N, float scale,
+                      hipStream_t st) {
   const size_t BHN = (size_t)BH * N;
   // workspace row scalars: LSE * log2(e), D, c, r
   float *lse = stats, *Dv = stats + BHN, *cv = stats + 2 * BHN, *rv = stats + 3 * BHN;
   hipError_t e = hipSuccess;
   if (stages & kPass1) {
-    e = flashbob::launch_query<T, D, false>(in[0], in[1], in[2], in[3], in[4], in[5], in[6], lse, Dv, cv, rv,
-                                            nullptr, nullptr, BH, N, scale, 0, causal, G, st);
+    e = flashbob::launch_query<T, D, false, false>(in[0], in[1], in[2], in[3], in[4], in[5], in[6], lse, Dv, cv,
+                                                   rv, nullptr, nullptr, nullptr, BH, N, scale, 0, causal, G, st);
     if (e != hipSuccess) return e;
   }
   if (stages & kPass2Query) {
-    e = flashbob::launch_query<T, D, true>(in[0], in[1], in[2], in[3], in[4], in[5], in[6], lse, Dv, cv, rv,
-                                           gQo, gdOo, BH, N, scale, 0, causal, G, st);
+    e = first ? flashbob::launch_query<T, D, true, true>(in[0], in[1], in[2], in[3], in[4], in[5], in[6], lse, Dv,
+                                                         cv, rv, gQo, gdOo, fb[0], BH, N, scale, 0, causal, G, st)
+              : flashbob::launch_query<T, D, true, false>(in[0], in[1], in[2], in[3], in[4], in[5], in[6], lse, Dv,
+                                                          cv, rv, gQo, gdOo, nullptr, BH, N, scale, 0, causal, G,
+                                                          st);
     if (e != hipSuccess) return e;
   }
   if (stages & kPass2Key) {
-    e = flashbob::launch_key<T, D>(in[0], in[1], in[2], in[3], in[4], in[5], in[6], lse, Dv, cv, rv, gKo, gVo,
-                                   BH / G, N, scale, causal, G, st);
+    e = first ? flashbob::launch_key<T, D, true>(in[0], in[1], in[2], in[3], in[4], in[5], in[6], lse, Dv, cv, rv,
+                                                 gKo, gVo, fb[1], fb[2], BH / G, N, scale, causal, G, st)
+              : flashbob::launch_key<T, D, false>(in[0], in[1], in[2], in[3], in[4], in[5], in[6], lse, Dv, cv, rv,
+                                                  gKo, gVo, nullptr, nullptr, BH / G, N, scale, causal, G, st);
   }
   return e;
 }
 
-hipError_t dispatch(int dtype, int d, int stages, int causal, const void* const* in, float* stats, float* gQo,
-                    float* gKo, float* gVo, float* gdOo, int BH, int G, int N, float scale, hipStream_t st) {
+hipError_t dispatch(int dtype, int d, int stages, int causal, bool first, const void* const* in, float* stats,
+                    float* gQo, float* gKo, float* gVo, float* gdOo, float* const* fb, int BH, int G, int N,
+                    float scale, hipStream_t st) {
   if (dtype == FLASHBOB_BF16)
-    return d == 64 ? run_stages<__bf16, 64>(stages, causal, in, stats, gQo, gKo, gVo, gdOo, BH, G, N, scale, st)
-                   : run_stages<__bf16, 128>(stages, causal, in, stats, gQo, gKo, gVo, gdOo, BH, G, N, scale, st);
-  return d == 64 ? run_stages<float, 64>(stages, causal, in, stats, gQo, gKo, gVo, gdOo, BH, G, N, scale, st)
-                 : run_stages<float, 128>(stages, causal, in, stats, gQo, gKo, gVo, gdOo, BH, G, N, scale, st);
+    return d == 64 ? run_stages<__bf16, 64>(stages, causal, first, in, stats, gQo, gKo, gVo, gdOo, fb, BH, G, N,
+                                            scale, st)
+                   : run_stages<__bf16, 128>(stages, causal, first, in, stats, gQo, gKo, gVo, gdOo, fb, BH, G, N,
+                                             scale, st);
+  return d == 64 ? run_stages<float, 64>(stages, causal, first, in, stats, gQo, gKo, gVo, gdOo, fb, BH, G, N, scale,
+                                         st)
+                 : run_stages<float, 128>(stages, causal, first, in, stats, gQo, gKo, gVo, gdOo, fb, BH, G, N,
+                                          scale, st);
 }
 
 template <typename T, int D>
 hipError_t rowstats_launch(const void* const* in, float* lse, float* Dv, float* cv, float* rv, int BH, int G,
                            int N, float scale, int causal, hipStream_t st) {
-  return flashbob::launch_query<T, D, false>(in[0], in[1], in[2], in[3], in[4], in[5], in[6], lse, Dv, cv, rv,
-                                             nullptr, nullptr, BH, N, scale, 1, causal, G, st);
+  return flashbob::launch_query<T, D, false, false>(in[0], in[1], in[2], in[3], in[4], in[5], in[6], lse, Dv, cv,
+                                                    rv, nullptr, nullptr, nullptr, BH, N, scale, 1, causal, G, st);
 }
 
 hipError_t dispatch_rowstats(int dtype, int d, int causal, const void* const* in, float* lse, float* Dv, float* cv,
@@ -167,11 +179,13 @@ void tensor_bytes(size_t numel_q, size_t numel_kv, size_t esz, size_t* in_bytes)
 }
 
 int flashbob_bob_ex(const void* Q, const void* K, const void* V, const void* dO, const void* gQ, const void* gK,
-                    const void* gV, float* gradQ, float* gradK, float* gradV, float* graddO, int B, int H,
-                    int H_kv, int N, int d, float scale, int dtype, int flags, int stages, void* workspace,
-                    size_t workspace_bytes, void* stream) {
-  if ((flags & ~FLASHBOB_CAUSAL) != 0 || stages <= 0 || (stages & ~FLASHBOB_STAGES_ALL) != 0)
+                    const void* gV, float* gradQ, float* gradK, float* gradV, float* graddO, float* dQ, float* dK,
+                    float* dV, int B, int H, int H_kv, int N, int d, float scale, int dtype, int flags, int stages,
+                    void* workspace, size_t workspace_bytes, void* stream) {
+  if ((flags & ~(FLASHBOB_CAUSAL | FLASHBOB_FIRST_BACKWARD)) != 0 || stages <= 0 ||
+      (stages & ~FLASHBOB_STAGES_ALL) != 0)
     return FLASHBOB_ERR_FLAGS;
+  const bool first = (flags & FLASHBOB_FIRST_BACKWARD) != 0;
   const void* ins[7] = {Q, K, V, dO, gQ, gK, gV};
   size_t numel = 0;
   int rc = check_common(ins, B, H, N, d, scale, dtype, &numel);
@@ -184,20 +198,23 @@ int flashbob_bob_ex(const void* Q, const void* K, const void* V, const void* dO,
   if (workspace_bytes < ws_need) return FLASHBOB_ERR_WORKSPACE;
   size_t ib[7];
   tensor_bytes(numel, numel_kv, esz, ib);
-  void* outs[5] = {gradQ, gradK, gradV, graddO, workspace};
-  const size_t ob[5] = {numel * 4, numel_kv * 4, numel_kv * 4, numel * 4, ws_need};
-  rc = check_outputs(ins, ib, outs, ob, 5);
+  void* outs[8] = {gradQ, gradK, gradV, graddO, workspace, dQ, dK, dV};
+  const size_t ob[8] = {numel * 4, numel_kv * 4, numel_kv * 4, numel * 4, ws_need,
+                        numel * 4, numel_kv * 4, numel_kv * 4};
+  rc = check_outputs(ins, ib, outs, ob, first ? 8 : 5);  // dQ, dK, dV only with the flag
   if (rc != FLASHBOB_OK) return rc;
-  const hipError_t e = dispatch(dtype, d, stages, (flags & FLASHBOB_CAUSAL) ? 1 : 0, ins,
-                                static_cast<float*>(workspace), gradQ, gradK, gradV, graddO, B * H, H / H_kv, N,
-                                scale, static_cast<hipStream_t>(stream));
+  float* const fb[3] = {dQ, dK, dV};
+  const hipError_t e = dispatch(dtype, d, stages, (flags & FLASHBOB_CAUSAL) ? 1 : 0, first, ins,
+                                static_cast<float*>(workspace), gradQ, gradK, gradV, graddO, fb, B * H, H / H_kv,
+                                N, scale, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? FLASHBOB_OK : hip_fail(e);
 }
 
 int flashbob_bob(const void* Q, const void* K, const void* V, const void* dO, const void* gQ, const void* gK,
                  const void* gV, float* gradQ, float* gradK, float* gradV, float* graddO, int B, int H, int N,
                  int d, float scale, int dtype, void* workspace, size_t workspace_bytes, void* stream) {
-  return flashbob_bob_ex(Q, K, V, dO, gQ, gK, gV, gradQ, gradK, gradV, graddO, B, H, H, N, d, scale, dtype, 0,
+  return flashbob_bob_ex(Q, K, V, dO, gQ, gK, gV, gradQ, gradK, gradV, graddO, nullptr, nullptr, nullptr, B, H, H,
+                         N, d, scale, dtype, 0,
                          FLASHBOB_STAGES_ALL, workspace, workspace_bytes, stream);
 }
 
@@ -205,7 +222,8 @@ int flashbob_bob_pass1(const void* Q, const void* K, const void* V, const void* 
                        const void* gK, const void* gV, float* gradQ, float* gradK, float* gradV, float* graddO,
                        int B, int H, int N, int d, float scale, int dtype, void* workspace,
                        size_t workspace_bytes, void* stream) {
-  return flashbob_bob_ex(Q, K, V, dO, gQ, gK, gV, gradQ, gradK, gradV, graddO, B, H, H, N, d, scale, dtype, 0,
+  return flashbob_bob_ex(Q, K, V, dO, gQ, gK, gV, gradQ, gradK, gradV, graddO, nullptr, nullptr, nullptr, B, H, H,
+                         N, d, scale, dtype, 0,
                          FLASHBOB_STAGE_PASS1, workspace, workspace_bytes, stream);
 }
 
@@ -213,7 +231,8 @@ int flashbob_bob_pass2_query(const void* Q, const void* K, const void* V, const 
                              const void* gK, const void* gV, float* gradQ, float* gradK, float* gradV,
                              float* graddO, int B, int H, int N, int d, float scale, int dtype, void* workspace,
                              size_t workspace_bytes, void* stream) {
-  return flashbob_bob_ex(Q, K, V, dO, gQ, gK, gV, gradQ, gradK, gradV, graddO, B, H, H, N, d, scale, dtype, 0,
+  return flashbob_bob_ex(Q, K, V, dO, gQ, gK, gV, gradQ, gradK, gradV, graddO, nullptr, nullptr, nullptr, B, H, H,
+                         N, d, scale, dtype, 0,
                          FLASHBOB_STAGE_PASS2_QUERY, workspace, workspace_bytes, stream);
 }
 
@@ -221,7 +240,8 @@ int flashbob_bob_pass2_key(const void* Q, const void* K, const void* V, const vo
                            const void* gK, const void* gV, float* gradQ, float* gradK, float* gradV,
                            float* graddO, int B, int H, int N, int d, float scale, int dtype, void* workspace,
                            size_t workspace_bytes, void* stream) {
-  return flashbob_bob_ex(Q, K, V, dO, gQ, gK, gV, gradQ, gradK, gradV, graddO, B, H, H, N, d, scale, dtype, 0,
+  return flashbob_bob_ex(Q, K, V, dO, gQ, gK, gV, gradQ, gradK, gradV, graddO, nullptr, nullptr, nullptr, B, H, H,
+                         N, d, scale, dtype, 0,
                          FLASHBOB_STAGE_PASS2_KEY, workspace, workspace_bytes, stream);
 }
 

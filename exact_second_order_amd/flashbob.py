@@ -16,6 +16,7 @@ LIB_PATH = os.path.join(_PKG, "libflashbob.so")
 FLASHBOB_F32 = 0
 FLASHBOB_BF16 = 1
 FLASHBOB_CAUSAL = 1
+FLASHBOB_FIRST_BACKWARD = 2
 STAGE_BITS = {"pass1": 1, "pass2_query": 2, "pass2_key": 4}
 
 ERRORS = {
@@ -79,7 +80,7 @@ def load_library(path=LIB_PATH):
         fn.restype = i
     lib.flashbob_rowstats.argtypes = [vp] * 7 + [vp] * 4 + [i, i, i, i, f, i, vp]
     lib.flashbob_rowstats.restype = i
-    lib.flashbob_bob_ex.argtypes = [vp] * 7 + [vp] * 4 + [i, i, i, i, i, f, i, i, i, vp, sz, vp]
+    lib.flashbob_bob_ex.argtypes = [vp] * 7 + [vp] * 7 + [i, i, i, i, i, f, i, i, i, vp, sz, vp]
     lib.flashbob_bob_ex.restype = i
     lib.flashbob_rowstats_ex.argtypes = [vp] * 7 + [vp] * 4 + [i, i, i, i, i, f, i, i, vp]
     lib.flashbob_rowstats_ex.restype = i
@@ -137,20 +138,59 @@ def _inputs(Q, K, V, dO, gQ, gK, gV):
     return ins, K.shape[1]
 
 
+def shapes_of(B, H, Hkv, N, d):
+    """Shapes of (gradQ, gradK, gradV, graddO); dQ, dK, dV follow the first three."""
+    return ((B, H, N, d), (B, Hkv, N, d), (B, Hkv, N, d), (B, H, N, d))
+
+
 def workspace_bytes(B, H, N, d):
     return int(load_library().flashbob_workspace_bytes(B, H, N, d))
 
 
-def bob_stage(stage, Q, K, V, dO, gQ, gK, gV, out, workspace, scale=None, stream=None, causal=False):
-    """Run one kernel of bob(): stage in STAGES ("pass1", "pass2_query", "pass2_key")."""
+def _check_out(tensors, shapes, device, what):
+    """Caller-given outputs: float32, contiguous, on the inputs' device, of
+    the expected shapes (the C ABI sees only pointers and trusts the sizes)."""
+    tensors = tuple(tensors)
+    if len(tensors) != len(shapes):
+        raise ValueError(f"{what}: expected {len(shapes)} tensors, got {len(tensors)}")
+    for t, s in zip(tensors, shapes):
+        if not isinstance(t, torch.Tensor) or t.dtype != torch.float32 or t.device != device:
+            raise TypeError(f"{what}: outputs must be float32 tensors on {device}")
+        if tuple(t.shape) != tuple(s) or not t.is_contiguous():
+            raise ValueError(f"{what}: expected contiguous {tuple(s)}, got {tuple(t.shape)}")
+    return tensors
+
+
+def _check_workspace(ws, B, H, N, d, device):
+    if not isinstance(ws, torch.Tensor) or ws.device != device or not ws.is_contiguous():
+        raise TypeError(f"workspace must be a contiguous tensor on {device}")
+    if ws.numel() * ws.element_size() < workspace_bytes(B, H, N, d):
+        raise ValueError(f"workspace needs {workspace_bytes(B, H, N, d)} bytes")
+    return ws
+
+
+def bob_stage(stage, Q, K, V, dO, gQ, gK, gV, out, workspace, scale=None, stream=None, causal=False,
+              first=None):
+    """Run one kernel of bob(): stage in STAGES ("pass1", "pass2_query", "pass2_key").
+
+    first: None, or the (dQ, dK, dV) float32 tensors that the pass-2 stages
+    also fill with the first backward (flag FLASHBOB_FIRST_BACKWARD).
+    """
     lib = load_library()
     ins, Hkv = _inputs(Q, K, V, dO, gQ, gK, gV)
     B, H, N, d = Q.shape
     if scale is None:
         scale = d ** -0.5
-    if causal or Hkv != H:
-        rc = lib.flashbob_bob_ex(*[_ptr(t) for t in ins], *[_ptr(t) for t in out], B, H, Hkv, N, d,
-                                 ctypes.c_float(scale), _dtype_code(Q.dtype), FLASHBOB_CAUSAL if causal else 0,
+    shapes = shapes_of(B, H, Hkv, N, d)
+    out = _check_out(out, shapes, Q.device, "out")
+    _check_workspace(workspace, B, H, N, d, Q.device)
+    if first is not None:
+        first = _check_out(first, shapes[:3], Q.device, "first")
+    if causal or Hkv != H or first is not None:
+        fb = first if first is not None else (None, None, None)
+        flags = (FLASHBOB_CAUSAL if causal else 0) | (FLASHBOB_FIRST_BACKWARD if first is not None else 0)
+        rc = lib.flashbob_bob_ex(*[_ptr(t) for t in ins], *[_ptr(t) for t in out], *[_ptr(t) for t in fb],
+                                 B, H, Hkv, N, d, ctypes.c_float(scale), _dtype_code(Q.dtype), flags,
                                  STAGE_BITS[stage], _ptr(workspace),
                                  ctypes.c_size_t(workspace.numel() * workspace.element_size()),
                                  _stream_handle(Q.device, stream))
@@ -163,7 +203,8 @@ def bob_stage(stage, Q, K, V, dO, gQ, gK, gV, out, workspace, scale=None, stream
     _check(rc)
 
 
-def bob(Q, K, V, dO, gQ, gK, gV, scale=None, out=None, workspace=None, stream=None, causal=False):
+def bob(Q, K, V, dO, gQ, gK, gV, scale=None, out=None, workspace=None, stream=None, causal=False,
+        first_backward=False, first_out=None):
     """Exact BoB of softmax attention: (gradQ, gradK, gradV, graddO), float32.
 
     Inputs [B, H, N, d] bf16 or fp32 device tensors; `scale` defaults to
@@ -172,21 +213,35 @@ def bob(Q, K, V, dO, gQ, gK, gV, scale=None, out=None, workspace=None, stream=No
     causal=True masks key j > query i (flashbob_bob_ex with FLASHBOB_CAUSAL).
     K, V, gK, gV may have fewer heads than Q (grouped-query attention): then
     gradK, gradV have their shape and sum over each group's query heads.
+    first_backward=True also returns the first backward (dQ, dK, dV) of the
+    same attention, float32, computed in the same passes: the result is then
+    (gradQ, gradK, gradV, graddO, dQ, dK, dV). `first_out` may hold the three
+    output tensors.
     """
     lib = load_library()
     ins, Hkv = _inputs(Q, K, V, dO, gQ, gK, gV)
     B, H, N, d = Q.shape
     if scale is None:
         scale = d ** -0.5
+    shapes = shapes_of(B, H, Hkv, N, d)
     if out is None:
-        shapes = ((B, H, N, d), (B, Hkv, N, d), (B, Hkv, N, d), (B, H, N, d))
         out = tuple(torch.empty(s, dtype=torch.float32, device=Q.device) for s in shapes)
+    out = _check_out(out, shapes, Q.device, "out")
     nws = lib.flashbob_workspace_bytes(B, H, N, d)
     if workspace is None:
         workspace = torch.empty(max(nws, 1), dtype=torch.uint8, device=Q.device)
-    if causal or Hkv != H:
-        rc = lib.flashbob_bob_ex(*[_ptr(t) for t in ins], *[_ptr(t) for t in out], B, H, Hkv, N, d,
-                                 ctypes.c_float(scale), _dtype_code(Q.dtype), FLASHBOB_CAUSAL if causal else 0, 7,
+    _check_workspace(workspace, B, H, N, d, Q.device)
+    first = None
+    if first_backward:
+        first = first_out
+        if first is None:
+            first = tuple(torch.empty(s, dtype=torch.float32, device=Q.device) for s in shapes[:3])
+        first = _check_out(first, shapes[:3], Q.device, "first_out")
+    if causal or Hkv != H or first is not None:
+        fb = first if first is not None else (None, None, None)
+        flags = (FLASHBOB_CAUSAL if causal else 0) | (FLASHBOB_FIRST_BACKWARD if first is not None else 0)
+        rc = lib.flashbob_bob_ex(*[_ptr(t) for t in ins], *[_ptr(t) for t in out], *[_ptr(t) for t in fb],
+                                 B, H, Hkv, N, d, ctypes.c_float(scale), _dtype_code(Q.dtype), flags, 7,
                                  _ptr(workspace), ctypes.c_size_t(workspace.numel() * workspace.element_size()),
                                  _stream_handle(Q.device, stream))
     else:
@@ -195,7 +250,7 @@ def bob(Q, K, V, dO, gQ, gK, gV, scale=None, out=None, workspace=None, stream=No
                               ctypes.c_size_t(workspace.numel() * workspace.element_size()),
                               _stream_handle(Q.device, stream))
     _check(rc)
-    return tuple(out)
+    return tuple(out) + (tuple(first) if first is not None else ())
 
 
 def rowstats(Q, K, V, dO, gQ, gK, gV, scale=None, stream=None, causal=False):

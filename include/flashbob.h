@@ -69,7 +69,8 @@ enum {
 
 /* Flags of the *_ex entry points. */
 enum {
-  FLASHBOB_CAUSAL = 1  /* query i attends to keys j <= i */
+  FLASHBOB_CAUSAL = 1,         /* query i attends to keys j <= i */
+  FLASHBOB_FIRST_BACKWARD = 2  /* flashbob_bob_ex only: also write the first backward dQ, dK, dV */
 };
 
 /* Stage sets of flashbob_bob_ex (the three kernels of the schedule). */
@@ -142,9 +143,15 @@ int flashbob_bob_pass2_key(const void* Q, const void* K, const void* V, const vo
  *           gradK, gradV are [B, H_kv, N, d]; query head h uses key/value head
  *           h / (H / H_kv), and gradK, gradV sum over each group's query heads
  *           (the gradients of the shared heads). Otherwise FLASHBOB_ERR_SHAPE.
- *   flags   0 or FLASHBOB_CAUSAL. Causal: per head, each query row i uses
- *           keys 0..i only; key blocks wholly above the diagonal are skipped,
- *           so the work is about half.
+ *   flags   any of FLASHBOB_CAUSAL, FLASHBOB_FIRST_BACKWARD. Causal: per head,
+ *           each query row i uses keys 0..i only; key blocks wholly above the
+ *           diagonal are skipped, so the work is about half. First backward:
+ *           dQ (float32, like gradQ) and dK, dV (float32, like gradK) also
+ *           receive the first backward of the same attention (dQ = s dS K,
+ *           dK = s dS^T Q, dV = P^T dO, summed over groups like gradK); dQ is
+ *           written by the pass-2 query stage, dK and dV by the key stage. The
+ *           extra products run in one-wave-per-SIMD variants of the pass-2
+ *           kernels. Without the flag dQ, dK, dV are ignored (may be NULL).
  *   stages  a non-empty subset of FLASHBOB_STAGES_ALL, run in the order
  *           pass 1, pass 2 query side, pass 2 key side. Pass 2 stages read the
  *           row scalars pass 1 left in `workspace` (computed with the same
@@ -154,6 +161,7 @@ int flashbob_bob_pass2_key(const void* Q, const void* K, const void* V, const vo
 int flashbob_bob_ex(const void* Q, const void* K, const void* V, const void* dO,
                     const void* gQ, const void* gK, const void* gV,
                     float* gradQ, float* gradK, float* gradV, float* graddO,
+                    float* dQ, float* dK, float* dV,
                     int B, int H, int H_kv, int N, int d, float scale, int dtype, int flags, int stages,
                     void* workspace, size_t workspace_bytes, void* stream);
 

@@ -177,17 +177,22 @@ def test_rowstats_validation():
     assert lib.flashbob_rowstats(*ins, *bad, 1, 1, 128, 64, ctypes.c_float(0.1), F32, vp(0)) == ALIGN
 
 
-def call_ex(ins, outs, B, H, N, d, scale, dtype, wsp, nws, flags=0, stages=7, hkv=None):
+# fake dQ, dK, dV (first backward outputs) past the workspace slot
+FIRST = [BASE + (12 + i) * STRIDE for i in range(3)]
+
+
+def call_ex(ins, outs, B, H, N, d, scale, dtype, wsp, nws, flags=0, stages=7, hkv=None, first=(0, 0, 0)):
     lib = fb.load_library()
     vp = ctypes.c_void_p
-    return lib.flashbob_bob_ex(*[vp(p) for p in ins], *[vp(p) for p in outs], B, H, H if hkv is None else hkv, N, d,
-                               ctypes.c_float(scale), dtype, flags, stages, vp(wsp), ctypes.c_size_t(nws), vp(0))
+    return lib.flashbob_bob_ex(*[vp(p) for p in ins], *[vp(p) for p in outs], *[vp(p) for p in first], B, H,
+                               H if hkv is None else hkv, N, d, ctypes.c_float(scale), dtype, flags, stages,
+                               vp(wsp), ctypes.c_size_t(nws), vp(0))
 
 
 def test_ex_rejects_unknown_flags_and_stage_sets():
     FLAGS = -10
-    for flags in (2, 4, -1, 1 << 20):
-        assert call_ex(*fake_args(), flags=flags) == FLAGS
+    for flags in (4, 8, 6, -1, 1 << 20):
+        assert call_ex(*fake_args(), flags=flags, first=FIRST) == FLAGS
     for stages in (0, 8, 9, -1, 16):
         assert call_ex(*fake_args(), stages=stages) == FLAGS
     # the flags check comes first, the shape checks still apply after it
@@ -203,8 +208,35 @@ def test_ex_rejects_unknown_flags_and_stage_sets():
 
 def test_ex_empty_problem_is_a_noop():
     # B*H*N == 0 returns OK before any HIP call, with or without the mask
-    for flags in (0, 1):
+    for flags in (0, 1, 2, 3):
         assert call_ex(*fake_args(B=0), flags=flags) == 0
+
+
+def test_ex_first_backward_output_checks():
+    # with FLASHBOB_FIRST_BACKWARD the dQ, dK, dV pointers are outputs like
+    # the others: NULL, misaligned and aliased ones are rejected; without it
+    # they are ignored, so NULL passes the checks (the call then fails only
+    # for want of a device)
+    import torch
+    FB = fb.FLASHBOB_FIRST_BACKWARD
+    for k in range(3):
+        first = list(FIRST)
+        first[k] = 0
+        assert call_ex(*fake_args(), flags=FB, first=first) == NULL
+        first[k] = FIRST[k] + 4
+        assert call_ex(*fake_args(), flags=FB | 1, first=first) == ALIGN
+        a = fake_args()
+        first[k] = a[0][3] + 16          # inside dO
+        assert call_ex(*a, flags=FB, first=first) == ALIAS
+        first[k] = a[1][k]               # on top of gradQ / gradK / gradV
+        assert call_ex(*a, flags=FB, first=first) == ALIAS
+    a = fake_args()
+    assert call_ex(*a, flags=FB, first=(FIRST[0], FIRST[0], FIRST[2])) == ALIAS
+    assert call_ex(*a, flags=FB, first=(a[8], FIRST[1], FIRST[2])) == ALIAS  # on the workspace
+    if torch.cuda.is_available():
+        return  # the calls below would launch kernels on fake pointers
+    assert call_ex(*fake_args(), flags=FB, first=FIRST) == -100
+    assert call_ex(*fake_args(), flags=0, first=(0, 0, 0)) == -100
 
 
 def test_ex_rejects_bad_kv_head_counts():

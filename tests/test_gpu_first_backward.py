@@ -1,0 +1,205 @@
+"""Parity of the first-backward outputs (dQ, dK, dV) that the HIP path returns
+next to the BoB outputs (flashbob_bob_ex with FLASHBOB_FIRST_BACKWARD), with
+the fp64 oracle's textbook first backward (oracle.attention_backward_batched).
+
+  * small and ragged shapes: every element of all seven outputs, both dtypes
+    and head dims, with and without the causal mask and grouped heads;
+  * the 4096-length workload: full oracle;
+  * the 65536-length workload in the benchmark's launch configuration: oracle
+    dQ rows for a sampled block of 256 queries and the first and last rows
+    per head, and for dK, dV the identities the first backward satisfies at
+    any size (columns of dK sum to zero, those of dV to the sum of dO's rows,
+    and sum_i Q_i . dQ_i = sum_j K_j . dK_j);
+  * the BoB outputs of the same call equal those of the plain call;
+  * stage subsets: each pass-2 stage fills its own first-backward outputs.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from exact_second_order_amd import flashbob as fb
+from helpers import NAMES, TOL, WORKLOADS, make_inputs, rel_fro, say, to_f64, workload_inputs
+
+pytestmark = pytest.mark.gpu
+
+
+def device(ins, dtype=None):
+    return [ins[k].to("cuda") if dtype is None else ins[k].to(dtype).to("cuda") for k in NAMES]
+
+
+def run_first(ins, scale, causal=False, dtype=None):
+    outs = fb.bob(*device(ins, dtype), scale=scale, causal=causal, first_backward=True)
+    torch.cuda.synchronize()
+    assert len(outs) == 7
+    return [o.cpu() for o in outs]
+
+
+def check_against_oracle(ins, outs, scale, causal, tol, label):
+    xs = [ins[k].to(torch.float64).numpy() for k in NAMES]
+    ref_bob = oracle.bob_gqa(*xs, scale, causal=causal)
+    ref_first = oracle.attention_backward_batched(*xs[:4], scale, causal=causal)
+    worst = 0.0
+    for k, ref in enumerate(list(ref_bob) + list(ref_first)):
+        e = rel_fro(to_f64(outs[k]), ref)
+        worst = max(worst, e)
+        assert e <= tol, f"{label} output {k}: rel {e:.3e} > {tol}"
+    return worst
+
+
+@pytest.mark.parametrize("causal", [False, True], ids=["full", "causal"])
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16], ids=["f32", "bf16"])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("H,Hkv", [(2, 2), (4, 1)])
+def test_first_small(H, Hkv, d, dtype, causal):
+    label = f"[first] B=2 H={H} Hkv={Hkv} N=257 d={d} {dtype} causal={causal}"
+    say(label)
+    ins = make_inputs(2, H, 257, d, dtype, seed=300 + H + Hkv + d, H_kv=Hkv)
+    outs = run_first(ins, d ** -0.5, causal)
+    say(f"{label}: worst rel {check_against_oracle(ins, outs, d ** -0.5, causal, TOL[dtype], label):.3e}")
+
+
+@pytest.mark.parametrize("causal", [False, True], ids=["full", "causal"])
+@pytest.mark.parametrize("N", [2, 33, 129, 200, 383, 520])
+def test_first_ragged(N, causal):
+    label = f"[first] ragged N={N} f32 d=64 causal={causal}"
+    say(label)
+    ins = make_inputs(1, 2, N, 64, torch.float32, seed=700 + N)
+    outs = run_first(ins, 0.125, causal)
+    check_against_oracle(ins, outs, 0.125, causal, TOL[torch.float32], label)
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16], ids=["f32", "bf16"])
+def test_first_single_key(dtype):
+    # N = 1: P = 1, so dS = 0 (dQ = dK = 0 and gradK = 0 exactly) and dV = dO;
+    # zero results are met up to fp32 rounding, so the bound is absolute
+    say(f"[first] single key {dtype}")
+    ins = make_inputs(1, 2, 1, 64, dtype, seed=9)
+    outs = run_first(ins, 0.125)
+    xs = [ins[k].to(torch.float64).numpy() for k in NAMES]
+    refs = list(oracle.bob_gqa(*xs, 0.125)) + list(oracle.attention_backward_batched(*xs[:4], 0.125))
+    for k, ref in enumerate(refs):
+        err = np.abs(to_f64(outs[k]) - ref).max()
+        assert err <= 1e-5 * max(1.0, np.abs(ref).max()), f"output {k}: {err:.3e}"
+
+
+@pytest.mark.parametrize("causal", [False, True], ids=["full", "causal"])
+def test_first_workload_4096(causal):
+    w = WORKLOADS[1]
+    label = f"[first] {w.name} causal={causal}"
+    say(label)
+    ins = workload_inputs(w)
+    outs = run_first(ins, w.scale, causal)
+    say(f"{label}: worst rel {check_against_oracle(ins, outs, w.scale, causal, TOL[w.dtype], label):.3e}")
+
+
+def test_first_leaves_bob_outputs_unchanged():
+    # the extra products must not disturb the BoB ones: same values as the
+    # plain call (the BoB products and their order are the same)
+    for dtype, causal, Hkv in ((torch.bfloat16, False, 4), (torch.float32, True, 2), (torch.bfloat16, True, 1)):
+        say(f"[first] unchanged BoB outputs {dtype} causal={causal} Hkv={Hkv}")
+        ins = make_inputs(1, 4, 1000, 64, dtype, seed=41, H_kv=Hkv)
+        dev = device(ins)
+        plain = fb.bob(*dev, causal=causal)
+        both = fb.bob(*dev, causal=causal, first_backward=True)
+        torch.cuda.synchronize()
+        for k in range(4):
+            e = rel_fro(to_f64(both[k]), to_f64(plain[k]))
+            assert e <= 1e-6, f"output {k}: {e:.3e}"
+
+
+def test_first_stage_subsets():
+    # pass 1 then each pass-2 stage alone: pass2_query fills dQ (not dK, dV),
+    # pass2_key fills dK and dV (not dQ)
+    say("[first] stage subsets")
+    ins = make_inputs(1, 2, 300, 64, torch.float32, seed=5)
+    dev = device(ins)
+    B, H, N, d = 1, 2, 300, 64
+    out = [torch.zeros(B, H, N, d, dtype=torch.float32, device="cuda") for _ in range(4)]
+    first = [torch.full((B, H, N, d), 7.0, dtype=torch.float32, device="cuda") for _ in range(3)]
+    ws = torch.empty(fb.workspace_bytes(B, H, N, d), dtype=torch.uint8, device="cuda")
+    fb.bob_stage("pass1", *dev, out, ws, scale=0.125, first=first)
+    fb.bob_stage("pass2_query", *dev, out, ws, scale=0.125, first=first)
+    torch.cuda.synchronize()
+    assert (first[1] == 7.0).all() and (first[2] == 7.0).all()
+    fb.bob_stage("pass2_key", *dev, out, ws, scale=0.125, first=first)
+    torch.cuda.synchronize()
+    xs = [ins[k].to(torch.float64).numpy() for k in NAMES]
+    ref = oracle.attention_backward_batched(*xs[:4], 0.125)
+    for k in range(3):
+        assert rel_fro(to_f64(first[k]), ref[k]) <= 1e-4
+
+
+def test_caller_outputs_are_checked():
+    # outputs the caller brings must be float32, contiguous, on the device
+    # and of the right shape: the C ABI only sees pointers
+    ins = make_inputs(1, 2, 64, 64, torch.float32, seed=6)
+    dev = device(ins)
+    ok = [torch.empty(1, 2, 64, 64, dtype=torch.float32, device="cuda") for _ in range(4)]
+    ws = torch.empty(fb.workspace_bytes(1, 2, 64, 64), dtype=torch.uint8, device="cuda")
+    bad_dtype = [torch.empty(1, 2, 64, 64, dtype=torch.float64, device="cuda")] + ok[1:]
+    with pytest.raises(TypeError):
+        fb.bob(*dev, out=bad_dtype)
+    with pytest.raises(TypeError):
+        fb.bob_stage("pass1", *dev, bad_dtype, ws)
+    with pytest.raises(TypeError):
+        fb.bob(*dev, first_backward=True, first_out=bad_dtype[:3])
+    with pytest.raises(ValueError):
+        fb.bob(*dev, out=[torch.empty(1, 2, 64, 32, dtype=torch.float32, device="cuda")] + ok[1:])
+    with pytest.raises(ValueError):
+        fb.bob(*dev, out=[torch.empty(1, 2, 64, 128, dtype=torch.float32, device="cuda")[..., ::2]] + ok[1:])
+    with pytest.raises(ValueError):
+        fb.bob_stage("pass1", *dev, ok, ws[:16])
+    with pytest.raises(ValueError):
+        fb.bob(*dev, out=ok[:3])
+    torch.cuda.synchronize()
+
+
+@pytest.fixture(scope="module")
+def big_first():
+    w = WORKLOADS[3]
+    say(f"[first] {w.name} device run (bf16, with first backward)")
+    ins = workload_inputs(w)
+    dev = device(ins)
+    both = fb.bob(*dev, scale=w.scale, first_backward=True)
+    plain = fb.bob(*dev, scale=w.scale)
+    torch.cuda.synchronize()
+    return w, ins, [o.cpu() for o in both], [o.cpu() for o in plain]
+
+
+def test_first_big_dq_rows_vs_oracle(big_first):
+    w, ins, both, _ = big_first
+    tol = TOL[w.dtype]
+    g = torch.Generator().manual_seed(11)
+    for h in range(w.H):
+        k = int(torch.randint(0, w.N // 256, (1,), generator=g))
+        rows = np.concatenate([np.arange(4), np.arange(256 * k, 256 * (k + 1)), np.arange(w.N - 4, w.N)])
+        xs = [ins[n][0, h].to(torch.float64).numpy() for n in ("Q", "K", "V", "dO")]
+        ref = oracle.attention_backward_rows_head(*xs, w.scale, rows)
+        e = rel_fro(to_f64(both[4][0, h][rows]), ref)
+        say(f"[first] {w.name} h={h} dQ rows {rows[4]}..: rel {e:.2e}")
+        assert e <= tol
+
+
+def test_first_big_key_side_identities(big_first):
+    w, ins, both, _ = big_first
+    tol = TOL[w.dtype]
+    dQ, dK, dV = (to_f64(t) for t in both[4:])
+    Q, K, dO = (ins[n].to(torch.float64).numpy() for n in ("Q", "K", "dO"))
+    # each query row of dS sums to zero: the columns of dK sum to zero
+    assert np.linalg.norm(dK.sum(axis=2)) <= tol * np.linalg.norm(dK)
+    # each row of P sums to one: the columns of dV sum to those of dO
+    assert rel_fro(dV.sum(axis=2), dO.sum(axis=2)) <= tol
+    # both equal scale * sum_ij dS_ij <Q_i, K_j>, per head
+    # (the sum cancels to about 2% of its absolute row terms on these inputs;
+    # bf16 rounding moves it by ~1e-5 of them, a wrong dK term by far more)
+    rq = np.einsum("bhnd,bhnd->bhn", Q, dQ)
+    lq, lk = rq.sum(axis=2), np.einsum("bhnd,bhnd->bh", K, dK)
+    assert (np.abs(lq - lk) <= 1e-3 * np.abs(rq).sum(axis=2)).all(), (lq, lk)
+
+
+def test_first_big_bob_outputs_unchanged(big_first):
+    _, _, both, plain = big_first
+    for k in range(4):
+        assert rel_fro(to_f64(both[k]), to_f64(plain[k])) <= 1e-6, k

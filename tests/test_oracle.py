@@ -25,7 +25,16 @@ import torch
 import oracle
 from oracle import bob_oracle
 
-torch.set_default_dtype(torch.float64)
+
+
+@pytest.fixture(autouse=True)
+def _float64_default():
+    # the torch references here are built in float64; the default is set per
+    # test and restored, so it does not leak into other test modules
+    prev = torch.get_default_dtype()
+    torch.set_default_dtype(torch.float64)
+    yield
+    torch.set_default_dtype(prev)
 
 SHAPES = [(1, 3), (5, 4), (33, 8), (64, 16)]
 
