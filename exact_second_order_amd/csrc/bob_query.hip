@@ -104,13 +104,15 @@ constexpr int kFlush = 64;  // blocks per level-1 chain
 // Online accumulation of one 32-key block (per lane: 16 keys of one query),
 // in two calls: chunk 0 first takes the block maximum and rescales, then each
 // chunk adds its 8 keys. In the TAIL variant keys at relative index
-// >= nvalid_rel are masked out.
-template <bool TAIL>
+// >= nvalid_rel are masked out. FIXED: the row's saved log-sum-exp serves as
+// the maximum for the whole sweep (p <= 1 throughout), so there is neither a
+// block maximum nor a rescale.
+template <bool TAIL, bool FIXED>
 __device__ __forceinline__ void online_chunk(int cc, const f32x16& S, const f32x16& G, const f32x16& dP,
                                              const f32x16& H, float sl2, int nvalid_rel, OnlineSums& st,
                                              float& mu) {
   const int h = lane_id() >> 5;
-  if (cc == 0) {
+  if (cc == 0 && !FIXED) {
     // block maximum of x = S * scale * log2(e); the caller makes the scale
     // non-negative (sl2 >= 0), so it is the maximum of S times sl2
     float mb = -INFINITY;
@@ -182,13 +184,14 @@ __device__ __forceinline__ void query_chunk(int cc, const f32x16& S, const f32x1
 // FIRST (pass 2q only): also return the first-backward dQ = s dS K (one more
 // product per block against the K^T operand already read; the extra
 // accumulator needs the one-wave-per-SIMD register budget).
-template <typename T, int D, bool GRADQ, bool FIRST>
+template <typename T, int D, bool GRADQ, bool FIRST, bool SAVED>
 __global__ __launch_bounds__(256, (QueryCfg<T, D, GRADQ>::OCC2 && !FIRST ? 2 : 1)) void query_kernel(
     const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V, const T* __restrict__ dO,
     const T* __restrict__ gQ, const T* __restrict__ gK, const T* __restrict__ gV, float* __restrict__ lse,
     float* __restrict__ Dv, float* __restrict__ cv, float* __restrict__ rv, float* __restrict__ gradQ,
-    float* __restrict__ graddO, float* __restrict__ dQo, int N, int nqblk, float scale, int lse_natural,
-    int causal, int G) {
+    float* __restrict__ graddO, float* __restrict__ dQo, const float* __restrict__ lse_in, int N, int nqblk,
+    float scale, int lse_natural, int causal, int G) {
+  static_assert(!(SAVED && GRADQ), "a saved log-sum-exp replaces pass 1's running maximum only");
   using Cfg = QueryCfg<T, D, GRADQ>;
   using E = Elem<T>;
   using F = typename E::frag;
@@ -245,6 +248,13 @@ __global__ __launch_bounds__(256, (QueryCfg<T, D, GRADQ>::OCC2 && !FIRST ? 2 : 1
   scale *= sgn;
   const float sl2 = scale * kLog2e;
   OnlineSums st;  // pass 1 state
+  float mu = 0.f;  // pass 1: the running max used for the current block
+  if constexpr (SAVED) {
+    // the saved natural-log LSE of the row, in the base-2 units of x = s S log2(e)
+    if (qvalid) st.m = lse_in[(size_t)head * N + q] * kLog2e;
+    else st.m = 0.f;
+    mu = st.m;
+  }
   // pass 2q state: the lane's row scalars and the output accumulators
   // (gradQ^T, graddO^T: d rows x the wave's 32 queries)
   // (pass-2 form: LSE * log2(e), -D, -c, -r)
@@ -328,14 +338,13 @@ __global__ __launch_bounds__(256, (QueryCfg<T, D, GRADQ>::OCC2 && !FIRST ? 2 : 1
   struct Frags {
     F P[2], dS[2], dS2[2], A[2];
   };
-  float mu = 0.f;  // pass 1: the running max used for the current block
   // elementwise work of 16-key chunk cc of block n: online sums (pass 1) or
   // operand fragments (pass 2q); TAIL masks keys past the sequence end
   auto elementwise = [&](auto tail, int n, int cc, const Tiles& t, Frags& f) __attribute__((always_inline)) {
     constexpr bool TAIL = decltype(tail)::value;
     const int nrel = qlim - n * BK;
     if constexpr (!GRADQ)
-      online_chunk<TAIL>(cc, t.S, t.G, t.dP, t.H, sl2, nrel, st, mu);
+      online_chunk<TAIL, SAVED>(cc, t.S, t.G, t.dP, t.H, sl2, nrel, st, mu);
     else
       query_chunk<T, TAIL>(cc, t.S, t.G, t.dP, t.H, sl2, scale, l2, Dq, cq, rq, nrel, f.P[cc], f.dS[cc],
                            f.dS2[cc], f.A[cc]);
@@ -474,43 +483,49 @@ __global__ __launch_bounds__(256, (QueryCfg<T, D, GRADQ>::OCC2 && !FIRST ? 2 : 1
   }
 }
 
-template <typename T, int D, bool GRADQ, bool FIRST>
+template <typename T, int D, bool GRADQ, bool FIRST, bool SAVED>
 hipError_t launch_query(const void* Q, const void* K, const void* V, const void* dO, const void* gQ,
                         const void* gK, const void* gV, float* lse, float* Dv, float* cv, float* rv,
-                        float* gradQ, float* graddO, float* dQ, int BH, int N, float scale, int lse_natural,
-                        int causal, int G, hipStream_t stream) {
+                        float* gradQ, float* graddO, float* dQ, const float* lse_in, int BH, int N, float scale,
+                        int lse_natural, int causal, int G, hipStream_t stream) {
   using Cfg = QueryCfg<T, D, GRADQ>;
   const int nqblk = (N + Cfg::BQ - 1) / Cfg::BQ;
   const long long nblocks = (long long)nqblk * BH;
   if (nblocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-  query_kernel<T, D, GRADQ, FIRST><<<dim3((unsigned)nblocks), dim3(256), 0, stream>>>(
+  query_kernel<T, D, GRADQ, FIRST, SAVED><<<dim3((unsigned)nblocks), dim3(256), 0, stream>>>(
       (const T*)Q, (const T*)K, (const T*)V, (const T*)dO, (const T*)gQ, (const T*)gK, (const T*)gV, lse, Dv,
-      cv, rv, gradQ, graddO, dQ, N, nqblk, scale, lse_natural, causal, G);
+      cv, rv, gradQ, graddO, dQ, lse_in, N, nqblk, scale, lse_natural, causal, G);
   return hipGetLastError();
 }
 
-#define FLASHBOB_INST_QUERY(T, D, G, F)                                                                   \
-  template hipError_t launch_query<T, D, G, F>(const void*, const void*, const void*, const void*,      \
-                                               const void*, const void*, const void*, float*, float*,   \
-                                               float*, float*, float*, float*, float*, int, int, float, \
-                                               int, int, int, hipStream_t);
+#define FLASHBOB_INST_QUERY(T, D, G, F, S)                                                                \
+  template hipError_t launch_query<T, D, G, F, S>(const void*, const void*, const void*, const void*,      \
+                                                  const void*, const void*, const void*, float*, float*,   \
+                                                  float*, float*, float*, float*, float*, const float*,    \
+                                                  int, int, float, int, int, int, hipStream_t);
 // Pass 1 and pass 2q instantiations are built as separate objects (pass 1
 // with MFMA results kept in VGPRs, which its register budget allows).
+// Pass 1: plain and with a saved log-sum-exp; pass 2q: plain and with the
+// first-backward dQ.
 #ifndef FLASHBOB_QUERY_PASS2
-FLASHBOB_INST_QUERY(bf16, 64, false, false)
-FLASHBOB_INST_QUERY(bf16, 128, false, false)
-FLASHBOB_INST_QUERY(float, 64, false, false)
-FLASHBOB_INST_QUERY(float, 128, false, false)
+FLASHBOB_INST_QUERY(bf16, 64, false, false, false)
+FLASHBOB_INST_QUERY(bf16, 128, false, false, false)
+FLASHBOB_INST_QUERY(float, 64, false, false, false)
+FLASHBOB_INST_QUERY(float, 128, false, false, false)
+FLASHBOB_INST_QUERY(bf16, 64, false, false, true)
+FLASHBOB_INST_QUERY(bf16, 128, false, false, true)
+FLASHBOB_INST_QUERY(float, 64, false, false, true)
+FLASHBOB_INST_QUERY(float, 128, false, false, true)
 #endif
 #ifndef FLASHBOB_QUERY_PASS1
-FLASHBOB_INST_QUERY(bf16, 64, true, false)
-FLASHBOB_INST_QUERY(bf16, 128, true, false)
-FLASHBOB_INST_QUERY(float, 64, true, false)
-FLASHBOB_INST_QUERY(float, 128, true, false)
-FLASHBOB_INST_QUERY(bf16, 64, true, true)
-FLASHBOB_INST_QUERY(bf16, 128, true, true)
-FLASHBOB_INST_QUERY(float, 64, true, true)
-FLASHBOB_INST_QUERY(float, 128, true, true)
+FLASHBOB_INST_QUERY(bf16, 64, true, false, false)
+FLASHBOB_INST_QUERY(bf16, 128, true, false, false)
+FLASHBOB_INST_QUERY(float, 64, true, false, false)
+FLASHBOB_INST_QUERY(float, 128, true, false, false)
+FLASHBOB_INST_QUERY(bf16, 64, true, true, false)
+FLASHBOB_INST_QUERY(bf16, 128, true, true, false)
+FLASHBOB_INST_QUERY(float, 64, true, true, false)
+FLASHBOB_INST_QUERY(float, 128, true, true, false)
 #endif
 
 }  // namespace flashbob

@@ -14,11 +14,11 @@
 
 namespace flashbob {
 typedef __bf16 bf16;
-template <typename T, int D, bool GRADQ, bool FIRST>
+template <typename T, int D, bool GRADQ, bool FIRST, bool SAVED>
 hipError_t launch_query(const void* Q, const void* K, const void* V, const void* dO, const void* gQ,
                         const void* gK, const void* gV, float* lse, float* Dv, float* cv, float* rv,
-                        float* gradQ, float* graddO, float* dQ, int BH, int N, float scale, int lse_natural,
-                        int causal, int G, hipStream_t stream);
+                        float* gradQ, float* graddO, float* dQ, const float* lse_in, int BH, int N, float scale,
+                        int lse_natural, int causal, int G, hipStream_t stream);
 template <typename T, int D, bool FIRST>
 hipError_t launch_key(const void* Q, const void* K, const void* V, const void* dO, const void* gQ, const void* gK,
                       const void* gV, const float* lse2, const float* Dv, const float* cv, const float* rv,
@@ -62,15 +62,15 @@ int check_common(const void* const* ins, int B, int H, int N, int d, float scale
 }
 
 // ins: the seven inputs with their byte sizes; outs: nout outputs with theirs.
-int check_outputs(const void* const* ins, const size_t* in_bytes, void* const* outs, const size_t* out_bytes,
-                  int nout) {
+int check_outputs(const void* const* ins, const size_t* in_bytes, int nin, void* const* outs,
+                  const size_t* out_bytes, int nout) {
   for (int i = 0; i < nout; ++i) {
     if (outs[i] == nullptr) return FLASHBOB_ERR_NULL;
     if (reinterpret_cast<uintptr_t>(outs[i]) % 16) return FLASHBOB_ERR_ALIGN;
   }
   for (int i = 0; i < nout; ++i) {
     const Range ro{reinterpret_cast<uintptr_t>(outs[i]), reinterpret_cast<uintptr_t>(outs[i]) + out_bytes[i]};
-    for (int j = 0; j < 7; ++j) {
+    for (int j = 0; j < nin; ++j) {
       const Range ri{reinterpret_cast<uintptr_t>(ins[j]), reinterpret_cast<uintptr_t>(ins[j]) + in_bytes[j]};
       if (overlaps(ro, ri)) return FLASHBOB_ERR_ALIAS;
     }
@@ -89,26 +89,32 @@ enum Stage {
   kPass2Key = FLASHBOB_STAGE_PASS2_KEY,
 };
 
-// first: also the first-backward outputs fb[3] = dQ, dK, dV
+// first: also the first-backward outputs fb[3] = dQ, dK, dV; lse_in: the
+// rows' saved log-sum-exp for pass 1, or null
 template <typename T, int D>
-hipError_t run_stages(int stages, int causal, bool first, const void* const* in, float* stats, float* gQo,
-                      float* gKo, float* gVo, float* gdOo, float* const* fb, int BH, int G, int N, float scale,
-                      hipStream_t st) {
+hipError_t run_stages(int stages, int causal, bool first, const void* const* in, const float* lse_in,
+                      float* stats, float* gQo, float* gKo, float* gVo, float* gdOo, float* const* fb, int BH,
+                      int G, int N, float scale, hipStream_t st) {
   const size_t BHN = (size_t)BH * N;
   // workspace row scalars: LSE * log2(e), D, c, r
   float *lse = stats, *Dv = stats + BHN, *cv = stats + 2 * BHN, *rv = stats + 3 * BHN;
   hipError_t e = hipSuccess;
   if (stages & kPass1) {
-    e = flashbob::launch_query<T, D, false, false>(in[0], in[1], in[2], in[3], in[4], in[5], in[6], lse, Dv, cv,
-                                                   rv, nullptr, nullptr, nullptr, BH, N, scale, 0, causal, G, st);
+    e = lse_in ? flashbob::launch_query<T, D, false, false, true>(in[0], in[1], in[2], in[3], in[4], in[5], in[6],
+                                                                  lse, Dv, cv, rv, nullptr, nullptr, nullptr,
+                                                                  lse_in, BH, N, scale, 0, causal, G, st)
+               : flashbob::launch_query<T, D, false, false, false>(in[0], in[1], in[2], in[3], in[4], in[5], in[6],
+                                                                   lse, Dv, cv, rv, nullptr, nullptr, nullptr,
+                                                                   nullptr, BH, N, scale, 0, causal, G, st);
     if (e != hipSuccess) return e;
   }
   if (stages & kPass2Query) {
-    e = first ? flashbob::launch_query<T, D, true, true>(in[0], in[1], in[2], in[3], in[4], in[5], in[6], lse, Dv,
-                                                         cv, rv, gQo, gdOo, fb[0], BH, N, scale, 0, causal, G, st)
-              : flashbob::launch_query<T, D, true, false>(in[0], in[1], in[2], in[3], in[4], in[5], in[6], lse, Dv,
-                                                          cv, rv, gQo, gdOo, nullptr, BH, N, scale, 0, causal, G,
-                                                          st);
+    e = first ? flashbob::launch_query<T, D, true, true, false>(in[0], in[1], in[2], in[3], in[4], in[5], in[6],
+                                                                lse, Dv, cv, rv, gQo, gdOo, fb[0], nullptr, BH, N,
+                                                                scale, 0, causal, G, st)
+              : flashbob::launch_query<T, D, true, false, false>(in[0], in[1], in[2], in[3], in[4], in[5], in[6],
+                                                                 lse, Dv, cv, rv, gQo, gdOo, nullptr, nullptr, BH,
+                                                                 N, scale, 0, causal, G, st);
     if (e != hipSuccess) return e;
   }
   if (stages & kPass2Key) {
@@ -120,25 +126,26 @@ hipError_t run_stages(int stages, int causal, bool first, const void* const* in,
   return e;
 }
 
-hipError_t dispatch(int dtype, int d, int stages, int causal, bool first, const void* const* in, float* stats,
-                    float* gQo, float* gKo, float* gVo, float* gdOo, float* const* fb, int BH, int G, int N,
-                    float scale, hipStream_t st) {
+hipError_t dispatch(int dtype, int d, int stages, int causal, bool first, const void* const* in,
+                    const float* lse_in, float* stats, float* gQo, float* gKo, float* gVo, float* gdOo,
+                    float* const* fb, int BH, int G, int N, float scale, hipStream_t st) {
   if (dtype == FLASHBOB_BF16)
-    return d == 64 ? run_stages<__bf16, 64>(stages, causal, first, in, stats, gQo, gKo, gVo, gdOo, fb, BH, G, N,
-                                            scale, st)
-                   : run_stages<__bf16, 128>(stages, causal, first, in, stats, gQo, gKo, gVo, gdOo, fb, BH, G, N,
-                                             scale, st);
-  return d == 64 ? run_stages<float, 64>(stages, causal, first, in, stats, gQo, gKo, gVo, gdOo, fb, BH, G, N, scale,
-                                         st)
-                 : run_stages<float, 128>(stages, causal, first, in, stats, gQo, gKo, gVo, gdOo, fb, BH, G, N,
-                                          scale, st);
+    return d == 64 ? run_stages<__bf16, 64>(stages, causal, first, in, lse_in, stats, gQo, gKo, gVo, gdOo, fb, BH,
+                                            G, N, scale, st)
+                   : run_stages<__bf16, 128>(stages, causal, first, in, lse_in, stats, gQo, gKo, gVo, gdOo, fb, BH,
+                                             G, N, scale, st);
+  return d == 64 ? run_stages<float, 64>(stages, causal, first, in, lse_in, stats, gQo, gKo, gVo, gdOo, fb, BH, G,
+                                         N, scale, st)
+                 : run_stages<float, 128>(stages, causal, first, in, lse_in, stats, gQo, gKo, gVo, gdOo, fb, BH, G,
+                                          N, scale, st);
 }
 
 template <typename T, int D>
 hipError_t rowstats_launch(const void* const* in, float* lse, float* Dv, float* cv, float* rv, int BH, int G,
                            int N, float scale, int causal, hipStream_t st) {
-  return flashbob::launch_query<T, D, false, false>(in[0], in[1], in[2], in[3], in[4], in[5], in[6], lse, Dv, cv,
-                                                    rv, nullptr, nullptr, nullptr, BH, N, scale, 1, causal, G, st);
+  return flashbob::launch_query<T, D, false, false, false>(in[0], in[1], in[2], in[3], in[4], in[5], in[6], lse,
+                                                           Dv, cv, rv, nullptr, nullptr, nullptr, nullptr, BH, N,
+                                                           scale, 1, causal, G, st);
 }
 
 hipError_t dispatch_rowstats(int dtype, int d, int causal, const void* const* in, float* lse, float* Dv, float* cv,
@@ -180,13 +187,14 @@ void tensor_bytes(size_t numel_q, size_t numel_kv, size_t esz, size_t* in_bytes)
 
 int flashbob_bob_ex(const void* Q, const void* K, const void* V, const void* dO, const void* gQ, const void* gK,
                     const void* gV, float* gradQ, float* gradK, float* gradV, float* graddO, float* dQ, float* dK,
-                    float* dV, int B, int H, int H_kv, int N, int d, float scale, int dtype, int flags, int stages,
-                    void* workspace, size_t workspace_bytes, void* stream) {
-  if ((flags & ~(FLASHBOB_CAUSAL | FLASHBOB_FIRST_BACKWARD)) != 0 || stages <= 0 ||
+                    float* dV, const float* lse_in, int B, int H, int H_kv, int N, int d, float scale, int dtype,
+                    int flags, int stages, void* workspace, size_t workspace_bytes, void* stream) {
+  if ((flags & ~(FLASHBOB_CAUSAL | FLASHBOB_FIRST_BACKWARD | FLASHBOB_SAVED_LSE)) != 0 || stages <= 0 ||
       (stages & ~FLASHBOB_STAGES_ALL) != 0)
     return FLASHBOB_ERR_FLAGS;
   const bool first = (flags & FLASHBOB_FIRST_BACKWARD) != 0;
-  const void* ins[7] = {Q, K, V, dO, gQ, gK, gV};
+  const bool saved = (flags & FLASHBOB_SAVED_LSE) != 0;
+  const void* ins[8] = {Q, K, V, dO, gQ, gK, gV, lse_in};
   size_t numel = 0;
   int rc = check_common(ins, B, H, N, d, scale, dtype, &numel);
   if (rc == FLASHBOB_OK) rc = check_kv_heads(H, H_kv);
@@ -196,25 +204,31 @@ int flashbob_bob_ex(const void* Q, const void* K, const void* V, const void* dO,
   const size_t ws_need = stats_bytes(B, H, N);
   if (workspace == nullptr) return FLASHBOB_ERR_NULL;
   if (workspace_bytes < ws_need) return FLASHBOB_ERR_WORKSPACE;
-  size_t ib[7];
+  if (saved) {  // one float per query row, read as scalars: 4-byte alignment
+    if (lse_in == nullptr) return FLASHBOB_ERR_NULL;
+    if (reinterpret_cast<uintptr_t>(lse_in) % 4) return FLASHBOB_ERR_ALIGN;
+  }
+  size_t ib[8];
   tensor_bytes(numel, numel_kv, esz, ib);
+  ib[7] = numel / (size_t)d * 4;  // lse_in: B*H*N floats
   void* outs[8] = {gradQ, gradK, gradV, graddO, workspace, dQ, dK, dV};
   const size_t ob[8] = {numel * 4, numel_kv * 4, numel_kv * 4, numel * 4, ws_need,
                         numel * 4, numel_kv * 4, numel_kv * 4};
-  rc = check_outputs(ins, ib, outs, ob, first ? 8 : 5);  // dQ, dK, dV only with the flag
+  // dQ, dK, dV are outputs only with their flag, lse_in an input only with its
+  rc = check_outputs(ins, ib, saved ? 8 : 7, outs, ob, first ? 8 : 5);
   if (rc != FLASHBOB_OK) return rc;
   float* const fb[3] = {dQ, dK, dV};
   const hipError_t e = dispatch(dtype, d, stages, (flags & FLASHBOB_CAUSAL) ? 1 : 0, first, ins,
-                                static_cast<float*>(workspace), gradQ, gradK, gradV, graddO, fb, B * H, H / H_kv,
-                                N, scale, static_cast<hipStream_t>(stream));
+                                saved ? lse_in : nullptr, static_cast<float*>(workspace), gradQ, gradK, gradV,
+                                graddO, fb, B * H, H / H_kv, N, scale, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? FLASHBOB_OK : hip_fail(e);
 }
 
 int flashbob_bob(const void* Q, const void* K, const void* V, const void* dO, const void* gQ, const void* gK,
                  const void* gV, float* gradQ, float* gradK, float* gradV, float* graddO, int B, int H, int N,
                  int d, float scale, int dtype, void* workspace, size_t workspace_bytes, void* stream) {
-  return flashbob_bob_ex(Q, K, V, dO, gQ, gK, gV, gradQ, gradK, gradV, graddO, nullptr, nullptr, nullptr, B, H, H,
-                         N, d, scale, dtype, 0,
+  return flashbob_bob_ex(Q, K, V, dO, gQ, gK, gV, gradQ, gradK, gradV, graddO, nullptr, nullptr, nullptr, nullptr,
+                         B, H, H, N, d, scale, dtype, 0,
                          FLASHBOB_STAGES_ALL, workspace, workspace_bytes, stream);
 }
 
@@ -222,8 +236,8 @@ int flashbob_bob_pass1(const void* Q, const void* K, const void* V, const void* 
                        const void* gK, const void* gV, float* gradQ, float* gradK, float* gradV, float* graddO,
                        int B, int H, int N, int d, float scale, int dtype, void* workspace,
                        size_t workspace_bytes, void* stream) {
-  return flashbob_bob_ex(Q, K, V, dO, gQ, gK, gV, gradQ, gradK, gradV, graddO, nullptr, nullptr, nullptr, B, H, H,
-                         N, d, scale, dtype, 0,
+  return flashbob_bob_ex(Q, K, V, dO, gQ, gK, gV, gradQ, gradK, gradV, graddO, nullptr, nullptr, nullptr, nullptr,
+                         B, H, H, N, d, scale, dtype, 0,
                          FLASHBOB_STAGE_PASS1, workspace, workspace_bytes, stream);
 }
 
@@ -231,8 +245,8 @@ int flashbob_bob_pass2_query(const void* Q, const void* K, const void* V, const 
                              const void* gK, const void* gV, float* gradQ, float* gradK, float* gradV,
                              float* graddO, int B, int H, int N, int d, float scale, int dtype, void* workspace,
                              size_t workspace_bytes, void* stream) {
-  return flashbob_bob_ex(Q, K, V, dO, gQ, gK, gV, gradQ, gradK, gradV, graddO, nullptr, nullptr, nullptr, B, H, H,
-                         N, d, scale, dtype, 0,
+  return flashbob_bob_ex(Q, K, V, dO, gQ, gK, gV, gradQ, gradK, gradV, graddO, nullptr, nullptr, nullptr, nullptr,
+                         B, H, H, N, d, scale, dtype, 0,
                          FLASHBOB_STAGE_PASS2_QUERY, workspace, workspace_bytes, stream);
 }
 
@@ -240,8 +254,8 @@ int flashbob_bob_pass2_key(const void* Q, const void* K, const void* V, const vo
                            const void* gK, const void* gV, float* gradQ, float* gradK, float* gradV,
                            float* graddO, int B, int H, int N, int d, float scale, int dtype, void* workspace,
                            size_t workspace_bytes, void* stream) {
-  return flashbob_bob_ex(Q, K, V, dO, gQ, gK, gV, gradQ, gradK, gradV, graddO, nullptr, nullptr, nullptr, B, H, H,
-                         N, d, scale, dtype, 0,
+  return flashbob_bob_ex(Q, K, V, dO, gQ, gK, gV, gradQ, gradK, gradV, graddO, nullptr, nullptr, nullptr, nullptr,
+                         B, H, H, N, d, scale, dtype, 0,
                          FLASHBOB_STAGE_PASS2_KEY, workspace, workspace_bytes, stream);
 }
 
@@ -260,7 +274,7 @@ int flashbob_rowstats_ex(const void* Q, const void* K, const void* V, const void
   const size_t vb = (size_t)B * H * N * sizeof(float);
   void* outs[4] = {lse, Dv, cv, rv};
   const size_t ob[4] = {vb, vb, vb, vb};
-  rc = check_outputs(ins, ib, outs, ob, 4);
+  rc = check_outputs(ins, ib, 7, outs, ob, 4);
   if (rc != FLASHBOB_OK) return rc;
   // pass 1 writing the plain row scalars into the caller's four vectors
   const hipError_t e = dispatch_rowstats(dtype, d, (flags & FLASHBOB_CAUSAL) ? 1 : 0, ins, lse, Dv, cv, rv, B * H,

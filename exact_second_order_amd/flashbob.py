@@ -17,6 +17,7 @@ FLASHBOB_F32 = 0
 FLASHBOB_BF16 = 1
 FLASHBOB_CAUSAL = 1
 FLASHBOB_FIRST_BACKWARD = 2
+FLASHBOB_SAVED_LSE = 4
 STAGE_BITS = {"pass1": 1, "pass2_query": 2, "pass2_key": 4}
 
 ERRORS = {
@@ -80,7 +81,7 @@ def load_library(path=LIB_PATH):
         fn.restype = i
     lib.flashbob_rowstats.argtypes = [vp] * 7 + [vp] * 4 + [i, i, i, i, f, i, vp]
     lib.flashbob_rowstats.restype = i
-    lib.flashbob_bob_ex.argtypes = [vp] * 7 + [vp] * 7 + [i, i, i, i, i, f, i, i, i, vp, sz, vp]
+    lib.flashbob_bob_ex.argtypes = [vp] * 7 + [vp] * 8 + [i, i, i, i, i, f, i, i, i, vp, sz, vp]
     lib.flashbob_bob_ex.restype = i
     lib.flashbob_rowstats_ex.argtypes = [vp] * 7 + [vp] * 4 + [i, i, i, i, i, f, i, i, vp]
     lib.flashbob_rowstats_ex.restype = i
@@ -161,6 +162,25 @@ def _check_out(tensors, shapes, device, what):
     return tensors
 
 
+def _check_lse(lse, B, H, N, device):
+    """A saved log-sum-exp: float32 [B, H, N] on the inputs' device."""
+    if not isinstance(lse, torch.Tensor) or lse.dtype != torch.float32 or lse.device != device:
+        raise TypeError(f"lse must be a float32 tensor on {device}")
+    if tuple(lse.shape) != (B, H, N) or not lse.is_contiguous():
+        raise ValueError(f"lse must be contiguous ({B}, {H}, {N}), got {tuple(lse.shape)}")
+    return lse
+
+
+def _call_ex(lib, ins, out, first, lse, B, H, Hkv, N, d, scale, dtype, causal, stages, workspace, stream):
+    flags = ((FLASHBOB_CAUSAL if causal else 0) | (FLASHBOB_FIRST_BACKWARD if first is not None else 0)
+             | (FLASHBOB_SAVED_LSE if lse is not None else 0))
+    fb = first if first is not None else (None, None, None)
+    return lib.flashbob_bob_ex(*[_ptr(t) for t in ins], *[_ptr(t) for t in out], *[_ptr(t) for t in fb],
+                               _ptr(lse), B, H, Hkv, N, d, ctypes.c_float(scale), _dtype_code(dtype), flags,
+                               stages, _ptr(workspace), ctypes.c_size_t(workspace.numel() * workspace.element_size()),
+                               stream)
+
+
 def _check_workspace(ws, B, H, N, d, device):
     if not isinstance(ws, torch.Tensor) or ws.device != device or not ws.is_contiguous():
         raise TypeError(f"workspace must be a contiguous tensor on {device}")
@@ -170,11 +190,13 @@ def _check_workspace(ws, B, H, N, d, device):
 
 
 def bob_stage(stage, Q, K, V, dO, gQ, gK, gV, out, workspace, scale=None, stream=None, causal=False,
-              first=None):
+              first=None, lse=None):
     """Run one kernel of bob(): stage in STAGES ("pass1", "pass2_query", "pass2_key").
 
     first: None, or the (dQ, dK, dV) float32 tensors that the pass-2 stages
     also fill with the first backward (flag FLASHBOB_FIRST_BACKWARD).
+    lse: None, or the rows' saved log-sum-exp [B, H, N] that pass 1 starts
+    from (flag FLASHBOB_SAVED_LSE).
     """
     lib = load_library()
     ins, Hkv = _inputs(Q, K, V, dO, gQ, gK, gV)
@@ -186,14 +208,11 @@ def bob_stage(stage, Q, K, V, dO, gQ, gK, gV, out, workspace, scale=None, stream
     _check_workspace(workspace, B, H, N, d, Q.device)
     if first is not None:
         first = _check_out(first, shapes[:3], Q.device, "first")
-    if causal or Hkv != H or first is not None:
-        fb = first if first is not None else (None, None, None)
-        flags = (FLASHBOB_CAUSAL if causal else 0) | (FLASHBOB_FIRST_BACKWARD if first is not None else 0)
-        rc = lib.flashbob_bob_ex(*[_ptr(t) for t in ins], *[_ptr(t) for t in out], *[_ptr(t) for t in fb],
-                                 B, H, Hkv, N, d, ctypes.c_float(scale), _dtype_code(Q.dtype), flags,
-                                 STAGE_BITS[stage], _ptr(workspace),
-                                 ctypes.c_size_t(workspace.numel() * workspace.element_size()),
-                                 _stream_handle(Q.device, stream))
+    if lse is not None:
+        _check_lse(lse, B, H, N, Q.device)
+    if causal or Hkv != H or first is not None or lse is not None:
+        rc = _call_ex(lib, ins, out, first, lse, B, H, Hkv, N, d, scale, Q.dtype, causal, STAGE_BITS[stage],
+                      workspace, _stream_handle(Q.device, stream))
     else:
         fn = getattr(lib, STAGES[stage])
         rc = fn(*[_ptr(t) for t in ins], *[_ptr(t) for t in out], B, H, N, d, ctypes.c_float(scale),
@@ -204,7 +223,7 @@ def bob_stage(stage, Q, K, V, dO, gQ, gK, gV, out, workspace, scale=None, stream
 
 
 def bob(Q, K, V, dO, gQ, gK, gV, scale=None, out=None, workspace=None, stream=None, causal=False,
-        first_backward=False, first_out=None):
+        first_backward=False, first_out=None, lse=None):
     """Exact BoB of softmax attention: (gradQ, gradK, gradV, graddO), float32.
 
     Inputs [B, H, N, d] bf16 or fp32 device tensors; `scale` defaults to
@@ -217,6 +236,10 @@ def bob(Q, K, V, dO, gQ, gK, gV, scale=None, out=None, workspace=None, stream=No
     same attention, float32, computed in the same passes: the result is then
     (gradQ, gradK, gradV, graddO, dQ, dK, dV). `first_out` may hold the three
     output tensors.
+    lse ([B, H, N] float32) is a saved log-sum-exp of the rows (as a forward
+    pass keeps it): pass 1 then starts from it instead of tracking a running
+    maximum (flag FLASHBOB_SAVED_LSE; the outputs do not depend on it beyond
+    rounding).
     """
     lib = load_library()
     ins, Hkv = _inputs(Q, K, V, dO, gQ, gK, gV)
@@ -237,13 +260,11 @@ def bob(Q, K, V, dO, gQ, gK, gV, scale=None, out=None, workspace=None, stream=No
         if first is None:
             first = tuple(torch.empty(s, dtype=torch.float32, device=Q.device) for s in shapes[:3])
         first = _check_out(first, shapes[:3], Q.device, "first_out")
-    if causal or Hkv != H or first is not None:
-        fb = first if first is not None else (None, None, None)
-        flags = (FLASHBOB_CAUSAL if causal else 0) | (FLASHBOB_FIRST_BACKWARD if first is not None else 0)
-        rc = lib.flashbob_bob_ex(*[_ptr(t) for t in ins], *[_ptr(t) for t in out], *[_ptr(t) for t in fb],
-                                 B, H, Hkv, N, d, ctypes.c_float(scale), _dtype_code(Q.dtype), flags, 7,
-                                 _ptr(workspace), ctypes.c_size_t(workspace.numel() * workspace.element_size()),
-                                 _stream_handle(Q.device, stream))
+    if lse is not None:
+        _check_lse(lse, B, H, N, Q.device)
+    if causal or Hkv != H or first is not None or lse is not None:
+        rc = _call_ex(lib, ins, out, first, lse, B, H, Hkv, N, d, scale, Q.dtype, causal, 7, workspace,
+                      _stream_handle(Q.device, stream))
     else:
         rc = lib.flashbob_bob(*[_ptr(t) for t in ins], *[_ptr(t) for t in out], B, H, N, d,
                               ctypes.c_float(scale), _dtype_code(Q.dtype), _ptr(workspace),

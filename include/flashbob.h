@@ -69,8 +69,9 @@ enum {
 
 /* Flags of the *_ex entry points. */
 enum {
-  FLASHBOB_CAUSAL = 1,         /* query i attends to keys j <= i */
-  FLASHBOB_FIRST_BACKWARD = 2  /* flashbob_bob_ex only: also write the first backward dQ, dK, dV */
+  FLASHBOB_CAUSAL = 1,          /* query i attends to keys j <= i */
+  FLASHBOB_FIRST_BACKWARD = 2,  /* flashbob_bob_ex only: also write the first backward dQ, dK, dV */
+  FLASHBOB_SAVED_LSE = 4        /* flashbob_bob_ex only: pass 1 starts from a saved log-sum-exp */
 };
 
 /* Stage sets of flashbob_bob_ex (the three kernels of the schedule). */
@@ -152,6 +153,16 @@ int flashbob_bob_pass2_key(const void* Q, const void* K, const void* V, const vo
  *           written by the pass-2 query stage, dK and dV by the key stage. The
  *           extra products run in one-wave-per-SIMD variants of the pass-2
  *           kernels. Without the flag dQ, dK, dV are ignored (may be NULL).
+ *           Saved LSE: lse_in ([B, H, N] float32, 4-byte aligned, an input
+ *           that must not overlap any output) holds each query row's
+ *           natural-log log-sum-exp of s Q K^T (masked like the call), as a
+ *           forward pass saves it. Pass 1 then uses it as the row maximum for
+ *           the whole sweep instead of tracking a running one, and still
+ *           normalises by the sum it accumulates, so the result does not
+ *           depend on lse_in being exact: values within 20 of the true ones
+ *           give the same outputs up to rounding (far enough below them the
+ *           exponentials overflow, far enough above they underflow). Without
+ *           the flag lse_in is ignored (may be NULL).
  *   stages  a non-empty subset of FLASHBOB_STAGES_ALL, run in the order
  *           pass 1, pass 2 query side, pass 2 key side. Pass 2 stages read the
  *           row scalars pass 1 left in `workspace` (computed with the same
@@ -161,7 +172,7 @@ int flashbob_bob_pass2_key(const void* Q, const void* K, const void* V, const vo
 int flashbob_bob_ex(const void* Q, const void* K, const void* V, const void* dO,
                     const void* gQ, const void* gK, const void* gV,
                     float* gradQ, float* gradK, float* gradV, float* graddO,
-                    float* dQ, float* dK, float* dV,
+                    float* dQ, float* dK, float* dV, const float* lse_in,
                     int B, int H, int H_kv, int N, int d, float scale, int dtype, int flags, int stages,
                     void* workspace, size_t workspace_bytes, void* stream);
 

@@ -181,18 +181,22 @@ def test_rowstats_validation():
 FIRST = [BASE + (12 + i) * STRIDE for i in range(3)]
 
 
-def call_ex(ins, outs, B, H, N, d, scale, dtype, wsp, nws, flags=0, stages=7, hkv=None, first=(0, 0, 0)):
+# a fake saved log-sum-exp input after those
+LSE = BASE + 15 * STRIDE
+
+
+def call_ex(ins, outs, B, H, N, d, scale, dtype, wsp, nws, flags=0, stages=7, hkv=None, first=(0, 0, 0), lse=0):
     lib = fb.load_library()
     vp = ctypes.c_void_p
-    return lib.flashbob_bob_ex(*[vp(p) for p in ins], *[vp(p) for p in outs], *[vp(p) for p in first], B, H,
-                               H if hkv is None else hkv, N, d, ctypes.c_float(scale), dtype, flags, stages,
+    return lib.flashbob_bob_ex(*[vp(p) for p in ins], *[vp(p) for p in outs], *[vp(p) for p in first], vp(lse),
+                               B, H, H if hkv is None else hkv, N, d, ctypes.c_float(scale), dtype, flags, stages,
                                vp(wsp), ctypes.c_size_t(nws), vp(0))
 
 
 def test_ex_rejects_unknown_flags_and_stage_sets():
     FLAGS = -10
-    for flags in (4, 8, 6, -1, 1 << 20):
-        assert call_ex(*fake_args(), flags=flags, first=FIRST) == FLAGS
+    for flags in (8, 9, 16, -1, 1 << 20):
+        assert call_ex(*fake_args(), flags=flags, first=FIRST, lse=LSE) == FLAGS
     for stages in (0, 8, 9, -1, 16):
         assert call_ex(*fake_args(), stages=stages) == FLAGS
     # the flags check comes first, the shape checks still apply after it
@@ -208,7 +212,7 @@ def test_ex_rejects_unknown_flags_and_stage_sets():
 
 def test_ex_empty_problem_is_a_noop():
     # B*H*N == 0 returns OK before any HIP call, with or without the mask
-    for flags in (0, 1, 2, 3):
+    for flags in range(8):
         assert call_ex(*fake_args(B=0), flags=flags) == 0
 
 
@@ -267,3 +271,22 @@ def test_ex_alias_check_uses_kv_sizes():
     assert call_ex(ins, outs, B, H, N, d, 0.1, F32, BASE + 11 * STRIDE, nws, hkv=1) == -100
     outs[1] = ins[1] + kv_bytes - 16       # one chunk of overlap
     assert call_ex(ins, outs, B, H, N, d, 0.1, F32, BASE + 11 * STRIDE, nws, hkv=1) == -8
+
+
+def test_ex_saved_lse_checks():
+    # FLASHBOB_SAVED_LSE makes lse_in an input: NULL, misaligned (it is read
+    # as 4-byte scalars) and overlapping an output are rejected; without the
+    # flag it is ignored
+    import torch
+    SV = fb.FLASHBOB_SAVED_LSE
+    a = fake_args()
+    assert call_ex(*a, flags=SV, lse=0) == NULL
+    assert call_ex(*a, flags=SV | 1, lse=LSE + 2) == ALIGN
+    assert call_ex(*a, flags=SV, lse=a[1][0] + 64) == ALIAS      # inside gradQ
+    assert call_ex(*a, flags=SV, lse=a[8]) == ALIAS              # on the workspace
+    assert call_ex(*a, flags=SV | 2, lse=FIRST[1] + 4, first=FIRST) == ALIAS  # inside dK
+    if torch.cuda.is_available():
+        return  # the calls below would launch kernels on fake pointers
+    assert call_ex(*a, flags=SV, lse=LSE + 4) == -100   # 4-byte aligned is enough
+    assert call_ex(*a, flags=SV, lse=a[0][0]) == -100   # reading an input's memory is no hazard
+    assert call_ex(*a, flags=0, lse=LSE + 1) == -100    # ignored without the flag
