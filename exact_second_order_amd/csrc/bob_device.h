@@ -273,23 +273,6 @@ __device__ __forceinline__ void st4(float* p, float a, float b, float c, float d
 // ---------------------------------------------------------------------------
 // global -> LDS row copies (16 bytes per lane per step), zero rows past `nrows`
 
-template <typename T, int ROWS, int COLS, int NTHREADS>
-__device__ __forceinline__ void copy_rows_to_lds(T* dst, int ldd, const T* src, int nrows_valid) {
-  constexpr int VEC = 16 / sizeof(T);
-  constexpr int VPR = COLS / VEC;  // vectors per row
-  constexpr int TOTAL = ROWS * VPR;
-  static_assert(TOTAL % NTHREADS == 0, "copy must split evenly over the workgroup");
-  typedef __attribute__((__vector_size__(16))) int v4i;
-#pragma unroll
-  for (int it = 0; it < TOTAL / NTHREADS; ++it) {
-    const int idx = it * NTHREADS + (int)threadIdx.x;
-    const int r = idx / VPR, cv = idx % VPR;
-    v4i v = {0, 0, 0, 0};
-    if (r < nrows_valid) v = *reinterpret_cast<const v4i*>(src + (size_t)r * COLS + cv * VEC);
-    *reinterpret_cast<v4i*>(dst + r * ldd + cv * VEC) = v;
-  }
-}
-
 // Register-staged copy of a [ROWS][COLS] row block (16 bytes per lane per
 // step): load() issues the global reads early, store() writes LDS later, so
 // the global latency hides behind the work done in between.
@@ -297,8 +280,11 @@ template <typename T, int ROWS, int COLS, int NTHREADS>
 struct RowPrefetch {
   static constexpr int VEC = 16 / sizeof(T);
   static constexpr int VPR = COLS / VEC;
-  static constexpr int NIT = ROWS * VPR / NTHREADS;  // ROWS = 0: unused placeholder
-  static_assert((ROWS * VPR) % NTHREADS == 0, "copy must split evenly over the workgroup");
+  static_assert(COLS % VEC == 0, "rows are whole 16-byte vectors");
+  static constexpr int TOTAL = ROWS * VPR;                     // vectors to copy
+  static constexpr int NIT = (TOTAL + NTHREADS - 1) / NTHREADS;  // ROWS = 0: unused placeholder
+  // whether the last step has idle threads (d = 32, 96 in bf16)
+  static constexpr bool RAGGED = TOTAL % NTHREADS != 0;
   typedef __attribute__((__vector_size__(16))) int v4i;
   v4i r[NIT > 0 ? NIT : 1];
 
@@ -308,7 +294,8 @@ struct RowPrefetch {
       const int idx = it * NTHREADS + (int)threadIdx.x;
       const int row = idx / VPR, cv = idx % VPR;
       r[it] = v4i{0, 0, 0, 0};
-      if (row < nrows_valid) r[it] = *reinterpret_cast<const v4i*>(src + (size_t)row * COLS + cv * VEC);
+      if ((!RAGGED || idx < TOTAL) && row < nrows_valid)
+        r[it] = *reinterpret_cast<const v4i*>(src + (size_t)row * COLS + cv * VEC);
     }
   }
   __device__ __forceinline__ void store(T* dst, int ldd) const {
@@ -316,7 +303,7 @@ struct RowPrefetch {
     for (int it = 0; it < NIT; ++it) {
       const int idx = it * NTHREADS + (int)threadIdx.x;
       const int row = idx / VPR, cv = idx % VPR;
-      *reinterpret_cast<v4i*>(dst + row * ldd + cv * VEC) = r[it];
+      if (!RAGGED || idx < TOTAL) *reinterpret_cast<v4i*>(dst + row * ldd + cv * VEC) = r[it];
     }
   }
 };

@@ -411,13 +411,16 @@ hipError_t launch_key(const void* Q, const void* K, const void* V, const void* d
                                           const void*, const void*, const float*, const float*,             \
                                           const float*, const float*, float*, float*, float*, float*, int,  \
                                           int, float, int, int, hipStream_t);
-FLASHBOB_INST_KEY(bf16, 64, false)
-FLASHBOB_INST_KEY(bf16, 128, false)
-FLASHBOB_INST_KEY(float, 64, false)
-FLASHBOB_INST_KEY(float, 128, false)
-FLASHBOB_INST_KEY(bf16, 64, true)
-FLASHBOB_INST_KEY(bf16, 128, true)
-FLASHBOB_INST_KEY(float, 64, true)
-FLASHBOB_INST_KEY(float, 128, true)
+#define FLASHBOB_INST_KEY_DIMS(F) \
+  FLASHBOB_INST_KEY(bf16, 32, F)  \
+  FLASHBOB_INST_KEY(bf16, 64, F)  \
+  FLASHBOB_INST_KEY(bf16, 96, F)  \
+  FLASHBOB_INST_KEY(bf16, 128, F) \
+  FLASHBOB_INST_KEY(float, 32, F) \
+  FLASHBOB_INST_KEY(float, 64, F) \
+  FLASHBOB_INST_KEY(float, 96, F) \
+  FLASHBOB_INST_KEY(float, 128, F)
+FLASHBOB_INST_KEY_DIMS(false)
+FLASHBOB_INST_KEY_DIMS(true)
 
 }  // namespace flashbob

@@ -507,25 +507,22 @@ hipError_t launch_query(const void* Q, const void* K, const void* V, const void*
 // with MFMA results kept in VGPRs, which its register budget allows).
 // Pass 1: plain and with a saved log-sum-exp; pass 2q: plain and with the
 // first-backward dQ.
+#define FLASHBOB_INST_QUERY_DIMS(G, F, S)  \
+  FLASHBOB_INST_QUERY(bf16, 32, G, F, S)   \
+  FLASHBOB_INST_QUERY(bf16, 64, G, F, S)   \
+  FLASHBOB_INST_QUERY(bf16, 96, G, F, S)   \
+  FLASHBOB_INST_QUERY(bf16, 128, G, F, S)  \
+  FLASHBOB_INST_QUERY(float, 32, G, F, S)  \
+  FLASHBOB_INST_QUERY(float, 64, G, F, S)  \
+  FLASHBOB_INST_QUERY(float, 96, G, F, S)  \
+  FLASHBOB_INST_QUERY(float, 128, G, F, S)
 #ifndef FLASHBOB_QUERY_PASS2
-FLASHBOB_INST_QUERY(bf16, 64, false, false, false)
-FLASHBOB_INST_QUERY(bf16, 128, false, false, false)
-FLASHBOB_INST_QUERY(float, 64, false, false, false)
-FLASHBOB_INST_QUERY(float, 128, false, false, false)
-FLASHBOB_INST_QUERY(bf16, 64, false, false, true)
-FLASHBOB_INST_QUERY(bf16, 128, false, false, true)
-FLASHBOB_INST_QUERY(float, 64, false, false, true)
-FLASHBOB_INST_QUERY(float, 128, false, false, true)
+FLASHBOB_INST_QUERY_DIMS(false, false, false)
+FLASHBOB_INST_QUERY_DIMS(false, false, true)
 #endif
 #ifndef FLASHBOB_QUERY_PASS1
-FLASHBOB_INST_QUERY(bf16, 64, true, false, false)
-FLASHBOB_INST_QUERY(bf16, 128, true, false, false)
-FLASHBOB_INST_QUERY(float, 64, true, false, false)
-FLASHBOB_INST_QUERY(float, 128, true, false, false)
-FLASHBOB_INST_QUERY(bf16, 64, true, true, false)
-FLASHBOB_INST_QUERY(bf16, 128, true, true, false)
-FLASHBOB_INST_QUERY(float, 64, true, true, false)
-FLASHBOB_INST_QUERY(float, 128, true, true, false)
+FLASHBOB_INST_QUERY_DIMS(true, false, false)
+FLASHBOB_INST_QUERY_DIMS(true, true, false)
 #endif
 
 }  // namespace flashbob

@@ -9,6 +9,7 @@
 #include <cstdint>
 #include <cstring>
 #include <string>
+#include <type_traits>
 
 #include "flashbob.h"
 
@@ -44,7 +45,7 @@ bool overlaps(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi; }
 // Shared validation. On success fills the element count of one tensor.
 int check_common(const void* const* ins, int B, int H, int N, int d, float scale, int dtype, size_t* numel) {
   if (B < 0 || H < 0 || N < 0) return FLASHBOB_ERR_SHAPE;
-  if (d != 64 && d != 128) return FLASHBOB_ERR_UNSUPPORTED_D;
+  if (d != 32 && d != 64 && d != 96 && d != 128) return FLASHBOB_ERR_UNSUPPORTED_D;
   if (dtype != FLASHBOB_F32 && dtype != FLASHBOB_BF16) return FLASHBOB_ERR_DTYPE;
   if (!std::isfinite(scale)) return FLASHBOB_ERR_SCALE;
   // B*H*N*d < 2^62 (fits every index computed in size_t) and B*H*N < 2^31
@@ -126,18 +127,35 @@ hipError_t run_stages(int stages, int causal, bool first, const void* const* in,
   return e;
 }
 
+template <typename T>
+struct TypeTag {
+  using type = T;
+};
+template <int D>
+using DimTag = std::integral_constant<int, D>;
+
+// Calls f(TypeTag<T>{}, DimTag<D>{}) for the element type and head dim of a
+// call (both validated before: d is one of the supported head dims).
+template <typename Fn>
+hipError_t on_type_and_dim(int dtype, int d, Fn&& f) {
+  auto dims = [&](auto t) -> hipError_t {
+    switch (d) {
+      case 32: return f(t, DimTag<32>{});
+      case 64: return f(t, DimTag<64>{});
+      case 96: return f(t, DimTag<96>{});
+      default: return f(t, DimTag<128>{});
+    }
+  };
+  return dtype == FLASHBOB_BF16 ? dims(TypeTag<__bf16>{}) : dims(TypeTag<float>{});
+}
+
 hipError_t dispatch(int dtype, int d, int stages, int causal, bool first, const void* const* in,
                     const float* lse_in, float* stats, float* gQo, float* gKo, float* gVo, float* gdOo,
                     float* const* fb, int BH, int G, int N, float scale, hipStream_t st) {
-  if (dtype == FLASHBOB_BF16)
-    return d == 64 ? run_stages<__bf16, 64>(stages, causal, first, in, lse_in, stats, gQo, gKo, gVo, gdOo, fb, BH,
-                                            G, N, scale, st)
-                   : run_stages<__bf16, 128>(stages, causal, first, in, lse_in, stats, gQo, gKo, gVo, gdOo, fb, BH,
-                                             G, N, scale, st);
-  return d == 64 ? run_stages<float, 64>(stages, causal, first, in, lse_in, stats, gQo, gKo, gVo, gdOo, fb, BH, G,
-                                         N, scale, st)
-                 : run_stages<float, 128>(stages, causal, first, in, lse_in, stats, gQo, gKo, gVo, gdOo, fb, BH, G,
-                                          N, scale, st);
+  return on_type_and_dim(dtype, d, [&](auto t, auto dd) {
+    return run_stages<typename decltype(t)::type, decltype(dd)::value>(stages, causal, first, in, lse_in, stats,
+                                                                       gQo, gKo, gVo, gdOo, fb, BH, G, N, scale, st);
+  });
 }
 
 template <typename T, int D>
@@ -150,11 +168,10 @@ hipError_t rowstats_launch(const void* const* in, float* lse, float* Dv, float* 
 
 hipError_t dispatch_rowstats(int dtype, int d, int causal, const void* const* in, float* lse, float* Dv, float* cv,
                              float* rv, int BH, int G, int N, float scale, hipStream_t st) {
-  if (dtype == FLASHBOB_BF16)
-    return d == 64 ? rowstats_launch<__bf16, 64>(in, lse, Dv, cv, rv, BH, G, N, scale, causal, st)
-                   : rowstats_launch<__bf16, 128>(in, lse, Dv, cv, rv, BH, G, N, scale, causal, st);
-  return d == 64 ? rowstats_launch<float, 64>(in, lse, Dv, cv, rv, BH, G, N, scale, causal, st)
-                 : rowstats_launch<float, 128>(in, lse, Dv, cv, rv, BH, G, N, scale, causal, st);
+  return on_type_and_dim(dtype, d, [&](auto t, auto dd) {
+    return rowstats_launch<typename decltype(t)::type, decltype(dd)::value>(in, lse, Dv, cv, rv, BH, G, N, scale,
+                                                                            causal, st);
+  });
 }
 
 size_t stats_bytes(int B, int H, int N) {
@@ -293,7 +310,7 @@ const char* flashbob_strerror(int code) {
     case FLASHBOB_OK: return "ok";
     case FLASHBOB_ERR_NULL: return "a required pointer is NULL";
     case FLASHBOB_ERR_SHAPE: return "invalid shape (negative size or too many elements)";
-    case FLASHBOB_ERR_UNSUPPORTED_D: return "unsupported head dimension (d must be 64 or 128)";
+    case FLASHBOB_ERR_UNSUPPORTED_D: return "unsupported head dimension (d must be 32, 64, 96 or 128)";
     case FLASHBOB_ERR_UNSUPPORTED_N: return "unsupported sequence length";
     case FLASHBOB_ERR_DTYPE: return "unknown dtype";
     case FLASHBOB_ERR_ALIGN: return "a pointer is not 16-byte aligned";

@@ -69,7 +69,7 @@ def call(ins, outs, B, H, N, d, scale, dtype, wsp, nws):
     return fb.raw_bob(ins, outs, B, H, N, d, scale, dtype, wsp, nws)
 
 
-@pytest.mark.parametrize("d", [0, 32, 63, 96, 256])
+@pytest.mark.parametrize("d", [0, 16, 48, 63, 100, 160, 256])
 def test_rejects_unsupported_d(d):
     a = list(fake_args())
     a[5] = d
@@ -201,7 +201,7 @@ def test_ex_rejects_unknown_flags_and_stage_sets():
         assert call_ex(*fake_args(), stages=stages) == FLAGS
     # the flags check comes first, the shape checks still apply after it
     a = list(fake_args())
-    a[5] = 96
+    a[5] = 80
     assert call_ex(*a, flags=1, stages=7) == UD
     lib = fb.load_library()
     vp = ctypes.c_void_p
