@@ -270,6 +270,15 @@ __device__ __forceinline__ void st4(float* p, float a, float b, float c, float d
   *reinterpret_cast<f32x4*>(p) = v;
 }
 
+// Store four consecutive output elements at element index i of an output
+// tensor held in float32, or in bf16 (rounded to nearest even) when bf16out.
+__device__ __forceinline__ void store_out4(void* base, size_t i, float a, float b, float c, float d, int bf16out) {
+  if (bf16out)
+    st4(static_cast<bf16*>(base) + i, a, b, c, d);
+  else
+    st4(static_cast<float*>(base) + i, a, b, c, d);
+}
+
 // ---------------------------------------------------------------------------
 // global -> LDS row copies (16 bytes per lane per step), zero rows past `nrows`
 

@@ -131,9 +131,8 @@ __global__ __launch_bounds__(256, (KeyCfg<T, D, FIRST>::OCC2 ? 2 : 1)) void key_
     const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V, const T* __restrict__ dO,
     const T* __restrict__ gQ, const T* __restrict__ gK, const T* __restrict__ gV,
     const float* __restrict__ lse2, const float* __restrict__ Dv, const float* __restrict__ cv,
-    const float* __restrict__ rv, float* __restrict__ gradK, float* __restrict__ gradV, float* __restrict__ dKo,
-    float* __restrict__ dVo, int N, int nkblk,
-    float scale, int causal, int G) {
+    const float* __restrict__ rv, void* __restrict__ gradK, void* __restrict__ gradV, void* __restrict__ dKo,
+    void* __restrict__ dVo, int N, int nkblk, float scale, int causal, int G, int out_bf16) {
   using Cfg = KeyCfg<T, D, FIRST>;
   using E = Elem<T>;
   using F = typename E::frag;
@@ -368,23 +367,23 @@ __global__ __launch_bounds__(256, (KeyCfg<T, D, FIRST>::OCC2 ? 2 : 1)) void key_
 
   // accK[j] slot i holds d = 32 j + acc_row(h, i) of this lane's key
   if (kvalid) {
-    float* gk = gradK + hoff + (size_t)key * D;
-    float* gv = gradV + hoff + (size_t)key * D;
+    const size_t row = hoff + (size_t)key * D;
 #pragma unroll
     for (int j = 0; j < NDB; ++j) {
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int d0 = 32 * j + 8 * g + 4 * h;
-        *reinterpret_cast<float4*>(gk + d0) = make_float4(scale * accK[j][4 * g], scale * accK[j][4 * g + 1],
-                                                          scale * accK[j][4 * g + 2], scale * accK[j][4 * g + 3]);
-        *reinterpret_cast<float4*>(gv + d0) =
-            make_float4(accV[j][4 * g], accV[j][4 * g + 1], accV[j][4 * g + 2], accV[j][4 * g + 3]);
+        const f32x16& a = accK[j];
+        const f32x16& v = accV[j];
+        store_out4(gradK, row + d0, scale * a[4 * g], scale * a[4 * g + 1], scale * a[4 * g + 2],
+                   scale * a[4 * g + 3], out_bf16);
+        store_out4(gradV, row + d0, v[4 * g], v[4 * g + 1], v[4 * g + 2], v[4 * g + 3], out_bf16);
         if constexpr (FIRST) {
-          const size_t o = hoff + (size_t)key * D + d0;
-          *reinterpret_cast<float4*>(dKo + o) = make_float4(scale * accdK[j][4 * g], scale * accdK[j][4 * g + 1],
-                                                            scale * accdK[j][4 * g + 2], scale * accdK[j][4 * g + 3]);
-          *reinterpret_cast<float4*>(dVo + o) =
-              make_float4(accdV[j][4 * g], accdV[j][4 * g + 1], accdV[j][4 * g + 2], accdV[j][4 * g + 3]);
+          const f32x16& fk = accdK[j];
+          const f32x16& fv = accdV[j];
+          store_out4(dKo, row + d0, scale * fk[4 * g], scale * fk[4 * g + 1], scale * fk[4 * g + 2],
+                     scale * fk[4 * g + 3], out_bf16);
+          store_out4(dVo, row + d0, fv[4 * g], fv[4 * g + 1], fv[4 * g + 2], fv[4 * g + 3], out_bf16);
         }
       }
     }
@@ -394,23 +393,23 @@ __global__ __launch_bounds__(256, (KeyCfg<T, D, FIRST>::OCC2 ? 2 : 1)) void key_
 template <typename T, int D, bool FIRST>
 hipError_t launch_key(const void* Q, const void* K, const void* V, const void* dO, const void* gQ, const void* gK,
                       const void* gV, const float* lse2, const float* Dv, const float* cv, const float* rv,
-                      float* gradK, float* gradV, float* dK, float* dV, int BHkv, int N, float scale, int causal,
-                      int G, hipStream_t stream) {
+                      void* gradK, void* gradV, void* dK, void* dV, int BHkv, int N, float scale, int causal,
+                      int G, int out_bf16, hipStream_t stream) {
   using Cfg = KeyCfg<T, D, FIRST>;
   const int nkblk = (N + Cfg::BC - 1) / Cfg::BC;
   const long long nblocks = (long long)nkblk * BHkv;
   if (nblocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   key_kernel<T, D, FIRST><<<dim3((unsigned)nblocks), dim3(256), 0, stream>>>(
       (const T*)Q, (const T*)K, (const T*)V, (const T*)dO, (const T*)gQ, (const T*)gK, (const T*)gV, lse2, Dv, cv,
-      rv, gradK, gradV, dK, dV, N, nkblk, scale, causal, G);
+      rv, gradK, gradV, dK, dV, N, nkblk, scale, causal, G, out_bf16);
   return hipGetLastError();
 }
 
 #define FLASHBOB_INST_KEY(T, D, F)                                                                         \
   template hipError_t launch_key<T, D, F>(const void*, const void*, const void*, const void*, const void*, \
                                           const void*, const void*, const float*, const float*,             \
-                                          const float*, const float*, float*, float*, float*, float*, int,  \
-                                          int, float, int, int, hipStream_t);
+                                          const float*, const float*, void*, void*, void*, void*, int, int, \
+                                          float, int, int, int, hipStream_t);
 #define FLASHBOB_INST_KEY_DIMS(F) \
   FLASHBOB_INST_KEY(bf16, 32, F)  \
   FLASHBOB_INST_KEY(bf16, 64, F)  \

@@ -188,9 +188,9 @@ template <typename T, int D, bool GRADQ, bool FIRST, bool SAVED>
 __global__ __launch_bounds__(256, (QueryCfg<T, D, GRADQ>::OCC2 && !FIRST ? 2 : 1)) void query_kernel(
     const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V, const T* __restrict__ dO,
     const T* __restrict__ gQ, const T* __restrict__ gK, const T* __restrict__ gV, float* __restrict__ lse,
-    float* __restrict__ Dv, float* __restrict__ cv, float* __restrict__ rv, float* __restrict__ gradQ,
-    float* __restrict__ graddO, float* __restrict__ dQo, const float* __restrict__ lse_in, int N, int nqblk,
-    float scale, int lse_natural, int causal, int G) {
+    float* __restrict__ Dv, float* __restrict__ cv, float* __restrict__ rv, void* __restrict__ gradQ,
+    void* __restrict__ graddO, void* __restrict__ dQo, const float* __restrict__ lse_in, int N, int nqblk,
+    float scale, int lse_natural, int causal, int G, int out_bf16) {
   static_assert(!(SAVED && GRADQ), "a saved log-sum-exp replaces pass 1's running maximum only");
   using Cfg = QueryCfg<T, D, GRADQ>;
   using E = Elem<T>;
@@ -461,22 +461,22 @@ __global__ __launch_bounds__(256, (QueryCfg<T, D, GRADQ>::OCC2 && !FIRST ? 2 : 1
   } else {
     // accQ[j] slot i holds d = 32 j + acc_row(h, i) of this lane's query
     if (qvalid) {
-      float* gq = gradQ + hoff + (size_t)q * D;
-      float* go = graddO + hoff + (size_t)q * D;
+      const size_t row = hoff + (size_t)q * D;
 #pragma unroll
       for (int j = 0; j < NDB; ++j) {
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
           const int d0 = 32 * j + 8 * g + 4 * h;
-          *reinterpret_cast<float4*>(gq + d0) =
-              make_float4(scale * accQ[j][4 * g], scale * accQ[j][4 * g + 1], scale * accQ[j][4 * g + 2],
-                          scale * accQ[j][4 * g + 3]);
-          *reinterpret_cast<float4*>(go + d0) =
-              make_float4(accO[j][4 * g], accO[j][4 * g + 1], accO[j][4 * g + 2], accO[j][4 * g + 3]);
-          if constexpr (FIRST)
-            *reinterpret_cast<float4*>(dQo + hoff + (size_t)q * D + d0) =
-                make_float4(scale * accdQ[j][4 * g], scale * accdQ[j][4 * g + 1], scale * accdQ[j][4 * g + 2],
-                            scale * accdQ[j][4 * g + 3]);
+          const f32x16& a = accQ[j];
+          const f32x16& o = accO[j];
+          store_out4(gradQ, row + d0, scale * a[4 * g], scale * a[4 * g + 1], scale * a[4 * g + 2],
+                     scale * a[4 * g + 3], out_bf16);
+          store_out4(graddO, row + d0, o[4 * g], o[4 * g + 1], o[4 * g + 2], o[4 * g + 3], out_bf16);
+          if constexpr (FIRST) {
+            const f32x16& f = accdQ[j];
+            store_out4(dQo, row + d0, scale * f[4 * g], scale * f[4 * g + 1], scale * f[4 * g + 2],
+                       scale * f[4 * g + 3], out_bf16);
+          }
         }
       }
     }
@@ -486,23 +486,23 @@ __global__ __launch_bounds__(256, (QueryCfg<T, D, GRADQ>::OCC2 && !FIRST ? 2 : 1
 template <typename T, int D, bool GRADQ, bool FIRST, bool SAVED>
 hipError_t launch_query(const void* Q, const void* K, const void* V, const void* dO, const void* gQ,
                         const void* gK, const void* gV, float* lse, float* Dv, float* cv, float* rv,
-                        float* gradQ, float* graddO, float* dQ, const float* lse_in, int BH, int N, float scale,
-                        int lse_natural, int causal, int G, hipStream_t stream) {
+                        void* gradQ, void* graddO, void* dQ, const float* lse_in, int BH, int N, float scale,
+                        int lse_natural, int causal, int G, int out_bf16, hipStream_t stream) {
   using Cfg = QueryCfg<T, D, GRADQ>;
   const int nqblk = (N + Cfg::BQ - 1) / Cfg::BQ;
   const long long nblocks = (long long)nqblk * BH;
   if (nblocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   query_kernel<T, D, GRADQ, FIRST, SAVED><<<dim3((unsigned)nblocks), dim3(256), 0, stream>>>(
       (const T*)Q, (const T*)K, (const T*)V, (const T*)dO, (const T*)gQ, (const T*)gK, (const T*)gV, lse, Dv,
-      cv, rv, gradQ, graddO, dQ, lse_in, N, nqblk, scale, lse_natural, causal, G);
+      cv, rv, gradQ, graddO, dQ, lse_in, N, nqblk, scale, lse_natural, causal, G, out_bf16);
   return hipGetLastError();
 }
 
 #define FLASHBOB_INST_QUERY(T, D, G, F, S)                                                                \
   template hipError_t launch_query<T, D, G, F, S>(const void*, const void*, const void*, const void*,      \
                                                   const void*, const void*, const void*, float*, float*,   \
-                                                  float*, float*, float*, float*, float*, const float*,    \
-                                                  int, int, float, int, int, int, hipStream_t);
+                                                  float*, float*, void*, void*, void*, const float*,       \
+                                                  int, int, float, int, int, int, int, hipStream_t);
 // Pass 1 and pass 2q instantiations are built as separate objects (pass 1
 // with MFMA results kept in VGPRs, which its register budget allows).
 // Pass 1: plain and with a saved log-sum-exp; pass 2q: plain and with the

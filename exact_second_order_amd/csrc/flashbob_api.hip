@@ -18,13 +18,13 @@ typedef __bf16 bf16;
 template <typename T, int D, bool GRADQ, bool FIRST, bool SAVED>
 hipError_t launch_query(const void* Q, const void* K, const void* V, const void* dO, const void* gQ,
                         const void* gK, const void* gV, float* lse, float* Dv, float* cv, float* rv,
-                        float* gradQ, float* graddO, float* dQ, const float* lse_in, int BH, int N, float scale,
-                        int lse_natural, int causal, int G, hipStream_t stream);
+                        void* gradQ, void* graddO, void* dQ, const float* lse_in, int BH, int N, float scale,
+                        int lse_natural, int causal, int G, int out_bf16, hipStream_t stream);
 template <typename T, int D, bool FIRST>
 hipError_t launch_key(const void* Q, const void* K, const void* V, const void* dO, const void* gQ, const void* gK,
                       const void* gV, const float* lse2, const float* Dv, const float* cv, const float* rv,
-                      float* gradK, float* gradV, float* dK, float* dV, int BHkv, int N, float scale, int causal,
-                      int G, hipStream_t stream);
+                      void* gradK, void* gradV, void* dK, void* dV, int BHkv, int N, float scale, int causal,
+                      int G, int out_bf16, hipStream_t stream);
 }  // namespace flashbob
 
 namespace {
@@ -90,39 +90,55 @@ enum Stage {
   kPass2Key = FLASHBOB_STAGE_PASS2_KEY,
 };
 
-// first: also the first-backward outputs fb[3] = dQ, dK, dV; lse_in: the
-// rows' saved log-sum-exp for pass 1, or null
+// Everything one flashbob_bob_ex call hands its kernels besides the inputs.
+struct Call {
+  int stages, causal;
+  const float* lse_in;  // the rows' saved log-sum-exp for pass 1, or null
+  float* stats;         // workspace: [4][B*H*N] row scalars
+  void *gradQ, *gradK, *gradV, *graddO;
+  void *dQ, *dK, *dV;   // first-backward outputs, or null
+  int out_bf16;         // outputs stored as bf16 instead of float32
+  int BH, G, N;
+  float scale;
+  hipStream_t stream;
+};
+
 template <typename T, int D>
-hipError_t run_stages(int stages, int causal, bool first, const void* const* in, const float* lse_in,
-                      float* stats, float* gQo, float* gKo, float* gVo, float* gdOo, float* const* fb, int BH,
-                      int G, int N, float scale, hipStream_t st) {
-  const size_t BHN = (size_t)BH * N;
+hipError_t run_stages(const void* const* in, const Call& c) {
+  const size_t BHN = (size_t)c.BH * c.N;
   // workspace row scalars: LSE * log2(e), D, c, r
-  float *lse = stats, *Dv = stats + BHN, *cv = stats + 2 * BHN, *rv = stats + 3 * BHN;
+  float *lse = c.stats, *Dv = c.stats + BHN, *cv = c.stats + 2 * BHN, *rv = c.stats + 3 * BHN;
+  const bool first = c.dQ != nullptr;
   hipError_t e = hipSuccess;
-  if (stages & kPass1) {
-    e = lse_in ? flashbob::launch_query<T, D, false, false, true>(in[0], in[1], in[2], in[3], in[4], in[5], in[6],
-                                                                  lse, Dv, cv, rv, nullptr, nullptr, nullptr,
-                                                                  lse_in, BH, N, scale, 0, causal, G, st)
-               : flashbob::launch_query<T, D, false, false, false>(in[0], in[1], in[2], in[3], in[4], in[5], in[6],
-                                                                   lse, Dv, cv, rv, nullptr, nullptr, nullptr,
-                                                                   nullptr, BH, N, scale, 0, causal, G, st);
+  if (c.stages & kPass1) {
+    e = c.lse_in ? flashbob::launch_query<T, D, false, false, true>(in[0], in[1], in[2], in[3], in[4], in[5], in[6],
+                                                                    lse, Dv, cv, rv, nullptr, nullptr, nullptr,
+                                                                    c.lse_in, c.BH, c.N, c.scale, 0, c.causal, c.G,
+                                                                    0, c.stream)
+                 : flashbob::launch_query<T, D, false, false, false>(in[0], in[1], in[2], in[3], in[4], in[5],
+                                                                     in[6], lse, Dv, cv, rv, nullptr, nullptr,
+                                                                     nullptr, nullptr, c.BH, c.N, c.scale, 0,
+                                                                     c.causal, c.G, 0, c.stream);
     if (e != hipSuccess) return e;
   }
-  if (stages & kPass2Query) {
+  if (c.stages & kPass2Query) {
     e = first ? flashbob::launch_query<T, D, true, true, false>(in[0], in[1], in[2], in[3], in[4], in[5], in[6],
-                                                                lse, Dv, cv, rv, gQo, gdOo, fb[0], nullptr, BH, N,
-                                                                scale, 0, causal, G, st)
+                                                                lse, Dv, cv, rv, c.gradQ, c.graddO, c.dQ, nullptr,
+                                                                c.BH, c.N, c.scale, 0, c.causal, c.G, c.out_bf16,
+                                                                c.stream)
               : flashbob::launch_query<T, D, true, false, false>(in[0], in[1], in[2], in[3], in[4], in[5], in[6],
-                                                                 lse, Dv, cv, rv, gQo, gdOo, nullptr, nullptr, BH,
-                                                                 N, scale, 0, causal, G, st);
+                                                                 lse, Dv, cv, rv, c.gradQ, c.graddO, nullptr,
+                                                                 nullptr, c.BH, c.N, c.scale, 0, c.causal, c.G,
+                                                                 c.out_bf16, c.stream);
     if (e != hipSuccess) return e;
   }
-  if (stages & kPass2Key) {
+  if (c.stages & kPass2Key) {
     e = first ? flashbob::launch_key<T, D, true>(in[0], in[1], in[2], in[3], in[4], in[5], in[6], lse, Dv, cv, rv,
-                                                 gKo, gVo, fb[1], fb[2], BH / G, N, scale, causal, G, st)
+                                                 c.gradK, c.gradV, c.dK, c.dV, c.BH / c.G, c.N, c.scale, c.causal,
+                                                 c.G, c.out_bf16, c.stream)
               : flashbob::launch_key<T, D, false>(in[0], in[1], in[2], in[3], in[4], in[5], in[6], lse, Dv, cv, rv,
-                                                  gKo, gVo, nullptr, nullptr, BH / G, N, scale, causal, G, st);
+                                                  c.gradK, c.gradV, nullptr, nullptr, c.BH / c.G, c.N, c.scale,
+                                                  c.causal, c.G, c.out_bf16, c.stream);
   }
   return e;
 }
@@ -149,12 +165,9 @@ hipError_t on_type_and_dim(int dtype, int d, Fn&& f) {
   return dtype == FLASHBOB_BF16 ? dims(TypeTag<__bf16>{}) : dims(TypeTag<float>{});
 }
 
-hipError_t dispatch(int dtype, int d, int stages, int causal, bool first, const void* const* in,
-                    const float* lse_in, float* stats, float* gQo, float* gKo, float* gVo, float* gdOo,
-                    float* const* fb, int BH, int G, int N, float scale, hipStream_t st) {
+hipError_t dispatch(int dtype, int d, const void* const* in, const Call& c) {
   return on_type_and_dim(dtype, d, [&](auto t, auto dd) {
-    return run_stages<typename decltype(t)::type, decltype(dd)::value>(stages, causal, first, in, lse_in, stats,
-                                                                       gQo, gKo, gVo, gdOo, fb, BH, G, N, scale, st);
+    return run_stages<typename decltype(t)::type, decltype(dd)::value>(in, c);
   });
 }
 
@@ -163,7 +176,7 @@ hipError_t rowstats_launch(const void* const* in, float* lse, float* Dv, float* 
                            int N, float scale, int causal, hipStream_t st) {
   return flashbob::launch_query<T, D, false, false, false>(in[0], in[1], in[2], in[3], in[4], in[5], in[6], lse,
                                                            Dv, cv, rv, nullptr, nullptr, nullptr, nullptr, BH, N,
-                                                           scale, 1, causal, G, st);
+                                                           scale, 1, causal, G, 0, st);
 }
 
 hipError_t dispatch_rowstats(int dtype, int d, int causal, const void* const* in, float* lse, float* Dv, float* cv,
@@ -203,20 +216,22 @@ void tensor_bytes(size_t numel_q, size_t numel_kv, size_t esz, size_t* in_bytes)
 }
 
 int flashbob_bob_ex(const void* Q, const void* K, const void* V, const void* dO, const void* gQ, const void* gK,
-                    const void* gV, float* gradQ, float* gradK, float* gradV, float* graddO, float* dQ, float* dK,
-                    float* dV, const float* lse_in, int B, int H, int H_kv, int N, int d, float scale, int dtype,
+                    const void* gV, void* gradQ, void* gradK, void* gradV, void* graddO, void* dQ, void* dK,
+                    void* dV, const float* lse_in, int B, int H, int H_kv, int N, int d, float scale, int dtype,
                     int flags, int stages, void* workspace, size_t workspace_bytes, void* stream) {
-  if ((flags & ~(FLASHBOB_CAUSAL | FLASHBOB_FIRST_BACKWARD | FLASHBOB_SAVED_LSE)) != 0 || stages <= 0 ||
-      (stages & ~FLASHBOB_STAGES_ALL) != 0)
+  constexpr int kKnownFlags = FLASHBOB_CAUSAL | FLASHBOB_FIRST_BACKWARD | FLASHBOB_SAVED_LSE | FLASHBOB_BF16_OUTPUTS;
+  if ((flags & ~kKnownFlags) != 0 || stages <= 0 || (stages & ~FLASHBOB_STAGES_ALL) != 0)
     return FLASHBOB_ERR_FLAGS;
   const bool first = (flags & FLASHBOB_FIRST_BACKWARD) != 0;
   const bool saved = (flags & FLASHBOB_SAVED_LSE) != 0;
+  const bool bf16_out = (flags & FLASHBOB_BF16_OUTPUTS) != 0;
   const void* ins[8] = {Q, K, V, dO, gQ, gK, gV, lse_in};
   size_t numel = 0;
   int rc = check_common(ins, B, H, N, d, scale, dtype, &numel);
   if (rc == FLASHBOB_OK) rc = check_kv_heads(H, H_kv);
   if (rc != FLASHBOB_OK || numel == 0) return rc;
   const size_t esz = dtype == FLASHBOB_BF16 ? 2 : 4;
+  const size_t osz = bf16_out ? 2 : 4;  // output element size
   const size_t numel_kv = numel / (size_t)H * (size_t)H_kv;
   const size_t ws_need = stats_bytes(B, H, N);
   if (workspace == nullptr) return FLASHBOB_ERR_NULL;
@@ -229,15 +244,32 @@ int flashbob_bob_ex(const void* Q, const void* K, const void* V, const void* dO,
   tensor_bytes(numel, numel_kv, esz, ib);
   ib[7] = numel / (size_t)d * 4;  // lse_in: B*H*N floats
   void* outs[8] = {gradQ, gradK, gradV, graddO, workspace, dQ, dK, dV};
-  const size_t ob[8] = {numel * 4, numel_kv * 4, numel_kv * 4, numel * 4, ws_need,
-                        numel * 4, numel_kv * 4, numel_kv * 4};
+  const size_t ob[8] = {numel * osz, numel_kv * osz, numel_kv * osz, numel * osz, ws_need,
+                        numel * osz, numel_kv * osz, numel_kv * osz};
   // dQ, dK, dV are outputs only with their flag, lse_in an input only with its
   rc = check_outputs(ins, ib, saved ? 8 : 7, outs, ob, first ? 8 : 5);
   if (rc != FLASHBOB_OK) return rc;
-  float* const fb[3] = {dQ, dK, dV};
-  const hipError_t e = dispatch(dtype, d, stages, (flags & FLASHBOB_CAUSAL) ? 1 : 0, first, ins,
-                                saved ? lse_in : nullptr, static_cast<float*>(workspace), gradQ, gradK, gradV,
-                                graddO, fb, B * H, H / H_kv, N, scale, static_cast<hipStream_t>(stream));
+  Call c{};
+  c.stages = stages;
+  c.causal = (flags & FLASHBOB_CAUSAL) ? 1 : 0;
+  c.lse_in = saved ? lse_in : nullptr;
+  c.stats = static_cast<float*>(workspace);
+  c.gradQ = gradQ;
+  c.gradK = gradK;
+  c.gradV = gradV;
+  c.graddO = graddO;
+  if (first) {
+    c.dQ = dQ;
+    c.dK = dK;
+    c.dV = dV;
+  }
+  c.out_bf16 = bf16_out ? 1 : 0;
+  c.BH = B * H;
+  c.G = H / H_kv;
+  c.N = N;
+  c.scale = scale;
+  c.stream = static_cast<hipStream_t>(stream);
+  const hipError_t e = dispatch(dtype, d, ins, c);
   return e == hipSuccess ? FLASHBOB_OK : hip_fail(e);
 }
 

@@ -18,6 +18,7 @@ FLASHBOB_BF16 = 1
 FLASHBOB_CAUSAL = 1
 FLASHBOB_FIRST_BACKWARD = 2
 FLASHBOB_SAVED_LSE = 4
+FLASHBOB_BF16_OUTPUTS = 8
 STAGE_BITS = {"pass1": 1, "pass2_query": 2, "pass2_key": 4}
 
 ERRORS = {
@@ -148,15 +149,16 @@ def workspace_bytes(B, H, N, d):
     return int(load_library().flashbob_workspace_bytes(B, H, N, d))
 
 
-def _check_out(tensors, shapes, device, what):
-    """Caller-given outputs: float32, contiguous, on the inputs' device, of
-    the expected shapes (the C ABI sees only pointers and trusts the sizes)."""
+def _check_out(tensors, shapes, device, what, dtype=torch.float32):
+    """Caller-given outputs: `dtype` (float32, or bfloat16 with the bf16-output
+    flag), contiguous, on the inputs' device, of the expected shapes (the C ABI
+    sees only pointers and trusts the sizes)."""
     tensors = tuple(tensors)
     if len(tensors) != len(shapes):
         raise ValueError(f"{what}: expected {len(shapes)} tensors, got {len(tensors)}")
     for t, s in zip(tensors, shapes):
-        if not isinstance(t, torch.Tensor) or t.dtype != torch.float32 or t.device != device:
-            raise TypeError(f"{what}: outputs must be float32 tensors on {device}")
+        if not isinstance(t, torch.Tensor) or t.dtype != dtype or t.device != device:
+            raise TypeError(f"{what}: outputs must be {dtype} tensors on {device}")
         if tuple(t.shape) != tuple(s) or not t.is_contiguous():
             raise ValueError(f"{what}: expected contiguous {tuple(s)}, got {tuple(t.shape)}")
     return tensors
@@ -171,9 +173,16 @@ def _check_lse(lse, B, H, N, device):
     return lse
 
 
+def _out_dtype(dt):
+    if dt not in (torch.float32, torch.bfloat16):
+        raise TypeError(f"unsupported output dtype {dt}; use torch.float32 or torch.bfloat16")
+    return dt
+
+
 def _call_ex(lib, ins, out, first, lse, B, H, Hkv, N, d, scale, dtype, causal, stages, workspace, stream):
     flags = ((FLASHBOB_CAUSAL if causal else 0) | (FLASHBOB_FIRST_BACKWARD if first is not None else 0)
-             | (FLASHBOB_SAVED_LSE if lse is not None else 0))
+             | (FLASHBOB_SAVED_LSE if lse is not None else 0)
+             | (FLASHBOB_BF16_OUTPUTS if out[0].dtype == torch.bfloat16 else 0))
     fb = first if first is not None else (None, None, None)
     return lib.flashbob_bob_ex(*[_ptr(t) for t in ins], *[_ptr(t) for t in out], *[_ptr(t) for t in fb],
                                _ptr(lse), B, H, Hkv, N, d, ctypes.c_float(scale), _dtype_code(dtype), flags,
@@ -197,6 +206,8 @@ def bob_stage(stage, Q, K, V, dO, gQ, gK, gV, out, workspace, scale=None, stream
     also fill with the first backward (flag FLASHBOB_FIRST_BACKWARD).
     lse: None, or the rows' saved log-sum-exp [B, H, N] that pass 1 starts
     from (flag FLASHBOB_SAVED_LSE).
+    The outputs' dtype (float32, or bfloat16: flag FLASHBOB_BF16_OUTPUTS) is
+    that of out[0]; every output must have it.
     """
     lib = load_library()
     ins, Hkv = _inputs(Q, K, V, dO, gQ, gK, gV)
@@ -204,13 +215,15 @@ def bob_stage(stage, Q, K, V, dO, gQ, gK, gV, out, workspace, scale=None, stream
     if scale is None:
         scale = d ** -0.5
     shapes = shapes_of(B, H, Hkv, N, d)
-    out = _check_out(out, shapes, Q.device, "out")
+    out = tuple(out)
+    odt = _out_dtype(out[0].dtype if out and isinstance(out[0], torch.Tensor) else torch.float32)
+    out = _check_out(out, shapes, Q.device, "out", odt)
     _check_workspace(workspace, B, H, N, d, Q.device)
     if first is not None:
-        first = _check_out(first, shapes[:3], Q.device, "first")
+        first = _check_out(first, shapes[:3], Q.device, "first", odt)
     if lse is not None:
         _check_lse(lse, B, H, N, Q.device)
-    if causal or Hkv != H or first is not None or lse is not None:
+    if causal or Hkv != H or first is not None or lse is not None or odt != torch.float32:
         rc = _call_ex(lib, ins, out, first, lse, B, H, Hkv, N, d, scale, Q.dtype, causal, STAGE_BITS[stage],
                       workspace, _stream_handle(Q.device, stream))
     else:
@@ -223,7 +236,7 @@ def bob_stage(stage, Q, K, V, dO, gQ, gK, gV, out, workspace, scale=None, stream
 
 
 def bob(Q, K, V, dO, gQ, gK, gV, scale=None, out=None, workspace=None, stream=None, causal=False,
-        first_backward=False, first_out=None, lse=None):
+        first_backward=False, first_out=None, lse=None, out_dtype=torch.float32):
     """Exact BoB of softmax attention: (gradQ, gradK, gradV, graddO), float32.
 
     Inputs [B, H, N, d] bf16 or fp32 device tensors; `scale` defaults to
@@ -240,6 +253,8 @@ def bob(Q, K, V, dO, gQ, gK, gV, scale=None, out=None, workspace=None, stream=No
     pass keeps it): pass 1 then starts from it instead of tracking a running
     maximum (flag FLASHBOB_SAVED_LSE; the outputs do not depend on it beyond
     rounding).
+    out_dtype=torch.bfloat16 stores every output as bf16 (the float32 results
+    rounded to nearest even; flag FLASHBOB_BF16_OUTPUTS).
     """
     lib = load_library()
     ins, Hkv = _inputs(Q, K, V, dO, gQ, gK, gV)
@@ -247,9 +262,10 @@ def bob(Q, K, V, dO, gQ, gK, gV, scale=None, out=None, workspace=None, stream=No
     if scale is None:
         scale = d ** -0.5
     shapes = shapes_of(B, H, Hkv, N, d)
+    odt = _out_dtype(out_dtype)
     if out is None:
-        out = tuple(torch.empty(s, dtype=torch.float32, device=Q.device) for s in shapes)
-    out = _check_out(out, shapes, Q.device, "out")
+        out = tuple(torch.empty(s, dtype=odt, device=Q.device) for s in shapes)
+    out = _check_out(out, shapes, Q.device, "out", odt)
     nws = lib.flashbob_workspace_bytes(B, H, N, d)
     if workspace is None:
         workspace = torch.empty(max(nws, 1), dtype=torch.uint8, device=Q.device)
@@ -258,11 +274,11 @@ def bob(Q, K, V, dO, gQ, gK, gV, scale=None, out=None, workspace=None, stream=No
     if first_backward:
         first = first_out
         if first is None:
-            first = tuple(torch.empty(s, dtype=torch.float32, device=Q.device) for s in shapes[:3])
-        first = _check_out(first, shapes[:3], Q.device, "first_out")
+            first = tuple(torch.empty(s, dtype=odt, device=Q.device) for s in shapes[:3])
+        first = _check_out(first, shapes[:3], Q.device, "first_out", odt)
     if lse is not None:
         _check_lse(lse, B, H, N, Q.device)
-    if causal or Hkv != H or first is not None or lse is not None:
+    if causal or Hkv != H or first is not None or lse is not None or odt != torch.float32:
         rc = _call_ex(lib, ins, out, first, lse, B, H, Hkv, N, d, scale, Q.dtype, causal, 7, workspace,
                       _stream_handle(Q.device, stream))
     else:

@@ -71,7 +71,8 @@ enum {
 enum {
   FLASHBOB_CAUSAL = 1,          /* query i attends to keys j <= i */
   FLASHBOB_FIRST_BACKWARD = 2,  /* flashbob_bob_ex only: also write the first backward dQ, dK, dV */
-  FLASHBOB_SAVED_LSE = 4        /* flashbob_bob_ex only: pass 1 starts from a saved log-sum-exp */
+  FLASHBOB_SAVED_LSE = 4,       /* flashbob_bob_ex only: pass 1 starts from a saved log-sum-exp */
+  FLASHBOB_BF16_OUTPUTS = 8     /* flashbob_bob_ex only: outputs are stored as bf16 */
 };
 
 /* Stage sets of flashbob_bob_ex (the three kernels of the schedule). */
@@ -163,6 +164,11 @@ int flashbob_bob_pass2_key(const void* Q, const void* K, const void* V, const vo
  *           give the same outputs up to rounding (far enough below them the
  *           exponentials overflow, far enough above they underflow). Without
  *           the flag lse_in is ignored (may be NULL).
+ *           bf16 outputs: gradQ, gradK, gradV, graddO (and dQ, dK, dV) hold
+ *           bf16 values (2 bytes per element, same shapes and 16-byte
+ *           alignment): the float32 results rounded to nearest even as they
+ *           are stored. The arithmetic is unchanged; the workspace and
+ *           lse_in stay float32. Without the flag the outputs are float32.
  *   stages  a non-empty subset of FLASHBOB_STAGES_ALL, run in the order
  *           pass 1, pass 2 query side, pass 2 key side. Pass 2 stages read the
  *           row scalars pass 1 left in `workspace` (computed with the same
@@ -171,8 +177,8 @@ int flashbob_bob_pass2_key(const void* Q, const void* K, const void* V, const vo
  * bits or stage sets return FLASHBOB_ERR_FLAGS. */
 int flashbob_bob_ex(const void* Q, const void* K, const void* V, const void* dO,
                     const void* gQ, const void* gK, const void* gV,
-                    float* gradQ, float* gradK, float* gradV, float* graddO,
-                    float* dQ, float* dK, float* dV, const float* lse_in,
+                    void* gradQ, void* gradK, void* gradV, void* graddO,
+                    void* dQ, void* dK, void* dV, const float* lse_in,
                     int B, int H, int H_kv, int N, int d, float scale, int dtype, int flags, int stages,
                     void* workspace, size_t workspace_bytes, void* stream);
 

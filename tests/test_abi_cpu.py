@@ -195,7 +195,7 @@ def call_ex(ins, outs, B, H, N, d, scale, dtype, wsp, nws, flags=0, stages=7, hk
 
 def test_ex_rejects_unknown_flags_and_stage_sets():
     FLAGS = -10
-    for flags in (8, 9, 16, -1, 1 << 20):
+    for flags in (16, 17, 32, -1, 1 << 20):
         assert call_ex(*fake_args(), flags=flags, first=FIRST, lse=LSE) == FLAGS
     for stages in (0, 8, 9, -1, 16):
         assert call_ex(*fake_args(), stages=stages) == FLAGS
@@ -212,7 +212,7 @@ def test_ex_rejects_unknown_flags_and_stage_sets():
 
 def test_ex_empty_problem_is_a_noop():
     # B*H*N == 0 returns OK before any HIP call, with or without the mask
-    for flags in range(8):
+    for flags in range(16):
         assert call_ex(*fake_args(B=0), flags=flags) == 0
 
 
@@ -290,3 +290,19 @@ def test_ex_saved_lse_checks():
     assert call_ex(*a, flags=SV, lse=LSE + 4) == -100   # 4-byte aligned is enough
     assert call_ex(*a, flags=SV, lse=a[0][0]) == -100   # reading an input's memory is no hazard
     assert call_ex(*a, flags=0, lse=LSE + 1) == -100    # ignored without the flag
+
+
+def test_ex_bf16_outputs_use_two_byte_sizes():
+    # with FLASHBOB_BF16_OUTPUTS every output is half as large: an output
+    # placed right after another's bf16 extent is legal (the call then fails
+    # only for want of a device), the same placement overlaps float32 outputs
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("would launch kernels on a real device with fake pointers")
+    B, H, N, d = 1, 1, 128, 64
+    ins, outs, *rest = fake_args(B=B, H=H, N=N, d=d)
+    outs = list(outs)
+    outs[1] = outs[0] + B * H * N * d * 2   # gradK right after a bf16 gradQ
+    a = (ins, outs, *rest)
+    assert call_ex(*a, flags=fb.FLASHBOB_BF16_OUTPUTS) == -100
+    assert call_ex(*a, flags=0) == ALIAS
