@@ -24,6 +24,7 @@ sys.path.insert(0, ROOT)
 METRIC = "BoB TFLOP/s + ms/call at N=65536,d=64 (1 MI355X); % of bf16 MFMA peak"
 PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}  # MI355X published dense MFMA peaks
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+MFMA_FILE = os.path.join(ROOT, "profiles", "mfma_util.json")
 KERNEL_SOURCES = ("exact_second_order_amd/csrc/bob_query.hip", "exact_second_order_amd/csrc/bob_key.hip",
                   "exact_second_order_amd/csrc/bob_device.h")
 
@@ -40,18 +41,32 @@ def kernel_source_hash():
     return h.hexdigest()[:16]
 
 
-def measured_traffic(stage, causal=False):
+def measured_traffic(stage, causal=False, workload="bob_b1h4n65536d64_bf16"):
     """HBM bytes per launch of `stage` from committed rocprofv3 counters, if
-    they were taken on the current kernel sources (and with the same mask);
-    else None."""
+    they were taken on the current kernel sources, the same workload and the
+    same mask; else None."""
     try:
         with open(TRAFFIC_FILE) as f:
             t = json.load(f)
     except (OSError, ValueError):
         return None
-    if t.get("kernel_source_sha256_16") != kernel_source_hash():
+    if t.get("kernel_source_sha256_16") != kernel_source_hash() or t.get("workload") != workload:
         return None
     return t.get("bytes_per_launch_causal" if causal else "bytes_per_launch", {}).get(stage)
+
+
+def measured_mfma(stage, workload="bob_b1h4n65536d64_bf16"):
+    """MFMA utilisation and shader clock of `stage` from committed rocprofv3
+    counters (unmasked), if taken on the current kernel sources and the same
+    workload; else None."""
+    try:
+        with open(MFMA_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_source_sha256_16") != kernel_source_hash() or t.get("workload") != workload:
+        return None
+    return t.get("kernels", {}).get(stage)
 
 
 def cpu_baseline(w, rows, block=512, causal=False):
@@ -189,12 +204,24 @@ def main():
         kf = 2.0 * units[st] * w.B * w.H * w.N * w.N * w.d * frac_pairs
         per_kernel[st] = {"ms": round(ms, 4), "tflops": round(kf / (ms * 1e-3) / 1e12, 2),
                           "frac": round(kf / (ms * 1e-3) / 1e12 / peak, 4), "units": units[st]}
+    # counter-derived figures (committed profiles of the plain headline run)
+    plain = not (args.causal or args.first_backward or args.saved_lse)
+    for st in stages:
+        traffic = (measured_traffic(st, args.causal, w.name)
+                   if not (args.first_backward or args.saved_lse) else None)
+        if traffic is not None:
+            per_kernel[st]["hbm_GBps"] = round(traffic / (per_kernel[st]["ms"] * 1e-3) / 1e9, 1)
+        m = measured_mfma(st, w.name) if plain else None
+        if m is not None:
+            per_kernel[st]["mfma_util"] = round(m["mfma_util"], 4)
+            per_kernel[st]["sclk_ghz"] = round(m["sclk_ghz"], 3)
     log(f"[bench] ms/step {ms_step:.3f}; {tflops:.1f} TFLOP/s = {100 * tflops / peak:.1f}% of {peak} peak; "
         f"kernels {per_kernel}")
     dom = max(stages, key=lambda st: per_kernel[st]["ms"])
     roofline = {"bound": "mfma", "achieved": per_kernel[dom]["tflops"], "peak": peak, "unit": "TFLOP/s",
                 "frac": per_kernel[dom]["frac"],
-                "traffic": None if (args.first_backward or args.saved_lse) else measured_traffic(dom, args.causal),
+                "traffic": (None if (args.first_backward or args.saved_lse)
+                            else measured_traffic(dom, args.causal, w.name)),
                 "kernel": kernel_names[dom], "launch_ms": per_kernel[dom]["ms"]}
 
     cpu = None

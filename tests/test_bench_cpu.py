@@ -1,0 +1,46 @@
+"""bench.py's host logic that needs no GPU: the committed counter summaries
+parse, name the three kernels, and are attached only to the workload (and
+kernel sources) they were taken on."""
+
+import json
+import os
+import subprocess
+import sys
+
+import bench
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+STAGES = ("pass1", "pass2_query", "pass2_key")
+
+
+def test_committed_counter_files_parse():
+    t = json.load(open(bench.TRAFFIC_FILE))
+    m = json.load(open(bench.MFMA_FILE))
+    for f in (t, m):
+        assert len(f["kernel_source_sha256_16"]) == 16
+        assert f["workload"] == "bob_b1h4n65536d64_bf16"
+    assert set(t["bytes_per_launch"]) == set(STAGES)
+    assert set(t["bytes_per_launch_causal"]) == set(STAGES)
+    for st in STAGES:
+        k = m["kernels"][st]
+        assert 0 < k["mfma_util"] < 1 and 1.0 < k["sclk_ghz"] < 2.5
+        assert abs(k["mfma_insts_over_algorithmic"] - 1) < 1e-6
+
+
+def test_counters_only_for_their_workload():
+    for st in STAGES:
+        assert bench.measured_traffic(st, False, "bob_b1h8n16384d128_bf16") is None
+        assert bench.measured_mfma(st, "bob_b1h1n262144d64_bf16") is None
+
+
+def test_counters_only_for_their_kernel_sources(monkeypatch):
+    monkeypatch.setattr(bench, "kernel_source_hash", lambda: "0" * 16)
+    for st in STAGES:
+        assert bench.measured_traffic(st) is None
+        assert bench.measured_mfma(st) is None
+
+
+def test_multi_gpu_request_exits_with_message():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=120)
+    assert r.returncode == 2 and "one GPU" in r.stderr
