@@ -132,24 +132,18 @@ __device__ __forceinline__ void online_chunk(int cc, const f32x16& S, const f32x
     st.ah *= alpha;
     st.m = mn;
   }
-  float bl = 0.f, bD = 0.f, bc = 0.f, be = 0.f, bh = 0.f;
 #pragma unroll
   for (int s = 0; s < 8; ++s) {
     const int i = 8 * cc + s;
     float p = fast_exp2(fmaf(S[i], sl2, -mu));
     if (TAIL && acc_row(h, i) >= nvalid_rel) p = 0.f;
     const float t = p * dP[i];
-    bl += p;
-    bD += t;
-    bc = fmaf(p, G[i], bc);
-    be = fmaf(t, G[i], be);
-    bh = fmaf(p, H[i], bh);
+    st.l += p;
+    st.aD += t;
+    st.ac = fmaf(p, G[i], st.ac);
+    st.ae = fmaf(t, G[i], st.ae);
+    st.ah = fmaf(p, H[i], st.ah);
   }
-  st.l += bl;
-  st.aD += bD;
-  st.ac += bc;
-  st.ae += be;
-  st.ah += bh;
 }
 
 // pass 2q elementwise step of one 16-key chunk cc of a 32-key block, turned
