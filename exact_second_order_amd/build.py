@@ -12,6 +12,10 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libflashbob.so")
+# a plain C program that drives the C ABI without torch (run by the tests)
+C_CHECK_SRC = os.path.join(ROOT, "tests", "c_abi_check.c")
+C_CHECK = os.path.join(PKG, "_build", "c_abi_check")
+ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
 
 # (source, extra flags): bob_query.hip is built twice. The pass-1 object keeps
 # MFMA results in VGPRs (its register budget allows it, and its elementwise
@@ -70,6 +74,10 @@ def build(verbose=False):
     tmp = LIB + ".tmp"
     _run([hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp], verbose)
     os.replace(tmp, LIB)
+    if os.path.exists(C_CHECK_SRC):
+        _run(["gcc", "-std=c11", "-O2", "-Wall", "-Werror", "-D__HIP_PLATFORM_AMD__", "-I", os.path.join(ROCM, "include"),
+              "-I", INCLUDE, C_CHECK_SRC, "-L", PKG, "-lflashbob", "-L", os.path.join(ROCM, "lib"), "-lamdhip64",
+              "-Wl,-rpath,$ORIGIN/..", "-Wl,-rpath," + os.path.join(ROCM, "lib"), "-o", C_CHECK], verbose)
     return LIB
 
 

@@ -306,3 +306,16 @@ def test_ex_bf16_outputs_use_two_byte_sizes():
     a = (ins, outs, *rest)
     assert call_ex(*a, flags=fb.FLASHBOB_BF16_OUTPUTS) == -100
     assert call_ex(*a, flags=0) == ALIAS
+
+
+def test_plain_c_caller_is_built_and_checks_its_arguments():
+    # the C program of tests/c_abi_check.c (built with the library) refuses a
+    # bad command line before making any HIP call
+    import subprocess
+    from exact_second_order_amd import build
+    assert os.path.exists(build.C_CHECK), "run python -m exact_second_order_amd.build"
+    r = subprocess.run([build.C_CHECK], capture_output=True, text=True, timeout=60)
+    assert r.returncode == 2 and "usage" in r.stderr
+    r = subprocess.run([build.C_CHECK, "1", "1", "0", "64", "0", "0.1", "0", "/nonexistent", "/nonexistent"],
+                       capture_output=True, text=True, timeout=60)
+    assert r.returncode == 2 and "bad arguments" in r.stderr
