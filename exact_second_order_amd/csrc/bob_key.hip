@@ -35,15 +35,16 @@ struct KeyCfg {
   static constexpr int BQ = 32;                        // queries per LDS stage (one MFMA block)
   static constexpr int LDQ = D + 16 / (int)sizeof(T);  // padded LDS row (elements)
   static constexpr int NCH = D / 16, NDB = D / 32;
-  // same staging and occupancy choices as the query-major kernel
+  // same staging choices as the query-major kernel; two waves per SIMD for
+  // bf16 d = 64 and for d = 32 (FIRST: the first-backward dK, dV accumulators
+  // need the one-wave budget)
   static constexpr bool SWZ = sizeof(T) == 2 && D == 64;
-  // (FIRST: the first-backward dK, dV accumulators need the one-wave budget)
-  static constexpr bool OCC2 = SWZ && !FIRST;
+  static constexpr bool OCC2 = (SWZ || D == 32) && !FIRST;
   static constexpr int NBUF = 2;                       // stage n in use, stage n+1 arriving
   // SWZ: which of the wave's K, gK, V, gV operand tensors (bits 0..3) live in
   // LDS instead of registers: gV only, which is what the register budget of two
   // waves per SIMD leaves over (every per-block LDS read costs time)
-  static constexpr int KLDS = OCC2 ? 0x8 : 0;
+  static constexpr int KLDS = (OCC2 && SWZ) ? 0x8 : 0;
   static constexpr int NKLDS = __builtin_popcount(KLDS);
   static constexpr int ROWLEN = SWZ ? D : LDQ;
   static constexpr int QSTAGE = 3 * BQ * ROWLEN;       // Q, gQ, dO elements of one stage

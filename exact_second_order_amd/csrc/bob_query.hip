@@ -46,12 +46,14 @@ struct QueryCfg {
   static constexpr int NCH = D / 16;                   // 16-wide k chunks over d
   static constexpr int NDB = D / 32;                   // 32-row blocks of d
   // bf16 d = 64 stages tiles with direct global->LDS loads into swizzled
-  // unpadded rows (no staging registers) and runs two waves per SIMD (<= 256
-  // registers: the second wave hides the first one's latencies and overlaps
-  // its VALU work with the other's MFMAs). The other variants stage through
-  // registers into padded rows at one wave per SIMD.
+  // unpadded rows (no staging registers); the other variants stage through
+  // registers into padded rows. Two waves per SIMD (<= 256 registers: the
+  // second wave hides the first one's latencies and overlaps its VALU work
+  // with the other's MFMAs) where the per-wave state fits: bf16 d = 64, pass 1
+  // in bf16 at every d (a few bytes spill at d = 96, 128, still faster), and
+  // d = 32; the rest run one wave per SIMD.
   static constexpr bool SWZ = sizeof(T) == 2 && D == 64;
-  static constexpr bool OCC2 = SWZ;
+  static constexpr bool OCC2 = SWZ || (!GRADQ && sizeof(T) == 2) || D == 32;
   static constexpr int NBUF = 2;                       // stage n in use, stage n+1 arriving
   static constexpr int STAGE = 4 * BK * (SWZ ? D : LDK);  // elements of one stage
   static constexpr size_t LDS_BYTES = NBUF * STAGE * sizeof(T);
