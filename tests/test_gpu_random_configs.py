@@ -64,3 +64,20 @@ def test_random_config(seed):
         else:
             e = rel_fro(got, ref)
             assert e <= tol, f"output {k}: rel {e:.3e} > {tol}"
+
+
+@pytest.mark.parametrize("N,causal", [(64, False), (33, True), (129, False)])
+def test_many_short_heads(N, causal):
+    # hundreds of heads of a few blocks each (many small workgroups, grouped
+    # heads, a single partial block when N < 64)
+    B, H, Hkv, d = 8, 16, 4, 64
+    say(f"[random] many short heads B={B} H={H} Hkv={Hkv} N={N} causal={causal}")
+    ins = make_inputs(B, H, N, d, torch.bfloat16, seed=4000 + N, H_kv=Hkv)
+    outs = fb.bob(*[ins[k].to("cuda") for k in NAMES], causal=causal, first_backward=True)
+    torch.cuda.synchronize()
+    xs = [ins[k].to(torch.float64).numpy() for k in NAMES]
+    refs = list(oracle.bob_gqa(*xs, d ** -0.5, causal=causal))
+    refs += list(oracle.attention_backward_batched(*xs[:4], d ** -0.5, causal=causal))
+    for k, (o, ref) in enumerate(zip(outs, refs)):
+        e = rel_fro(to_f64(o), ref)
+        assert e <= TOL[torch.bfloat16], f"output {k}: rel {e:.3e}"
