@@ -16,7 +16,9 @@ Independent routes used:
     bilinearity, zero cotangents, N = 1, key-shift invariance.
 """
 
+import json
 import math
+import os
 
 import numpy as np
 import pytest
@@ -562,3 +564,33 @@ def test_first_backward_rows_match_autograd(causal):
     assert rel(got, ref) < 1e-12
     if causal:
         assert np.abs(got[0]).max() < 1e-14  # one visible key: dS = 0
+
+
+# ----------------------------------------------------------------------------
+# exact values by symbolic differentiation of the objective's definition
+# (tests/golden/symbolic_bob.json, written by tests/golden/make_symbolic_bob.py
+# with sympy: no oracle code involved)
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", "symbolic_bob.json")
+
+
+def _golden_cases():
+    with open(GOLDEN) as f:
+        return json.load(f)["cases"]
+
+
+@pytest.mark.parametrize("case", _golden_cases(), ids=lambda c: c["name"])
+def test_oracle_matches_symbolic_differentiation(case):
+    from fractions import Fraction
+
+    def arr(rows):
+        return np.array([[float(Fraction(x)) for x in r] for r in rows])
+
+    xs = [arr(case["inputs"][k]) for k in ("Q", "K", "V", "dO", "gQ", "gK", "gV")]
+    s = float(Fraction(case["scale"]))
+    got = oracle.bob_head(*xs, s, causal=case["causal"])
+    for k, name in enumerate(("gradQ", "gradK", "gradV", "graddO")):
+        want = arr(case["outputs"][name])
+        assert np.abs(got[k] - want).max() <= 1e-12 * max(1.0, np.abs(want).max()), name
+    L = oracle.bob_objective(*xs, s, causal=case["causal"])
+    assert abs(L - float(case["objective"])) <= 1e-12 * max(1.0, abs(float(case["objective"])))
