@@ -297,14 +297,17 @@ struct RowPrefetch {
   typedef __attribute__((__vector_size__(16))) int v4i;
   v4i r[NIT > 0 ? NIT : 1];
 
+  // Raw buffer loads over the valid rows only: rows past nrows_valid (and the
+  // surplus steps of a RAGGED copy, whose rows lie past the block) read as
+  // zero without a branch, so the caller's loop body stays one basic block.
   __device__ __forceinline__ void load(const T* src, int nrows_valid) {
+    const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(src, nrows_valid * COLS * (int)sizeof(T));
 #pragma unroll
     for (int it = 0; it < NIT; ++it) {
       const int idx = it * NTHREADS + (int)threadIdx.x;
       const int row = idx / VPR, cv = idx % VPR;
-      r[it] = v4i{0, 0, 0, 0};
-      if ((!RAGGED || idx < TOTAL) && row < nrows_valid)
-        r[it] = *reinterpret_cast<const v4i*>(src + (size_t)row * COLS + cv * VEC);
+      r[it] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(
+                                          rs, (row * COLS + cv * VEC) * (int)sizeof(T), 0, 0));
     }
   }
   __device__ __forceinline__ void store(T* dst, int ldd) const {

@@ -48,7 +48,11 @@ struct KeyCfg {
   static constexpr int NKLDS = __builtin_popcount(KLDS);
   static constexpr int ROWLEN = SWZ ? D : LDQ;
   static constexpr int QSTAGE = 3 * BQ * ROWLEN;       // Q, gQ, dO elements of one stage
-  static constexpr int SSTAGE = 4 * BQ;                // row scalars of one stage (floats)
+  // floats per row-scalar slot of a stage: SWZ loads a slot with one 4-byte
+  // buffer load per lane of a wave, so its slot spans 64 floats (lanes 32..63
+  // read past the stage's rows, get zeros, and write them to the padding)
+  static constexpr int SLOT = SWZ ? 64 : BQ;
+  static constexpr int SSTAGE = 4 * SLOT;              // row scalars of one stage (floats)
   // the LDS-resident key-side tiles (NKLDS per wave, 32 x D each) follow the
   // stage buffers
   static constexpr size_t KSIDE = (size_t)4 * NKLDS * 32 * D * sizeof(T);
@@ -147,7 +151,7 @@ __global__ __launch_bounds__(256, (KeyCfg<T, D, FIRST>::OCC2 ? 2 : 1)) void key_
   auto tile = [&](int b, int t) __attribute__((always_inline)) { return reinterpret_cast<T*>(smem) + (b * 3 + t) * BQ * ROWLEN; };
   auto sQ = [&](int b, int t, int row, int col) __attribute__((always_inline)) { return tile(b, t) + row * ROWLEN + col; };
   auto sS = [&](int b, int t) __attribute__((always_inline)) {
-    return reinterpret_cast<float*>(smem + NBUF * Cfg::QSTAGE * sizeof(T)) + (b * 4 + t) * BQ;
+    return reinterpret_cast<float*>(smem + NBUF * Cfg::QSTAGE * sizeof(T)) + (b * 4 + t) * Cfg::SLOT;
   };
   auto lds_rows = [&](int b, int t, int c16) __attribute__((always_inline)) -> F {
     if constexpr (SWZ) return ld_rows_sw(tile(b, t), 0, c16);
@@ -163,6 +167,8 @@ __global__ __launch_bounds__(256, (KeyCfg<T, D, FIRST>::OCC2 ? 2 : 1)) void key_
   // key/value head `head`; the query heads of its group are head * G + g
   const size_t hoff = (size_t)head * N * D;
   size_t qoff = 0, soff = 0;  // query head of the current group member
+  // the row scalar this wave (SWZ) or thread (otherwise) stages, of that member
+  const float* stat_src = nullptr;
   const int w = wave_id(), l = lane_id(), h = l >> 5, col = l & 31;
   const int key = kblk * Cfg::BC + 32 * w + col;  // this lane's key
   const bool kvalid = key < N;
@@ -231,28 +237,23 @@ __global__ __launch_bounds__(256, (KeyCfg<T, D, FIRST>::OCC2 ? 2 : 1)) void key_
       load_tile_sw(tile(b, 1), gQ + qoff + (size_t)q0 * D, nq);
       load_tile_sw(tile(b, 2), dO + qoff + (size_t)q0 * D, nq);
       // wave w fetches row scalar w (LSE*log2e, -D, -c/s, -r) of the stage's
-      // queries: lane L < 32 -> row L, written at LDS float L of sS(b, w);
-      // rows past the end read as zero
-      if (l < 32) {
-        const float* arr = w == 0 ? lse2 : w == 1 ? Dv : w == 2 ? cv : rv;
-        typedef __attribute__((address_space(3))) void lds_void;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(buffer_rsrc(arr + soff + q0, nq * 4), (lds_void*)sS(b, w), 4,
-                                                 4 * l, 0, 0, 0);
-      }
+      // queries: lane L -> row L, written at LDS float L of sS(b, w); rows past
+      // the end (and lanes 32..63) read as zero. No branch: the loop body
+      // stays one straight-line block.
+      typedef __attribute__((address_space(3))) void lds_void;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(buffer_rsrc(stat_src + q0, nq * 4), (lds_void*)sS(b, w), 4, 4 * l,
+                                               0, 0, 0);
     } else {
       pq.load(Q + qoff + (size_t)q0 * D, nq);
       pg.load(gQ + qoff + (size_t)q0 * D, nq);
       pd.load(dO + qoff + (size_t)q0 * D, nq);
-      if ((int)threadIdx.x < 4 * BQ) {
-        const int t = threadIdx.x / BQ, i = threadIdx.x % BQ;
-        const bool ok = i < nq;
-        const size_t o = soff + q0 + i;
-        // queries past the end get LSE = +inf, hence P = 0
-        if (t == 0) pstat = ok ? lse2[o] : INFINITY;
-        else if (t == 1) pstat = ok ? Dv[o] : 0.f;
-        else if (t == 2) pstat = ok ? cv[o] : 0.f;
-        else pstat = ok ? rv[o] : 0.f;
-      }
+      // thread -> (scalar (tid / BQ) % 4, row tid % BQ); threads 128..255 repeat
+      // 0..127 (same values to the same LDS slots), so there is no branch.
+      // Queries past the end get LSE = +inf (hence P = 0) and zero scalars;
+      // the row index is clamped so every load stays in bounds.
+      const int i = threadIdx.x % BQ;
+      const float v = stat_src[q0 + min(i, nq - 1)];
+      pstat = i < nq ? v : (((threadIdx.x / BQ) & 3) == 0 ? INFINITY : 0.f);
     }
   };
   auto commit = [&](int n) __attribute__((always_inline)) {
@@ -263,7 +264,7 @@ __global__ __launch_bounds__(256, (KeyCfg<T, D, FIRST>::OCC2 ? 2 : 1)) void key_
       pq.store(sQ(b, 0, 0, 0), LDQ);
       pg.store(sQ(b, 1, 0, 0), LDQ);
       pd.store(sQ(b, 2, 0, 0), LDQ);
-      if ((int)threadIdx.x < 4 * BQ) sS(b, threadIdx.x / BQ)[threadIdx.x % BQ] = pstat;
+      sS(b, (threadIdx.x / BQ) & 3)[threadIdx.x % BQ] = pstat;
     }
   };
 
@@ -339,31 +340,47 @@ __global__ __launch_bounds__(256, (KeyCfg<T, D, FIRST>::OCC2 ? 2 : 1)) void key_
   for (int g = 0; g < G; ++g) {
     qoff = (size_t)(head * G + g) * N * D;
     soff = (size_t)(head * G + g) * N;
+    {
+      const int si = SWZ ? w : (int)(threadIdx.x / BQ) & 3;
+      stat_src = (si == 0 ? lse2 : si == 1 ? Dv : si == 2 ? cv : rv) + soff;
+    }
     prefetch(nstart);  // nstart < nblk; the previous member's last barrier freed both buffers
     commit(nstart);
     __syncthreads();
-    // iterations in pairs from the even nstart, so that the stage buffer index
-    // is a compile-time constant in both halves
-    for (int i = nstart >> 1; 2 * i < nblk; ++i) {
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const int n = 2 * i + u;
-        if (u == 1 && n >= nblk) break;  // odd block count: the last pair is a single
-        const bool pf = n + 1 < nblk;
-        if (pf) prefetch(n + 1);
-        recompute(n, t, 0, NCH);
-#pragma unroll
-        for (int cc = 0; cc < 2; ++cc) {
-          if (ktail || n < ndiag || (n == nblk - 1 && last_partial))
-            elementwise(F1{}, n, cc, t, f);
-          else
-            elementwise(F0{}, n, cc, t, f);
-          outputs(n, cc, f);
-        }
-        if (pf) commit(n + 1);  // its buffer last held stage n-1, read in iteration n-1
-        __syncthreads();
-      }
+    // Blocks in ascending order. The masked ones take the masked elementwise
+    // path: the causal diagonal [nstart, ndiag), a partial last query block,
+    // and every block of a partial key block (ktail). The unmasked stretch
+    // between them runs as a branch-free pair loop (no mask test, the next
+    // stage always prefetched), so each pair is one straight-line block the
+    // scheduler can interleave.
+    const int mask_end = ktail ? nblk : min(ndiag, nblk);  // masked head [nstart, mask_end)
+    const int clean_end = ktail ? nblk : max(mask_end, nblk - (last_partial ? 1 : 0));  // unmasked up to here
+    // one 32-query block n: TAIL selects the masked path, PF prefetches stage
+    // n + 1 (into the buffer that last held stage n - 1, read in block n - 1)
+#define FLASHBOB_KEY_BLOCK(n, TAIL, PF)               \
+  {                                                   \
+    if (PF) prefetch((n) + 1);                        \
+    recompute((n), t, 0, NCH);                        \
+    _Pragma("unroll") for (int cc = 0; cc < 2; ++cc) { \
+      elementwise(TAIL, (n), cc, t, f);               \
+      outputs((n), cc, f);                            \
+    }                                                 \
+    if (PF) commit((n) + 1);                          \
+    __syncthreads();                                  \
+  }
+    for (int n = nstart; n < mask_end; ++n) FLASHBOB_KEY_BLOCK(n, F1{}, n + 1 < nblk)
+    // pairs from the even mask_end, so the stage buffer index of each half is a
+    // compile-time constant; both halves have a next stage
+    int i = mask_end >> 1;
+    for (; 2 * i + 2 <= clean_end && 2 * i + 2 < nblk; ++i) {
+      FLASHBOB_KEY_BLOCK(2 * i, F0{}, true)
+      FLASHBOB_KEY_BLOCK(2 * i + 1, F0{}, true)
     }
+    // the rest of the unmasked stretch (at most two blocks; mask_end is odd only
+    // when the masked head runs to nblk, and then this stretch is empty)
+    for (int n = max(2 * i, mask_end); n < clean_end; ++n) FLASHBOB_KEY_BLOCK(n, F0{}, n + 1 < nblk)
+    if (!ktail && last_partial && nblk - 1 >= mask_end) FLASHBOB_KEY_BLOCK(nblk - 1, F1{}, false)
+#undef FLASHBOB_KEY_BLOCK
   }
 
   // accK[j] slot i holds d = 32 j + acc_row(h, i) of this lane's key
