@@ -292,19 +292,24 @@ struct RowPrefetch {
   static_assert(COLS % VEC == 0, "rows are whole 16-byte vectors");
   static constexpr int TOTAL = ROWS * VPR;                     // vectors to copy
   static constexpr int NIT = (TOTAL + NTHREADS - 1) / NTHREADS;  // ROWS = 0: unused placeholder
-  // whether the last step has idle threads (d = 32, 96 in bf16)
+  // whether the steps do not split evenly (d = 32, 96 in bf16): the surplus
+  // steps then repeat real ones (index mod TOTAL), storing the same values to
+  // the same LDS slots, so no step needs a guard
   static constexpr bool RAGGED = TOTAL % NTHREADS != 0;
+  __device__ __forceinline__ static int step_index(int it) {
+    const int idx = it * NTHREADS + (int)threadIdx.x;
+    return RAGGED ? idx % TOTAL : idx;
+  }
   typedef __attribute__((__vector_size__(16))) int v4i;
   v4i r[NIT > 0 ? NIT : 1];
 
-  // Raw buffer loads over the valid rows only: rows past nrows_valid (and the
-  // surplus steps of a RAGGED copy, whose rows lie past the block) read as
+  // Raw buffer loads over the valid rows only: rows past nrows_valid read as
   // zero without a branch, so the caller's loop body stays one basic block.
   __device__ __forceinline__ void load(const T* src, int nrows_valid) {
     const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(src, nrows_valid * COLS * (int)sizeof(T));
 #pragma unroll
     for (int it = 0; it < NIT; ++it) {
-      const int idx = it * NTHREADS + (int)threadIdx.x;
+      const int idx = step_index(it);
       const int row = idx / VPR, cv = idx % VPR;
       r[it] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(
                                           rs, (row * COLS + cv * VEC) * (int)sizeof(T), 0, 0));
@@ -313,9 +318,9 @@ struct RowPrefetch {
   __device__ __forceinline__ void store(T* dst, int ldd) const {
 #pragma unroll
     for (int it = 0; it < NIT; ++it) {
-      const int idx = it * NTHREADS + (int)threadIdx.x;
+      const int idx = step_index(it);
       const int row = idx / VPR, cv = idx % VPR;
-      if (!RAGGED || idx < TOTAL) *reinterpret_cast<v4i*>(dst + row * ldd + cv * VEC) = r[it];
+      *reinterpret_cast<v4i*>(dst + row * ldd + cv * VEC) = r[it];
     }
   }
 };
