@@ -19,8 +19,10 @@
 // the exponent. P, dS, dS2, A then feed the next
 // MFMAs straight from the accumulator registers as B operands (k = queries in
 // accumulator row order), against Q^T, gQ^T, dO^T read from the LDS stage with
-// transpose loads in the same order. gradK^T and gradV^T stay in registers for
-// the whole sweep.
+// transpose loads in the same order. gradK^T and gradV^T (FIRST: also the
+// first-backward dK^T = s dS^T Q and dV^T = P^T dO) stay in registers for the
+// whole sweep. The masked blocks (causal diagonal, partial blocks) run apart
+// from a branch-free pair loop over the rest.
 
 #include <type_traits>
 

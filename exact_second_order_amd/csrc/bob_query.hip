@@ -14,11 +14,13 @@
 //            One sweep with an online running max m: accumulate
 //            l = sum Pt, aD = sum Pt dP, ac = sum Pt G, ae = sum Pt dP G,
 //            ah = sum Pt H (Pt = exp(s S - m)), then D = aD/l, c = ac/l,
-//            r = ae/l - D c + ah/l, LSE = m + ln l.
+//            r = ae/l - D c + ah/l, LSE = m + ln l. (SAVED: m is fixed at a
+//            saved log-sum-exp of the row for the whole sweep.)
 //   pass 2q: dS  = P (dP - D),  A = P (G - c),  dS2 = dS (G - c) + P (H - r),
 //            gradQ = s (dS2 K + dS gK),  graddO = A V + P gV.
 //            Pass 1 hands the scalars over as LSE log2(e), -D, -c/s and -r
 //            (the key-major kernel starts its dP, G, H accumulators from them).
+//            FIRST: also the first-backward dQ = s dS K.
 //
 // gfx950 schedule: a workgroup of 4 waves owns 128 queries (32 per wave) and
 // streams the keys in 32-row stages (K, gK, V, gV) through two LDS buffers,
