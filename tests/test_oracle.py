@@ -581,16 +581,25 @@ def _golden_cases():
 
 @pytest.mark.parametrize("case", _golden_cases(), ids=lambda c: c["name"])
 def test_oracle_matches_symbolic_differentiation(case):
+    # BoB outputs and objective (grouped case: through bob_gqa) and the first
+    # backward (sympy differentiated the forward <dO, O>, not the backward
+    # formulas) against the exact values
     from fractions import Fraction
 
-    def arr(rows):
-        return np.array([[float(Fraction(x)) for x in r] for r in rows])
+    def arr(heads):  # [heads][N][d] strings -> [1, heads, N, d] float64
+        return np.array([[[[float(Fraction(x)) for x in r] for r in m] for m in heads]])
 
-    xs = [arr(case["inputs"][k]) for k in ("Q", "K", "V", "dO", "gQ", "gK", "gV")]
+    x = {k: arr(case["inputs"][k]) for k in ("Q", "K", "V", "dO", "gQ", "gK", "gV")}
+    xs = [x[k] for k in ("Q", "K", "V", "dO", "gQ", "gK", "gV")]
     s = float(Fraction(case["scale"]))
-    got = oracle.bob_head(*xs, s, causal=case["causal"])
-    for k, name in enumerate(("gradQ", "gradK", "gradV", "graddO")):
+    causal = case["causal"]
+    got = list(oracle.bob_gqa(*xs, s, causal=causal))
+    got += list(oracle.attention_backward_batched(*xs[:4], s, causal=causal))
+    for k, name in enumerate(("gradQ", "gradK", "gradV", "graddO", "dQ", "dK", "dV")):
         want = arr(case["outputs"][name])
+        assert got[k].shape == want.shape, name
         assert np.abs(got[k] - want).max() <= 1e-12 * max(1.0, np.abs(want).max()), name
-    L = oracle.bob_objective(*xs, s, causal=case["causal"])
-    assert abs(L - float(case["objective"])) <= 1e-12 * max(1.0, abs(float(case["objective"])))
+    if case["group"] == 1:
+        h = [x[k][0, 0] for k in ("Q", "K", "V", "dO", "gQ", "gK", "gV")]
+        L = oracle.bob_objective(*h, s, causal=causal)
+        assert abs(L - float(case["objective"])) <= 1e-12 * max(1.0, abs(float(case["objective"])))
