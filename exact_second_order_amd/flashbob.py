@@ -237,11 +237,12 @@ def bob_stage(stage, Q, K, V, dO, gQ, gK, gV, out, workspace, scale=None, stream
 
 def bob(Q, K, V, dO, gQ, gK, gV, scale=None, out=None, workspace=None, stream=None, causal=False,
         first_backward=False, first_out=None, lse=None, out_dtype=torch.float32):
-    """Exact BoB of softmax attention: (gradQ, gradK, gradV, graddO), float32.
+    """Exact BoB of softmax attention: (gradQ, gradK, gradV, graddO).
 
     Inputs [B, H, N, d] bf16 or fp32 device tensors; `scale` defaults to
-    1/sqrt(d). `out` (four float32 tensors) and `workspace` (uint8 tensor of
-    at least workspace_bytes(B, H, N, d)) may be given to avoid allocation.
+    1/sqrt(d). `out` (four tensors of dtype out_dtype, shapes as returned)
+    and `workspace` (a device tensor of at least workspace_bytes(B, H, N, d)
+    bytes) may be given; with them (and first_out) the call allocates nothing.
     causal=True masks key j > query i (flashbob_bob_ex with FLASHBOB_CAUSAL).
     K, V, gK, gV may have fewer heads than Q (grouped-query attention): then
     gradK, gradV have their shape and sum over each group's query heads.
