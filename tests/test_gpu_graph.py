@@ -1,8 +1,13 @@
-"""The library call inside a captured HIP graph (torch.cuda.CUDAGraph): the
-C ABI allocates nothing and records no memset, so a graph of one BoB call with
-preallocated outputs and workspace replays to the eager result. Replayed
-several times with eager work and new input values between replays; every
-replay is compared bit for bit with an eager call on the same inputs."""
+"""Capture and concurrency.
+
+The library call inside a captured HIP graph (torch.cuda.CUDAGraph): the C ABI
+allocates nothing and records no memset, so a graph of one BoB call with
+preallocated outputs and workspace replays to the eager result. It is replayed
+several times with eager work and new input values between replays, and every
+replay is compared bit for bit with an eager call on the same inputs.
+
+Host threads calling concurrently on their own streams get the results of
+serial calls (the library keeps no global state)."""
 
 import pytest
 import torch
@@ -45,3 +50,38 @@ def test_graph_replay_matches_eager(causal, first):
         torch.cuda.synchronize()
         for k, (a, b) in enumerate(zip(got, ref)):
             assert torch.equal(a, b), f"replay {rep} output {k} differs from the eager call"
+
+
+def test_concurrent_host_threads_on_separate_streams():
+    # the library keeps no global state: four host threads, each on its own
+    # stream with its own problem, get the same results as serial calls
+    import threading
+
+    say("[graph] four host threads, four streams")
+    probs = [make_inputs(1, 2, 600 + 50 * i, 64, torch.bfloat16, seed=1850 + i) for i in range(4)]
+    dev = [[p[k].to("cuda") for k in NAMES] for p in probs]
+    ref = [fb.bob(*x, causal=bool(i % 2)) for i, x in enumerate(dev)]
+    torch.cuda.synchronize()
+    got = [None] * 4
+    errors = []
+
+    def work(i):
+        try:
+            s = torch.cuda.Stream()
+            with torch.cuda.stream(s):
+                for _ in range(3):
+                    got[i] = fb.bob(*dev[i], causal=bool(i % 2), stream=s)
+            s.synchronize()
+        except Exception as e:  # reported below
+            errors.append(e)
+
+    threads = [threading.Thread(target=work, args=(i,)) for i in range(4)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    torch.cuda.synchronize()
+    assert not errors, errors
+    for i in range(4):
+        for k in range(4):
+            assert torch.equal(got[i][k], ref[i][k]), (i, k)
