@@ -164,8 +164,11 @@ __global__ __launch_bounds__(256, (KeyCfg<T, D, FIRST>::OCC2 ? 2 : 1)) void key_
     else return ld_cols_perm(sQ(b, t, krow0, col0), LDQ);
   };
 
-  const int head = blockIdx.x / nkblk;
-  const int kblk = blockIdx.x % nkblk;
+  // causal: the longest sweeps (the first key blocks) start first, across all
+  // key/value heads at once
+  const int nheads = (int)(gridDim.x / nkblk);
+  const int head = causal ? (int)(blockIdx.x % nheads) : (int)(blockIdx.x / nkblk);
+  const int kblk = causal ? (int)(blockIdx.x / nheads) : (int)(blockIdx.x % nkblk);
   // key/value head `head`; the query heads of its group are head * G + g
   const size_t hoff = (size_t)head * N * D;
   size_t qoff = 0, soff = 0;  // query head of the current group member

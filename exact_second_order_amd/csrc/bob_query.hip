@@ -209,9 +209,12 @@ __global__ __launch_bounds__(256, (QueryCfg<T, D, GRADQ>::OCC2 && !FIRST ? 2 : 1
     else return ld_cols_perm(sK(b, t, krow0, col0), LDK);
   };
 
-  const int head = blockIdx.x / nqblk;
-  // (causal: the longest sweeps, the last query blocks, start first)
-  const int qblk = causal ? nqblk - 1 - (int)(blockIdx.x % nqblk) : (int)(blockIdx.x % nqblk);
+  // causal: the longest sweeps (the last query blocks) start first, across
+  // all heads at once (consecutive workgroups take the same block of
+  // successive heads)
+  const int nheads = (int)(gridDim.x / nqblk);
+  const int head = causal ? (int)(blockIdx.x % nheads) : (int)(blockIdx.x / nqblk);
+  const int qblk = causal ? nqblk - 1 - (int)(blockIdx.x / nheads) : (int)(blockIdx.x % nqblk);
   const size_t hoff = (size_t)head * N * D;         // query head (Q, dO, gQ, outputs)
   const size_t koff = (size_t)(head / G) * N * D;   // its key/value head (groups of G)
   const int w = wave_id(), l = lane_id(), h = l >> 5, col = l & 31;
