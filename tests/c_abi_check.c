@@ -65,6 +65,10 @@ int main(int argc, char** argv) {
   const int dtype = atoi(argv[5]), causal = atoi(argv[7]);
   const float scale = (float)atof(argv[6]);
   const char *in_dir = argv[8], *out_dir = argv[9];
+  /* stdout is a pipe under the test runner: unbuffered, so nothing printed is
+     lost if the process ends abnormally; progress goes to stderr */
+  setvbuf(stdout, NULL, _IONBF, 0);
+#define STEP(msg) fprintf(stderr, "c_abi_check: %s\n", msg)
   if (B <= 0 || H <= 0 || N <= 0 || (dtype != FLASHBOB_F32 && dtype != FLASHBOB_BF16)) {
     fprintf(stderr, "bad arguments\n");
     return 2;
@@ -82,6 +86,7 @@ int main(int argc, char** argv) {
     HIP_OK(hipMemcpy(dev_in[i], host, numel * esz, hipMemcpyHostToDevice));
   }
   for (int i = 0; i < 4; ++i) HIP_OK(hipMalloc((void**)&dev_out[i], numel * 4));
+  STEP("inputs on the device");
   const size_t ws_bytes = flashbob_workspace_bytes(B, H, N, d);
   void* ws = NULL;
   HIP_OK(hipMalloc(&ws, ws_bytes));
@@ -105,11 +110,14 @@ int main(int argc, char** argv) {
     fprintf(stderr, "flashbob call failed: %d (%s)\n", rc, flashbob_strerror(rc));
     return 1;
   }
+  STEP("call enqueued");
   HIP_OK(hipDeviceSynchronize());
+  STEP("call finished");
   for (int i = 0; i < 4; ++i) {
     HIP_OK(hipMemcpy(host, dev_out[i], numel * 4, hipMemcpyDeviceToHost));
     if (write_file(out_dir, kOut[i], host, numel * 4)) return 1;
   }
+  STEP("outputs written");
   for (int i = 0; i < 7; ++i) HIP_OK(hipFree(dev_in[i]));
   for (int i = 0; i < 4; ++i) HIP_OK(hipFree(dev_out[i]));
   HIP_OK(hipFree(ws));
