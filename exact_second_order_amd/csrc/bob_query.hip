@@ -56,6 +56,11 @@ struct QueryCfg {
   // d = 32; the rest run one wave per SIMD.
   static constexpr bool SWZ = sizeof(T) == 2 && D == 64;
   static constexpr bool OCC2 = SWZ || (!GRADQ && sizeof(T) == 2) || D == 32;
+  // waves per SIMD: pass 1 in bf16 at d = 64 fits 168 registers (its steady
+  // loop spill-free; a few values spill around the masked blocks and the
+  // epilogue) and runs three, which hides more of each wave's exp and MFMA
+  // latency than two
+  static constexpr int OCC = (!GRADQ && SWZ) ? 3 : OCC2 ? 2 : 1;
   static constexpr int NBUF = 2;                       // stage n in use, stage n+1 arriving
   static constexpr int STAGE = 4 * BK * (SWZ ? D : LDK);  // elements of one stage
   static constexpr size_t LDS_BYTES = NBUF * STAGE * sizeof(T);
@@ -183,7 +188,7 @@ __device__ __forceinline__ void query_chunk(int cc, const f32x16& S, const f32x1
 // product per block against the K^T operand already read; the extra
 // accumulator needs the one-wave-per-SIMD register budget).
 template <typename T, int D, bool GRADQ, bool FIRST, bool SAVED>
-__global__ __launch_bounds__(256, (QueryCfg<T, D, GRADQ>::OCC2 && !FIRST ? 2 : 1)) void query_kernel(
+__global__ __launch_bounds__(256, (FIRST ? 1 : QueryCfg<T, D, GRADQ>::OCC)) void query_kernel(
     const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V, const T* __restrict__ dO,
     const T* __restrict__ gQ, const T* __restrict__ gK, const T* __restrict__ gV, float* __restrict__ lse,
     float* __restrict__ Dv, float* __restrict__ cv, float* __restrict__ rv, void* __restrict__ gradQ,
