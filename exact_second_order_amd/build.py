@@ -3,6 +3,7 @@
 Usage: python -m exact_second_order_amd.build   (or call build()).
 """
 
+import concurrent.futures
 import os
 import subprocess
 import sys
@@ -65,12 +66,14 @@ def build(verbose=False):
     """Compile every object and link libflashbob.so (always rebuilds)."""
     objdir = os.path.join(PKG, "_build")
     os.makedirs(objdir, exist_ok=True)
-    objs = []
-    for i, (src, extra) in enumerate(OBJECTS):
-        obj = os.path.join(objdir, f"{i}_{os.path.splitext(src)[0]}.o")
-        _run([hipcc(), *HIPCC_FLAGS, *extra, "-I", INCLUDE, "-I", CSRC, "-c", os.path.join(CSRC, src),
-              "-o", obj], verbose)
-        objs.append(obj)
+    objs = [os.path.join(objdir, f"{i}_{os.path.splitext(src)[0]}.o") for i, (src, _) in enumerate(OBJECTS)]
+    cmds = [[hipcc(), *HIPCC_FLAGS, *extra, "-I", INCLUDE, "-I", CSRC, "-c", os.path.join(CSRC, src), "-o", obj]
+            for (src, extra), obj in zip(OBJECTS, objs)]
+    # the objects compile independently: one hipcc per object, a few at a time
+    workers = max(1, min(len(cmds), os.cpu_count() or 1, 4))
+    with concurrent.futures.ThreadPoolExecutor(workers) as pool:
+        for f in [pool.submit(_run, c, verbose) for c in cmds]:
+            f.result()
     tmp = LIB + ".tmp"
     _run([hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp], verbose)
     os.replace(tmp, LIB)

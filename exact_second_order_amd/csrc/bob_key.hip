@@ -438,6 +438,7 @@ hipError_t launch_key(const void* Q, const void* K, const void* V, const void* d
   FLASHBOB_INST_KEY(bf16, 64, F)  \
   FLASHBOB_INST_KEY(bf16, 96, F)  \
   FLASHBOB_INST_KEY(bf16, 128, F) \
+  FLASHBOB_INST_KEY(bf16, 256, F) \
   FLASHBOB_INST_KEY(float, 32, F) \
   FLASHBOB_INST_KEY(float, 64, F) \
   FLASHBOB_INST_KEY(float, 96, F) \

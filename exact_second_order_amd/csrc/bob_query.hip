@@ -518,6 +518,7 @@ hipError_t launch_query(const void* Q, const void* K, const void* V, const void*
   FLASHBOB_INST_QUERY(bf16, 64, G, F, S)   \
   FLASHBOB_INST_QUERY(bf16, 96, G, F, S)   \
   FLASHBOB_INST_QUERY(bf16, 128, G, F, S)  \
+  FLASHBOB_INST_QUERY(bf16, 256, G, F, S)  \
   FLASHBOB_INST_QUERY(float, 32, G, F, S)  \
   FLASHBOB_INST_QUERY(float, 64, G, F, S)  \
   FLASHBOB_INST_QUERY(float, 96, G, F, S)  \

@@ -45,7 +45,9 @@ bool overlaps(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi; }
 // Shared validation. On success fills the element count of one tensor.
 int check_common(const void* const* ins, int B, int H, int N, int d, float scale, int dtype, size_t* numel) {
   if (B < 0 || H < 0 || N < 0) return FLASHBOB_ERR_SHAPE;
-  if (d != 32 && d != 64 && d != 96 && d != 128) return FLASHBOB_ERR_UNSUPPORTED_D;
+  // d = 256 in bf16 only: an fp32 stage at d = 256 needs more than the 160 KB of LDS
+  if (d != 32 && d != 64 && d != 96 && d != 128 && !(d == 256 && dtype == FLASHBOB_BF16))
+    return FLASHBOB_ERR_UNSUPPORTED_D;
   if (dtype != FLASHBOB_F32 && dtype != FLASHBOB_BF16) return FLASHBOB_ERR_DTYPE;
   if (!std::isfinite(scale)) return FLASHBOB_ERR_SCALE;
   // B*H*N*d < 2^62 (fits every index computed in size_t) and B*H*N < 2^31
@@ -159,6 +161,9 @@ hipError_t on_type_and_dim(int dtype, int d, Fn&& f) {
       case 32: return f(t, DimTag<32>{});
       case 64: return f(t, DimTag<64>{});
       case 96: return f(t, DimTag<96>{});
+      case 256:
+        if constexpr (std::is_same_v<typename decltype(t)::type, __bf16>) return f(t, DimTag<256>{});
+        else return hipErrorInvalidValue;  // refused by the argument checks
       default: return f(t, DimTag<128>{});
     }
   };
@@ -342,7 +347,7 @@ const char* flashbob_strerror(int code) {
     case FLASHBOB_OK: return "ok";
     case FLASHBOB_ERR_NULL: return "a required pointer is NULL";
     case FLASHBOB_ERR_SHAPE: return "invalid shape (negative size or too many elements)";
-    case FLASHBOB_ERR_UNSUPPORTED_D: return "unsupported head dimension (d must be 32, 64, 96 or 128)";
+    case FLASHBOB_ERR_UNSUPPORTED_D: return "unsupported head dimension (d must be 32, 64, 96 or 128, or 256 with bf16 inputs)";
     case FLASHBOB_ERR_UNSUPPORTED_N: return "unsupported sequence length";
     case FLASHBOB_ERR_DTYPE: return "unknown dtype";
     case FLASHBOB_ERR_ALIGN: return "a pointer is not 16-byte aligned";

@@ -30,7 +30,8 @@
  *     asynchronously; no host synchronisation happens inside the call and the
  *     library keeps no state between calls, so calls on different streams
  *     with disjoint buffers may run concurrently.
- *   - Supported: d in {32, 64, 96, 128}; N >= 1 (any length, ragged tails masked);
+ *   - Supported: d in {32, 64, 96, 128}, and d = 256 with FLASHBOB_BF16 inputs;
+ *     N >= 1 (any length, ragged tails masked);
  *     B, H >= 0 (B*H*N == 0 is a no-op returning FLASHBOB_OK);
  *     B*H*N*d < 2^62; dtype FLASHBOB_F32 or FLASHBOB_BF16.
  *   - Errors are negative return codes. Every argument check runs before any
@@ -56,7 +57,7 @@ enum {
   FLASHBOB_OK = 0,
   FLASHBOB_ERR_NULL = -1,           /* a required pointer is NULL */
   FLASHBOB_ERR_SHAPE = -2,          /* negative size, or B*H*N*d too large */
-  FLASHBOB_ERR_UNSUPPORTED_D = -3,  /* d not in {32, 64, 96, 128} */
+  FLASHBOB_ERR_UNSUPPORTED_D = -3,  /* d not in {32, 64, 96, 128} (or 256 with bf16 inputs) */
   FLASHBOB_ERR_UNSUPPORTED_N = -4,  /* reserved (no N is rejected today besides N < 0) */
   FLASHBOB_ERR_DTYPE = -5,          /* unknown dtype */
   FLASHBOB_ERR_ALIGN = -6,          /* a pointer is not 16-byte aligned */

@@ -76,6 +76,13 @@ def test_rejects_unsupported_d(d):
     assert call(*a) == UD
 
 
+def test_head_dim_256_bf16_only():
+    # bf16 at d = 256 passes the head-dim check (and stops at the missing
+    # workspace); fp32 at d = 256 is refused
+    assert call(*fake_args(d=256, dtype=BF16, ws=0)) == WS
+    assert call(*fake_args(d=256, dtype=F32, ws=0)) == UD
+
+
 def test_rejects_negative_sizes_and_overflow():
     for idx in (2, 3, 4):
         a = list(fake_args())
