@@ -188,7 +188,14 @@ __global__ __launch_bounds__(256, (KeyCfg<T, D, FIRST>::OCC2 ? 2 : 1)) void key_
   // (KLDS members) this wave's LDS tiles, which keeps the kernel within its
   // register budget
   constexpr int KLDS = Cfg::KLDS;
-  F bK[(KLDS & 1) ? 1 : NCH], bgK[(KLDS & 2) ? 1 : NCH], bV[(KLDS & 4) ? 1 : NCH], bgV[(KLDS & 8) ? 1 : NCH];
+  // STREAM (d >= 256, where the four key-side tensors would take 256
+  // registers on top of the d-wide accumulators): every key-side operand is
+  // re-read from global memory (L1/L2) per block instead; a lane past the end
+  // reads the last key row (its P is masked to zero, its outputs not stored)
+  constexpr bool STREAM = D >= 256;
+  constexpr int KREG = STREAM ? 0xf : KLDS;  // tensors not held in registers
+  const size_t ro_any = hoff + (size_t)min(key, N - 1) * D;
+  F bK[(KREG & 1) ? 1 : NCH], bgK[(KREG & 2) ? 1 : NCH], bV[(KREG & 4) ? 1 : NCH], bgV[(KREG & 8) ? 1 : NCH];
   {
     const int k0w = kblk * Cfg::BC + 32 * w;
     const int nkw = max(1, min(32, N - k0w));  // waves wholly past the end copy row N-1 (masked)
@@ -203,18 +210,23 @@ __global__ __launch_bounds__(256, (KeyCfg<T, D, FIRST>::OCC2 ? 2 : 1)) void key_
     }
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
-      if constexpr (!(KLDS & 1)) bK[c] = load_key_frag(K + ro, kvalid, c);
-      if constexpr (!(KLDS & 2)) bgK[c] = load_key_frag(gK + ro, kvalid, c);
-      if constexpr (!(KLDS & 4)) bV[c] = load_key_frag(V + ro, kvalid, c);
-      if constexpr (!(KLDS & 8)) bgV[c] = load_key_frag(gV + ro, kvalid, c);
+      if constexpr (!(KREG & 1)) bK[c] = load_key_frag(K + ro, kvalid, c);
+      if constexpr (!(KREG & 2)) bgK[c] = load_key_frag(gK + ro, kvalid, c);
+      if constexpr (!(KREG & 4)) bV[c] = load_key_frag(V + ro, kvalid, c);
+      if constexpr (!(KREG & 8)) bgV[c] = load_key_frag(gV + ro, kvalid, c);
     }
   }
-  auto keyop = [&](int t, int c) __attribute__((always_inline)) -> F {
-    if constexpr (SWZ) {
-      if (KLDS & (1 << t)) return ld_rows_sw(ktile(t), 0, c);
+  // kr: the streamed key row offset (STREAM), made opaque once per block
+  auto keyop = [&](int t, int c, size_t kr) __attribute__((always_inline)) -> F {
+    if constexpr (STREAM) {
+      return load_frag_any((t == 0 ? K : t == 1 ? gK : t == 2 ? V : gV) + kr, c);
+    } else {
+      if constexpr (SWZ) {
+        if (KLDS & (1 << t)) return ld_rows_sw(ktile(t), 0, c);
+      }
+      return t == 0 ? bK[(KLDS & 1) ? 0 : c]
+                    : t == 1 ? bgK[(KLDS & 2) ? 0 : c] : t == 2 ? bV[(KLDS & 4) ? 0 : c] : bgV[(KLDS & 8) ? 0 : c];
     }
-    return t == 0 ? bK[(KLDS & 1) ? 0 : c]
-                  : t == 1 ? bgK[(KLDS & 2) ? 0 : c] : t == 2 ? bV[(KLDS & 4) ? 0 : c] : bgV[(KLDS & 8) ? 0 : c];
   };
   // gradK^T, gradV^T: d rows x the wave's 32 keys
   f32x16 accK[NDB], accV[NDB], accdK[FIRST ? NDB : 1], accdV[FIRST ? NDB : 1];
@@ -287,17 +299,18 @@ __global__ __launch_bounds__(256, (KeyCfg<T, D, FIRST>::OCC2 ? 2 : 1)) void key_
       t.G = rows_as_acc(sS(b, 2));
       t.H = rows_as_acc(sS(b, 3));
     }
+    const size_t kr = STREAM ? opaque(ro_any) : 0;
 #pragma unroll
     for (int c = c0; c < c1; ++c) {
       const F aq = lds_rows(b, 0, c);  // lane <-> query, k over d
       const F agq = lds_rows(b, 1, c);
       const F ado = lds_rows(b, 2, c);
-      const F k = keyop(0, c);
+      const F k = keyop(0, c, kr);
       E::mma(t.S, aq, k);
       E::mma(t.G, agq, k);
-      E::mma(t.G, aq, keyop(1, c));
-      E::mma(t.dP, ado, keyop(2, c));
-      E::mma(t.H, ado, keyop(3, c));
+      E::mma(t.G, aq, keyop(1, c, kr));
+      E::mma(t.dP, ado, keyop(2, c, kr));
+      E::mma(t.H, ado, keyop(3, c, kr));
     }
   };
   struct Frags {

@@ -227,28 +227,35 @@ __global__ __launch_bounds__(256, (FIRST ? 1 : QueryCfg<T, D, GRADQ>::OCC)) void
   const bool qvalid = q < N;
   const int qlim = causal ? min(N, q + 1) : N;    // keys [0, qlim) are visible to it
 
-  // B operands of the wave's 32 queries (lane <-> query, k over d)
-  F fQ[NCH], fgQ[NCH], fdO[NCH];
-  {
-    const T* rq = Q + hoff + (size_t)q * D;
-    const T* rgq = gQ + hoff + (size_t)q * D;
-    const T* rdo = dO + hoff + (size_t)q * D;
+  // B operands of the wave's 32 queries (lane <-> query, k over d), held in
+  // registers for the sweep; STREAM (pass 2q at d >= 256, where they would take
+  // 192 registers on top of the d-wide accumulators) re-reads them from global
+  // memory (L1/L2) per block instead
+  constexpr bool STREAM = GRADQ && D >= 256;
+  const size_t qrow = hoff + (size_t)q * D;
+  // (a streaming lane past the end reads the last row: its P is zero through
+  // its infinite log-sum-exp and its outputs are not stored)
+  const size_t qrow_any = hoff + (size_t)min(q, N - 1) * D;
+  F fQ[STREAM ? 1 : NCH], fgQ[STREAM ? 1 : NCH], fdO[STREAM ? 1 : NCH];
+  if constexpr (!STREAM) {
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
-      fQ[c] = load_row_frag(rq, qvalid, c);
-      fgQ[c] = load_row_frag(rgq, qvalid, c);
-      fdO[c] = load_row_frag(rdo, qvalid, c);
+      fQ[c] = load_row_frag(Q + qrow, qvalid, c);
+      fgQ[c] = load_row_frag(gQ + qrow, qvalid, c);
+      fdO[c] = load_row_frag(dO + qrow, qvalid, c);
     }
   }
 
   // Pass 1 works with |scale|: for a negative scale it negates Q and gQ, which
   // leaves s S and s G unchanged and lets the online maximum be taken on S.
   const float sgn = (!GRADQ && scale < 0.f) ? -1.f : 1.f;
-  if (sgn < 0.f) {
+  if constexpr (!STREAM) {
+    if (sgn < 0.f) {
 #pragma unroll
-    for (int c = 0; c < NCH; ++c) {
-      negate(fQ[c]);
-      negate(fgQ[c]);
+      for (int c = 0; c < NCH; ++c) {
+        negate(fQ[c]);
+        negate(fgQ[c]);
+      }
     }
   }
   scale *= sgn;
@@ -328,17 +335,21 @@ __global__ __launch_bounds__(256, (FIRST ? 1 : QueryCfg<T, D, GRADQ>::OCC)) void
       t.dP = f32x16{};
       t.H = f32x16{};
     }
+    const size_t qr = STREAM ? opaque(qrow_any) : qrow;
 #pragma unroll
     for (int c = c0; c < c1; ++c) {
       const F ak = lds_rows(b, 0, 0, c);  // lane <-> key, k over d
       const F agk = lds_rows(b, 1, 0, c);
       const F av = lds_rows(b, 2, 0, c);
       const F agv = lds_rows(b, 3, 0, c);
-      E::mma(t.S, ak, fQ[c]);
-      E::mma(t.G, ak, fgQ[c]);
-      E::mma(t.G, agk, fQ[c]);
-      E::mma(t.dP, av, fdO[c]);
-      E::mma(t.H, agv, fdO[c]);
+      const F bq = STREAM ? load_frag_any(Q + qr, c) : fQ[STREAM ? 0 : c];
+      const F bgq = STREAM ? load_frag_any(gQ + qr, c) : fgQ[STREAM ? 0 : c];
+      const F bdo = STREAM ? load_frag_any(dO + qr, c) : fdO[STREAM ? 0 : c];
+      E::mma(t.S, ak, bq);
+      E::mma(t.G, ak, bgq);
+      E::mma(t.G, agk, bq);
+      E::mma(t.dP, av, bdo);
+      E::mma(t.H, agv, bdo);
     }
   };
   struct Frags {
