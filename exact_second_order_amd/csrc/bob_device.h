@@ -252,27 +252,6 @@ __device__ __forceinline__ void negate(f32x8& f) {
   f = __builtin_bit_cast(f32x8, __builtin_bit_cast(u32x8, f) ^ 0x80000000u);
 }
 
-// One fragment (16 k values) of a row held by this lane, loaded without a
-// validity test (the caller points invalid lanes at a real row and masks
-// their results), so a loop body that streams it stays one basic block.
-__device__ __forceinline__ bf16x8 load_frag_any(const bf16* row, int c) {
-  return *reinterpret_cast<const bf16x8*>(row + 16 * c + 8 * (lane_id() >> 5));
-}
-__device__ __forceinline__ f32x8 load_frag_any(const float* row, int c) {
-  const int h = lane_id() >> 5;
-  f32x8 f;
-#pragma unroll
-  for (int s = 0; s < 8; ++s) f[s] = row[16 * c + Elem<float>::kmap(h, s)];
-  return f;
-}
-
-// The same value, opaque to the optimiser: loads addressed through it are
-// issued where they are used instead of being hoisted out of the loop.
-__device__ __forceinline__ size_t opaque(size_t x) {
-  asm volatile("" : "+v"(x));
-  return x;
-}
-
 // Wait for this wave's outstanding global loads, including direct-to-LDS ones.
 __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 

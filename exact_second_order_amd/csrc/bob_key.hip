@@ -37,6 +37,12 @@ struct KeyCfg {
   static constexpr int BQ = 32;                        // queries per LDS stage (one MFMA block)
   static constexpr int LDQ = D + 16 / (int)sizeof(T);  // padded LDS row (elements)
   static constexpr int NCH = D / 16, NDB = D / 32;
+  // d >= 256: each key block is handled by OSPLIT workgroups, each
+  // accumulating its own share of gradK, gradV's columns (the score tiles are
+  // recomputed by each), so the key-side operands stay in registers beside
+  // accumulators for only part of d
+  static constexpr int OSPLIT = D >= 256 ? 4 : 1;
+  static constexpr int NDBO = NDB / OSPLIT;  // 32-row blocks of d per workgroup
   // same staging choices as the query-major kernel; two waves per SIMD for
   // bf16 d = 64 and for d = 32 (FIRST: the first-backward dK, dV accumulators
   // need the one-wave budget)
@@ -166,9 +172,14 @@ __global__ __launch_bounds__(256, (KeyCfg<T, D, FIRST>::OCC2 ? 2 : 1)) void key_
 
   // causal: the longest sweeps (the first key blocks) start first, across all
   // key/value heads at once
-  const int nheads = (int)(gridDim.x / nkblk);
-  const int head = causal ? (int)(blockIdx.x % nheads) : (int)(blockIdx.x / nkblk);
-  const int kblk = causal ? (int)(blockIdx.x / nheads) : (int)(blockIdx.x % nkblk);
+  // (OSPLIT: consecutive workgroups share a key block and split its output
+  // columns; part = which share)
+  constexpr int OSPLIT = Cfg::OSPLIT, NDBO = Cfg::NDBO;
+  const int part = OSPLIT > 1 ? (int)(blockIdx.x % OSPLIT) : 0;
+  const unsigned bid = OSPLIT > 1 ? blockIdx.x / OSPLIT : blockIdx.x;
+  const int nheads = (int)((OSPLIT > 1 ? gridDim.x / OSPLIT : gridDim.x) / nkblk);
+  const int head = causal ? (int)(bid % nheads) : (int)(bid / nkblk);
+  const int kblk = causal ? (int)(bid / nheads) : (int)(bid % nkblk);
   // key/value head `head`; the query heads of its group are head * G + g
   const size_t hoff = (size_t)head * N * D;
   size_t qoff = 0, soff = 0;  // query head of the current group member
@@ -188,14 +199,7 @@ __global__ __launch_bounds__(256, (KeyCfg<T, D, FIRST>::OCC2 ? 2 : 1)) void key_
   // (KLDS members) this wave's LDS tiles, which keeps the kernel within its
   // register budget
   constexpr int KLDS = Cfg::KLDS;
-  // STREAM (d >= 256, where the four key-side tensors would take 256
-  // registers on top of the d-wide accumulators): every key-side operand is
-  // re-read from global memory (L1/L2) per block instead; a lane past the end
-  // reads the last key row (its P is masked to zero, its outputs not stored)
-  constexpr bool STREAM = D >= 256;
-  constexpr int KREG = STREAM ? 0xf : KLDS;  // tensors not held in registers
-  const size_t ro_any = hoff + (size_t)min(key, N - 1) * D;
-  F bK[(KREG & 1) ? 1 : NCH], bgK[(KREG & 2) ? 1 : NCH], bV[(KREG & 4) ? 1 : NCH], bgV[(KREG & 8) ? 1 : NCH];
+  F bK[(KLDS & 1) ? 1 : NCH], bgK[(KLDS & 2) ? 1 : NCH], bV[(KLDS & 4) ? 1 : NCH], bgV[(KLDS & 8) ? 1 : NCH];
   {
     const int k0w = kblk * Cfg::BC + 32 * w;
     const int nkw = max(1, min(32, N - k0w));  // waves wholly past the end copy row N-1 (masked)
@@ -210,28 +214,23 @@ __global__ __launch_bounds__(256, (KeyCfg<T, D, FIRST>::OCC2 ? 2 : 1)) void key_
     }
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
-      if constexpr (!(KREG & 1)) bK[c] = load_key_frag(K + ro, kvalid, c);
-      if constexpr (!(KREG & 2)) bgK[c] = load_key_frag(gK + ro, kvalid, c);
-      if constexpr (!(KREG & 4)) bV[c] = load_key_frag(V + ro, kvalid, c);
-      if constexpr (!(KREG & 8)) bgV[c] = load_key_frag(gV + ro, kvalid, c);
+      if constexpr (!(KLDS & 1)) bK[c] = load_key_frag(K + ro, kvalid, c);
+      if constexpr (!(KLDS & 2)) bgK[c] = load_key_frag(gK + ro, kvalid, c);
+      if constexpr (!(KLDS & 4)) bV[c] = load_key_frag(V + ro, kvalid, c);
+      if constexpr (!(KLDS & 8)) bgV[c] = load_key_frag(gV + ro, kvalid, c);
     }
   }
-  // kr: the streamed key row offset (STREAM), made opaque once per block
-  auto keyop = [&](int t, int c, size_t kr) __attribute__((always_inline)) -> F {
-    if constexpr (STREAM) {
-      return load_frag_any((t == 0 ? K : t == 1 ? gK : t == 2 ? V : gV) + kr, c);
-    } else {
-      if constexpr (SWZ) {
-        if (KLDS & (1 << t)) return ld_rows_sw(ktile(t), 0, c);
-      }
-      return t == 0 ? bK[(KLDS & 1) ? 0 : c]
-                    : t == 1 ? bgK[(KLDS & 2) ? 0 : c] : t == 2 ? bV[(KLDS & 4) ? 0 : c] : bgV[(KLDS & 8) ? 0 : c];
+  auto keyop = [&](int t, int c) __attribute__((always_inline)) -> F {
+    if constexpr (SWZ) {
+      if (KLDS & (1 << t)) return ld_rows_sw(ktile(t), 0, c);
     }
+    return t == 0 ? bK[(KLDS & 1) ? 0 : c]
+                  : t == 1 ? bgK[(KLDS & 2) ? 0 : c] : t == 2 ? bV[(KLDS & 4) ? 0 : c] : bgV[(KLDS & 8) ? 0 : c];
   };
   // gradK^T, gradV^T: d rows x the wave's 32 keys
-  f32x16 accK[NDB], accV[NDB], accdK[FIRST ? NDB : 1], accdV[FIRST ? NDB : 1];
+  f32x16 accK[NDBO], accV[NDBO], accdK[FIRST ? NDBO : 1], accdV[FIRST ? NDBO : 1];
 #pragma unroll
-  for (int j = 0; j < NDB; ++j) {
+  for (int j = 0; j < NDBO; ++j) {
     accK[j] = f32x16{};
     accV[j] = f32x16{};
     if constexpr (FIRST) {
@@ -299,18 +298,17 @@ __global__ __launch_bounds__(256, (KeyCfg<T, D, FIRST>::OCC2 ? 2 : 1)) void key_
       t.G = rows_as_acc(sS(b, 2));
       t.H = rows_as_acc(sS(b, 3));
     }
-    const size_t kr = STREAM ? opaque(ro_any) : 0;
 #pragma unroll
     for (int c = c0; c < c1; ++c) {
       const F aq = lds_rows(b, 0, c);  // lane <-> query, k over d
       const F agq = lds_rows(b, 1, c);
       const F ado = lds_rows(b, 2, c);
-      const F k = keyop(0, c, kr);
+      const F k = keyop(0, c);
       E::mma(t.S, aq, k);
       E::mma(t.G, agq, k);
-      E::mma(t.G, aq, keyop(1, c, kr));
-      E::mma(t.dP, ado, keyop(2, c, kr));
-      E::mma(t.H, ado, keyop(3, c, kr));
+      E::mma(t.G, aq, keyop(1, c));
+      E::mma(t.dP, ado, keyop(2, c));
+      E::mma(t.H, ado, keyop(3, c));
     }
   };
   struct Frags {
@@ -327,11 +325,13 @@ __global__ __launch_bounds__(256, (KeyCfg<T, D, FIRST>::OCC2 ? 2 : 1)) void key_
   auto outputs = [&](int n, int cc, const Frags& f) __attribute__((always_inline)) {
     const int b = n & (NBUF - 1);
 #pragma unroll
-    for (int j = 0; j < NDB; ++j) {
-      // lane <-> d, k over this chunk's queries (accumulator row order)
-      const F tQ = lds_cols(b, 0, 16 * cc, 32 * j);
-      const F tgQ = lds_cols(b, 1, 16 * cc, 32 * j);
-      const F tdO = lds_cols(b, 2, 16 * cc, 32 * j);
+    for (int j = 0; j < NDBO; ++j) {
+      // lane <-> d, k over this chunk's queries (accumulator row order); this
+      // workgroup's share of the columns starts at block part * NDBO
+      const int jd = 32 * (part * NDBO + j);
+      const F tQ = lds_cols(b, 0, 16 * cc, jd);
+      const F tgQ = lds_cols(b, 1, 16 * cc, jd);
+      const F tdO = lds_cols(b, 2, 16 * cc, jd);
       E::mma(accK[j], tQ, f.dS2[cc]);
       E::mma(accK[j], tgQ, f.dS[cc]);
       E::mma(accV[j], tdO, f.A[cc]);
@@ -405,10 +405,10 @@ __global__ __launch_bounds__(256, (KeyCfg<T, D, FIRST>::OCC2 ? 2 : 1)) void key_
   if (kvalid) {
     const size_t row = hoff + (size_t)key * D;
 #pragma unroll
-    for (int j = 0; j < NDB; ++j) {
+    for (int j = 0; j < NDBO; ++j) {
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        const int d0 = 32 * j + 8 * g + 4 * h;
+        const int d0 = 32 * (part * NDBO + j) + 8 * g + 4 * h;
         const f32x16& a = accK[j];
         const f32x16& v = accV[j];
         store_out4(gradK, row + d0, scale * a[4 * g], scale * a[4 * g + 1], scale * a[4 * g + 2],
@@ -433,7 +433,7 @@ hipError_t launch_key(const void* Q, const void* K, const void* V, const void* d
                       int G, int out_bf16, hipStream_t stream) {
   using Cfg = KeyCfg<T, D, FIRST>;
   const int nkblk = (N + Cfg::BC - 1) / Cfg::BC;
-  const long long nblocks = (long long)nkblk * BHkv;
+  const long long nblocks = (long long)nkblk * BHkv * Cfg::OSPLIT;
   if (nblocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   key_kernel<T, D, FIRST><<<dim3((unsigned)nblocks), dim3(256), 0, stream>>>(
       (const T*)Q, (const T*)K, (const T*)V, (const T*)dO, (const T*)gQ, (const T*)gK, (const T*)gV, lse2, Dv, cv,

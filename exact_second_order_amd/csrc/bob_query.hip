@@ -47,6 +47,12 @@ struct QueryCfg {
   static constexpr int LDK = D + 16 / (int)sizeof(T);  // padded LDS row (elements)
   static constexpr int NCH = D / 16;                   // 16-wide k chunks over d
   static constexpr int NDB = D / 32;                   // 32-row blocks of d
+  // pass 2q at d >= 256: each query block is handled by OSPLIT workgroups,
+  // each accumulating its own share of the output columns (the score tiles
+  // are recomputed by each), so the d-wide operands stay in registers beside
+  // accumulators for only part of d
+  static constexpr int OSPLIT = (GRADQ && D >= 256) ? 2 : 1;
+  static constexpr int NDBO = NDB / OSPLIT;            // 32-row blocks of d per workgroup
   // bf16 d = 64 stages tiles with direct global->LDS loads into swizzled
   // unpadded rows (no staging registers); the other variants stage through
   // registers into padded rows. Two waves per SIMD (<= 256 registers: the
@@ -217,9 +223,14 @@ __global__ __launch_bounds__(256, (FIRST ? 1 : QueryCfg<T, D, GRADQ>::OCC)) void
   // causal: the longest sweeps (the last query blocks) start first, across
   // all heads at once (consecutive workgroups take the same block of
   // successive heads)
-  const int nheads = (int)(gridDim.x / nqblk);
-  const int head = causal ? (int)(blockIdx.x % nheads) : (int)(blockIdx.x / nqblk);
-  const int qblk = causal ? nqblk - 1 - (int)(blockIdx.x / nheads) : (int)(blockIdx.x % nqblk);
+  // (OSPLIT: consecutive workgroups share a query block and split its output
+  // columns; part = which share)
+  constexpr int OSPLIT = Cfg::OSPLIT, NDBO = Cfg::NDBO;
+  const int part = OSPLIT > 1 ? (int)(blockIdx.x % OSPLIT) : 0;
+  const unsigned bid = OSPLIT > 1 ? blockIdx.x / OSPLIT : blockIdx.x;
+  const int nheads = (int)((OSPLIT > 1 ? gridDim.x / OSPLIT : gridDim.x) / nqblk);
+  const int head = causal ? (int)(bid % nheads) : (int)(bid / nqblk);
+  const int qblk = causal ? nqblk - 1 - (int)(bid / nheads) : (int)(bid % nqblk);
   const size_t hoff = (size_t)head * N * D;         // query head (Q, dO, gQ, outputs)
   const size_t koff = (size_t)(head / G) * N * D;   // its key/value head (groups of G)
   const int w = wave_id(), l = lane_id(), h = l >> 5, col = l & 31;
@@ -227,35 +238,28 @@ __global__ __launch_bounds__(256, (FIRST ? 1 : QueryCfg<T, D, GRADQ>::OCC)) void
   const bool qvalid = q < N;
   const int qlim = causal ? min(N, q + 1) : N;    // keys [0, qlim) are visible to it
 
-  // B operands of the wave's 32 queries (lane <-> query, k over d), held in
-  // registers for the sweep; STREAM (pass 2q at d >= 256, where they would take
-  // 192 registers on top of the d-wide accumulators) re-reads them from global
-  // memory (L1/L2) per block instead
-  constexpr bool STREAM = GRADQ && D >= 256;
-  const size_t qrow = hoff + (size_t)q * D;
-  // (a streaming lane past the end reads the last row: its P is zero through
-  // its infinite log-sum-exp and its outputs are not stored)
-  const size_t qrow_any = hoff + (size_t)min(q, N - 1) * D;
-  F fQ[STREAM ? 1 : NCH], fgQ[STREAM ? 1 : NCH], fdO[STREAM ? 1 : NCH];
-  if constexpr (!STREAM) {
+  // B operands of the wave's 32 queries (lane <-> query, k over d)
+  F fQ[NCH], fgQ[NCH], fdO[NCH];
+  {
+    const T* rq = Q + hoff + (size_t)q * D;
+    const T* rgq = gQ + hoff + (size_t)q * D;
+    const T* rdo = dO + hoff + (size_t)q * D;
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
-      fQ[c] = load_row_frag(Q + qrow, qvalid, c);
-      fgQ[c] = load_row_frag(gQ + qrow, qvalid, c);
-      fdO[c] = load_row_frag(dO + qrow, qvalid, c);
+      fQ[c] = load_row_frag(rq, qvalid, c);
+      fgQ[c] = load_row_frag(rgq, qvalid, c);
+      fdO[c] = load_row_frag(rdo, qvalid, c);
     }
   }
 
   // Pass 1 works with |scale|: for a negative scale it negates Q and gQ, which
   // leaves s S and s G unchanged and lets the online maximum be taken on S.
   const float sgn = (!GRADQ && scale < 0.f) ? -1.f : 1.f;
-  if constexpr (!STREAM) {
-    if (sgn < 0.f) {
+  if (sgn < 0.f) {
 #pragma unroll
-      for (int c = 0; c < NCH; ++c) {
-        negate(fQ[c]);
-        negate(fgQ[c]);
-      }
+    for (int c = 0; c < NCH; ++c) {
+      negate(fQ[c]);
+      negate(fgQ[c]);
     }
   }
   scale *= sgn;
@@ -272,7 +276,7 @@ __global__ __launch_bounds__(256, (FIRST ? 1 : QueryCfg<T, D, GRADQ>::OCC)) void
   // (gradQ^T, graddO^T: d rows x the wave's 32 queries)
   // (pass-2 form: LSE * log2(e), -D, -c, -r)
   float l2 = INFINITY, Dq = 0.f, cq = 0.f, rq = 0.f;
-  f32x16 accQ[GRADQ ? NDB : 1], accO[GRADQ ? NDB : 1], accdQ[FIRST ? NDB : 1];
+  f32x16 accQ[GRADQ ? NDBO : 1], accO[GRADQ ? NDBO : 1], accdQ[FIRST ? NDBO : 1];
   if constexpr (GRADQ) {
     if (qvalid) {
       const size_t o = (size_t)head * N + q;
@@ -282,7 +286,7 @@ __global__ __launch_bounds__(256, (FIRST ? 1 : QueryCfg<T, D, GRADQ>::OCC)) void
       rq = rv[o];
     }
 #pragma unroll
-    for (int j = 0; j < NDB; ++j) {
+    for (int j = 0; j < NDBO; ++j) {
       accQ[j] = f32x16{};
       accO[j] = f32x16{};
       if constexpr (FIRST) accdQ[j] = f32x16{};
@@ -335,21 +339,17 @@ __global__ __launch_bounds__(256, (FIRST ? 1 : QueryCfg<T, D, GRADQ>::OCC)) void
       t.dP = f32x16{};
       t.H = f32x16{};
     }
-    const size_t qr = STREAM ? opaque(qrow_any) : qrow;
 #pragma unroll
     for (int c = c0; c < c1; ++c) {
       const F ak = lds_rows(b, 0, 0, c);  // lane <-> key, k over d
       const F agk = lds_rows(b, 1, 0, c);
       const F av = lds_rows(b, 2, 0, c);
       const F agv = lds_rows(b, 3, 0, c);
-      const F bq = STREAM ? load_frag_any(Q + qr, c) : fQ[STREAM ? 0 : c];
-      const F bgq = STREAM ? load_frag_any(gQ + qr, c) : fgQ[STREAM ? 0 : c];
-      const F bdo = STREAM ? load_frag_any(dO + qr, c) : fdO[STREAM ? 0 : c];
-      E::mma(t.S, ak, bq);
-      E::mma(t.G, ak, bgq);
-      E::mma(t.G, agk, bq);
-      E::mma(t.dP, av, bdo);
-      E::mma(t.H, agv, bdo);
+      E::mma(t.S, ak, fQ[c]);
+      E::mma(t.G, ak, fgQ[c]);
+      E::mma(t.G, agk, fQ[c]);
+      E::mma(t.dP, av, fdO[c]);
+      E::mma(t.H, agv, fdO[c]);
     }
   };
   struct Frags {
@@ -371,12 +371,14 @@ __global__ __launch_bounds__(256, (FIRST ? 1 : QueryCfg<T, D, GRADQ>::OCC)) void
     if constexpr (GRADQ) {
       const int b = n & (NBUF - 1);
 #pragma unroll
-      for (int j = 0; j < NDB; ++j) {
-        // lane <-> d, k over this chunk's keys (accumulator row order)
-        const F tK = lds_cols(b, 0, 16 * cc, 32 * j);
-        const F tgK = lds_cols(b, 1, 16 * cc, 32 * j);
-        const F tV = lds_cols(b, 2, 16 * cc, 32 * j);
-        const F tgV = lds_cols(b, 3, 16 * cc, 32 * j);
+      for (int j = 0; j < NDBO; ++j) {
+        // lane <-> d, k over this chunk's keys (accumulator row order); this
+        // workgroup's share of the columns starts at block part * NDBO
+        const int jd = 32 * (part * NDBO + j);
+        const F tK = lds_cols(b, 0, 16 * cc, jd);
+        const F tgK = lds_cols(b, 1, 16 * cc, jd);
+        const F tV = lds_cols(b, 2, 16 * cc, jd);
+        const F tgV = lds_cols(b, 3, 16 * cc, jd);
         E::mma(accQ[j], tK, f.dS2[cc]);
         E::mma(accQ[j], tgK, f.dS[cc]);
         E::mma(accO[j], tV, f.A[cc]);
@@ -480,10 +482,10 @@ __global__ __launch_bounds__(256, (FIRST ? 1 : QueryCfg<T, D, GRADQ>::OCC)) void
     if (qvalid) {
       const size_t row = hoff + (size_t)q * D;
 #pragma unroll
-      for (int j = 0; j < NDB; ++j) {
+      for (int j = 0; j < NDBO; ++j) {
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-          const int d0 = 32 * j + 8 * g + 4 * h;
+          const int d0 = 32 * (part * NDBO + j) + 8 * g + 4 * h;
           const f32x16& a = accQ[j];
           const f32x16& o = accO[j];
           store_out4(gradQ, row + d0, scale * a[4 * g], scale * a[4 * g + 1], scale * a[4 * g + 2],
@@ -507,7 +509,7 @@ hipError_t launch_query(const void* Q, const void* K, const void* V, const void*
                         int lse_natural, int causal, int G, int out_bf16, hipStream_t stream) {
   using Cfg = QueryCfg<T, D, GRADQ>;
   const int nqblk = (N + Cfg::BQ - 1) / Cfg::BQ;
-  const long long nblocks = (long long)nqblk * BH;
+  const long long nblocks = (long long)nqblk * BH * Cfg::OSPLIT;
   if (nblocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   query_kernel<T, D, GRADQ, FIRST, SAVED><<<dim3((unsigned)nblocks), dim3(256), 0, stream>>>(
       (const T*)Q, (const T*)K, (const T*)V, (const T*)dO, (const T*)gQ, (const T*)gK, (const T*)gV, lse, Dv,
