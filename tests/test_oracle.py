@@ -11,7 +11,8 @@ Independent routes used:
   * central finite differences of the scalar objective;
   * forward-mode JVP of attention (graddO is the JVP along the cotangents);
   * second derivatives of the forward along a line (quadratic form);
-  * torch's scaled_dot_product_attention backward (special case gQ = gK = 0);
+  * torch's scaled_dot_product_attention backward (special case gQ = gK = 0)
+    and forward (the attention the oracle differentiates, plain and causal);
   * identities the mathematics fixes: Hessian symmetry, Euler identity,
     bilinearity, zero cotangents, N = 1, key-shift invariance.
 """
@@ -603,3 +604,75 @@ def test_oracle_matches_symbolic_differentiation(case):
         h = [x[k][0, 0] for k in ("Q", "K", "V", "dO", "gQ", "gK", "gV")]
         L = oracle.bob_objective(*h, s, causal=causal)
         assert abs(L - float(case["objective"])) <= 1e-12 * max(1.0, abs(float(case["objective"])))
+
+
+# ----------------------------------------------------------------------------
+# the attention forward itself (the function whose derivatives BoB takes)
+
+
+@pytest.mark.parametrize("N,d", SHAPES)
+@pytest.mark.parametrize("causal", [False, True])
+def test_attention_forward_matches_sdpa(N, d, causal):
+    """oracle.attention_forward against torch's scaled_dot_product_attention in
+    float64 (a library routine for the same definition, softmax(s Q K^T) V)."""
+    Q, K, V = rand_inputs(N, d, seed=31 + N + d)[:3]
+    s = 0.7 / math.sqrt(d)
+    t = [torch.tensor(x)[None, None] for x in (Q, K, V)]
+    ref = torch.nn.functional.scaled_dot_product_attention(*t, is_causal=causal, scale=s)[0, 0].numpy()
+    assert rel(oracle.attention_forward(Q, K, V, s, causal=causal), ref) < 1e-13
+
+
+def test_attention_forward_closed_forms():
+    """Special cases with answers that need no library: one key returns V;
+    Q = 0 makes every score equal, so each row averages the values it sees
+    (all rows plainly, rows 0..i causally); a large scale turns the softmax
+    into a selection of the best-matching key."""
+    rng = np.random.default_rng(5)
+    d = 6
+    K1, V1 = rng.standard_normal((1, d)), rng.standard_normal((1, d))
+    Q1 = rng.standard_normal((1, d))
+    assert np.allclose(oracle.attention_forward(Q1, K1, V1, 0.3), V1, rtol=0, atol=1e-15)
+    N = 7
+    K, V = rng.standard_normal((N, d)), rng.standard_normal((N, d))
+    Z = np.zeros((N, d))
+    assert np.allclose(oracle.attention_forward(Z, K, V, 0.5), np.tile(V.mean(axis=0), (N, 1)), atol=1e-14)
+    running = np.cumsum(V, axis=0) / np.arange(1, N + 1)[:, None]
+    assert np.allclose(oracle.attention_forward(Z, K, V, 0.5, causal=True), running, atol=1e-14)
+    # orthogonal keys, each query a multiple of one key: the selection is exact
+    # up to exp(-scale * gap) ~ 1e-43
+    Kd = np.eye(N, d) * 3.0
+    perm = np.array([3, 0, 5, 1, 4, 2, 0])
+    Qs = Kd[perm] if d >= N else None
+    if Qs is not None:
+        got = oracle.attention_forward(Qs, Kd, V, 100.0)
+        assert np.allclose(got, V[perm], atol=1e-12)
+
+
+@pytest.mark.parametrize("variant", ["softmax_over_queries", "no_mask", "mask_off_by_one", "V_rows_permuted"])
+def test_attention_forward_pins_catch_planted_mistakes(variant, monkeypatch):
+    """Each planted mistake in the forward (written into the oracle, on the
+    CPU) fails the pins above."""
+    orig_mask = bob_oracle._mask_scores
+    orig_softmax = bob_oracle.softmax_rows
+    if variant == "softmax_over_queries":
+        monkeypatch.setattr(bob_oracle, "softmax_rows", lambda S: orig_softmax(np.asarray(S).T).T)
+    elif variant == "no_mask":
+        monkeypatch.setattr(bob_oracle, "_mask_scores", lambda S, qidx, causal: S)
+    elif variant == "mask_off_by_one":
+        def shifted(S, qidx, causal):
+            return orig_mask(S, np.asarray(qidx) + 1, causal) if causal else S
+        monkeypatch.setattr(bob_oracle, "_mask_scores", shifted)
+    Q, K, V = rand_inputs(9, 4, seed=77)[:3]
+    if variant == "V_rows_permuted":
+        # the mistake is an operand-order one: feed V with its rows reversed
+        # through the real oracle and check the pin sees the difference
+        V_used = V[::-1].copy()
+    else:
+        V_used = V
+    s = 0.6
+    t = [torch.tensor(x)[None, None] for x in (Q, K, V)]
+    worst = 0.0
+    for causal in (False, True):
+        ref = torch.nn.functional.scaled_dot_product_attention(*t, is_causal=causal, scale=s)[0, 0].numpy()
+        worst = max(worst, rel(bob_oracle.attention_forward(Q, K, V_used, s, causal=causal), ref))
+    assert not worst <= 1e-3, f"planted {variant} not caught (worst rel {worst})"
