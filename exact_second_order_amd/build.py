@@ -38,6 +38,8 @@ HIPCC_FLAGS = [
     # no packed fp32 VALU ops (v_pk_*_f32) in device code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wno-unused-command-line-argument",
+    # only the C ABI (marked FLASHBOB_API in include/flashbob.h) is exported
+    "-fvisibility=hidden",
 ]
 
 
@@ -75,7 +77,8 @@ def build(verbose=False):
         for f in [pool.submit(_run, c, verbose) for c in cmds]:
             f.result()
     tmp = LIB + ".tmp"
-    _run([hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp], verbose)
+    _run([hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", *objs,
+          "-Wl,--version-script=" + os.path.join(CSRC, "exports.map"), "-o", tmp], verbose)
     os.replace(tmp, LIB)
     if os.path.exists(C_CHECK_SRC):
         _run(["gcc", "-std=c11", "-O2", "-Wall", "-Werror", "-D__HIP_PLATFORM_AMD__", "-I", os.path.join(ROCM, "include"),

@@ -45,10 +45,11 @@ bool overlaps(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi; }
 // Shared validation. On success fills the element count of one tensor.
 int check_common(const void* const* ins, int B, int H, int N, int d, float scale, int dtype, size_t* numel) {
   if (B < 0 || H < 0 || N < 0) return FLASHBOB_ERR_SHAPE;
+  // the dtype first: the head dims supported depend on it
+  if (dtype != FLASHBOB_F32 && dtype != FLASHBOB_BF16) return FLASHBOB_ERR_DTYPE;
   // d = 256 in bf16 only: an fp32 stage at d = 256 needs more than the 160 KB of LDS
   if (d != 32 && d != 64 && d != 96 && d != 128 && !(d == 256 && dtype == FLASHBOB_BF16))
     return FLASHBOB_ERR_UNSUPPORTED_D;
-  if (dtype != FLASHBOB_F32 && dtype != FLASHBOB_BF16) return FLASHBOB_ERR_DTYPE;
   if (!std::isfinite(scale)) return FLASHBOB_ERR_SCALE;
   // B*H*N*d < 2^62 (fits every index computed in size_t) and B*H*N < 2^31
   const unsigned __int128 n = (unsigned __int128)B * H * N * d;
@@ -192,6 +193,19 @@ hipError_t dispatch_rowstats(int dtype, int d, int causal, const void* const* in
   });
 }
 
+// Key/value heads: 1 <= H_kv <= H with H a multiple of H_kv (any H_kv when H
+// is 0). Query-side tensors hold B*H*N*d elements, key/value-side ones
+// B*H_kv*N*d.
+int check_kv_heads(int H, int H_kv) {
+  if (H_kv < 0 || (H > 0 && (H_kv == 0 || H % H_kv != 0))) return FLASHBOB_ERR_SHAPE;
+  return FLASHBOB_OK;
+}
+
+void tensor_bytes(size_t numel_q, size_t numel_kv, size_t esz, size_t* in_bytes) {
+  const bool q_side[7] = {true, false, false, true, true, false, false};  // Q K V dO gQ gK gV
+  for (int i = 0; i < 7; ++i) in_bytes[i] = (q_side[i] ? numel_q : numel_kv) * esz;
+}
+
 size_t stats_bytes(int B, int H, int N) {
   const size_t raw = (size_t)4 * sizeof(float) * (size_t)B * (size_t)H * (size_t)N;
   return (raw + 255) & ~(size_t)255;
@@ -205,19 +219,6 @@ size_t flashbob_workspace_bytes(int B, int H, int N, int d) {
   (void)d;
   if (B <= 0 || H <= 0 || N <= 0) return 0;
   return stats_bytes(B, H, N);
-}
-
-// Key/value heads: 1 <= H_kv <= H with H a multiple of H_kv (any H_kv when H
-// is 0). Query-side tensors hold B*H*N*d elements, key/value-side ones
-// B*H_kv*N*d.
-int check_kv_heads(int H, int H_kv) {
-  if (H_kv < 0 || (H > 0 && (H_kv == 0 || H % H_kv != 0))) return FLASHBOB_ERR_SHAPE;
-  return FLASHBOB_OK;
-}
-
-void tensor_bytes(size_t numel_q, size_t numel_kv, size_t esz, size_t* in_bytes) {
-  const bool q_side[7] = {true, false, false, true, true, false, false};  // Q K V dO gQ gK gV
-  for (int i = 0; i < 7; ++i) in_bytes[i] = (q_side[i] ? numel_q : numel_kv) * esz;
 }
 
 int flashbob_bob_ex(const void* Q, const void* K, const void* V, const void* dO, const void* gQ, const void* gK,

@@ -44,6 +44,14 @@
 
 #include <stddef.h>
 
+/* Exported entry points (the library is built with hidden default
+ * visibility, so only these are visible to a loader). */
+#if defined(__GNUC__) || defined(__clang__)
+#define FLASHBOB_API __attribute__((visibility("default")))
+#else
+#define FLASHBOB_API
+#endif
+
 #ifdef __cplusplus
 extern "C" {
 #endif
@@ -86,10 +94,15 @@ enum {
 
 /* Bytes of device workspace flashbob_bob needs: four float32 row-scalar
  * vectors [B, H, N] (LSE, D, c, r), rounded up to 256 bytes. Returns 0 for
- * B*H*N == 0 or for invalid (negative) sizes. */
-size_t flashbob_workspace_bytes(int B, int H, int N, int d);
+ * B*H*N == 0 or for invalid (negative) sizes.
+ * Source: FlashBoB (arXiv 2609.24089), Abstract: the first pass hands the
+ * second one row statistics only, O(N) per head, never an N x N tensor. */
+FLASHBOB_API size_t flashbob_workspace_bytes(int B, int H, int N, int d);
 
 /* Exact BoB (the method's two-pass schedule: row scalars, then outputs).
+ * Source: FlashBoB (arXiv 2609.24089), Abstract: exact differentiation
+ * through the attention backward, organised as two passes over on-chip
+ * tiles with no N x N intermediate in device memory.
  *   Q, K, V, dO      [B, H, N, d] inputs of the attention first backward
  *   gQ, gK, gV       [B, H, N, d] cotangents on its outputs dQ, dK, dV
  *                    (all seven in `dtype`)
@@ -106,14 +119,16 @@ size_t flashbob_workspace_bytes(int B, int H, int N, int d);
  * kernels: a query-major sweep producing gradQ and graddO and a key-major
  * sweep producing gradK and gradV, each accumulating in registers (no
  * atomics, so results are bitwise reproducible run to run). */
-int flashbob_bob(const void* Q, const void* K, const void* V, const void* dO,
+FLASHBOB_API int flashbob_bob(const void* Q, const void* K, const void* V, const void* dO,
                  const void* gQ, const void* gK, const void* gV,
                  float* gradQ, float* gradK, float* gradV, float* graddO,
                  int B, int H, int N, int d, float scale, int dtype,
                  void* workspace, size_t workspace_bytes, void* stream);
 
 /* The three kernels of flashbob_bob as separate calls, for callers that time
- * or schedule them individually. Same arguments and checks as flashbob_bob;
+ * or schedule them individually. Source: FlashBoB (arXiv 2609.24089),
+ * Abstract: the two passes of the schedule (the second split here into a
+ * query-side and a key-side sweep). Same arguments and checks as flashbob_bob;
  * calling pass1, pass2_query and pass2_key in this order on one stream with
  * the same buffers is exactly flashbob_bob (the two pass-2 calls are
  * independent of each other).
@@ -123,23 +138,26 @@ int flashbob_bob(const void* Q, const void* K, const void* V, const void* dO,
  *                graddO (query-major sweep over the keys).
  *   pass2_key:   reads the row scalars from `workspace`, writes gradK and
  *                gradV (key-major sweep over the queries). */
-int flashbob_bob_pass1(const void* Q, const void* K, const void* V, const void* dO,
+FLASHBOB_API int flashbob_bob_pass1(const void* Q, const void* K, const void* V, const void* dO,
                        const void* gQ, const void* gK, const void* gV,
                        float* gradQ, float* gradK, float* gradV, float* graddO,
                        int B, int H, int N, int d, float scale, int dtype,
                        void* workspace, size_t workspace_bytes, void* stream);
-int flashbob_bob_pass2_query(const void* Q, const void* K, const void* V, const void* dO,
+FLASHBOB_API int flashbob_bob_pass2_query(const void* Q, const void* K, const void* V, const void* dO,
                              const void* gQ, const void* gK, const void* gV,
                              float* gradQ, float* gradK, float* gradV, float* graddO,
                              int B, int H, int N, int d, float scale, int dtype,
                              void* workspace, size_t workspace_bytes, void* stream);
-int flashbob_bob_pass2_key(const void* Q, const void* K, const void* V, const void* dO,
+FLASHBOB_API int flashbob_bob_pass2_key(const void* Q, const void* K, const void* V, const void* dO,
                            const void* gQ, const void* gK, const void* gV,
                            float* gradQ, float* gradK, float* gradV, float* graddO,
                            int B, int H, int N, int d, float scale, int dtype,
                            void* workspace, size_t workspace_bytes, void* stream);
 
-/* General form of flashbob_bob and of the three stage calls below:
+/* General form of flashbob_bob and of the three stage calls above.
+ * Source: FlashBoB (arXiv 2609.24089), Abstract (the BoB itself); masks,
+ * grouped heads, the first-backward outputs, a saved log-sum-exp and bf16
+ * outputs are extensions beyond it:
  *   H_kv    key/value heads (grouped-query attention; H_kv = H is plain
  *           multi-head, H_kv = 1 multi-query). 1 <= H_kv <= H, H a multiple
  *           of H_kv. Q, dO, gQ, gradQ, graddO are [B, H, N, d]; K, V, gK, gV,
@@ -176,7 +194,7 @@ int flashbob_bob_pass2_key(const void* Q, const void* K, const void* V, const vo
  *           flags and inputs).
  * Other arguments, checks and return codes as flashbob_bob; unknown flag
  * bits or stage sets return FLASHBOB_ERR_FLAGS. */
-int flashbob_bob_ex(const void* Q, const void* K, const void* V, const void* dO,
+FLASHBOB_API int flashbob_bob_ex(const void* Q, const void* K, const void* V, const void* dO,
                     const void* gQ, const void* gK, const void* gV,
                     void* gradQ, void* gradK, void* gradV, void* graddO,
                     void* dQ, void* dK, void* dV, const float* lse_in,
@@ -184,12 +202,15 @@ int flashbob_bob_ex(const void* Q, const void* K, const void* V, const void* dO,
                     void* workspace, size_t workspace_bytes, void* stream);
 
 /* Pass 1 alone (row statistics), exported for testing the first pass.
+ * Source: FlashBoB (arXiv 2609.24089), Abstract: the two row-wise scalars
+ * that fix every BoB output through affine maps (read as c and r below,
+ * next to the first backward's D and the log-sum-exp).
  * Writes, per query row, LSE (natural-log log-sum-exp of s Q K^T), the
  * first-backward scalar D = rowsum(dO o O) and the two BoB row scalars
  *     c = rowsum(P o G),   r = rowsum(dS o G) + rowsum(P o H),
  * where G = s (gQ K^T + Q gK^T) and H = dO gV^T; each output is [B, H, N]
  * float32. Inputs as for flashbob_bob. */
-int flashbob_rowstats(const void* Q, const void* K, const void* V, const void* dO,
+FLASHBOB_API int flashbob_rowstats(const void* Q, const void* K, const void* V, const void* dO,
                       const void* gQ, const void* gK, const void* gV,
                       float* lse, float* D, float* c, float* r,
                       int B, int H, int N, int d, float scale, int dtype,
@@ -198,18 +219,19 @@ int flashbob_rowstats(const void* Q, const void* K, const void* V, const void* d
 /* flashbob_rowstats with key/value heads H_kv (as for flashbob_bob_ex) and
  * flags (0 or FLASHBOB_CAUSAL; with the mask, the row scalars are those of the
  * causal attention). */
-int flashbob_rowstats_ex(const void* Q, const void* K, const void* V, const void* dO,
+FLASHBOB_API int flashbob_rowstats_ex(const void* Q, const void* K, const void* V, const void* dO,
                          const void* gQ, const void* gK, const void* gV,
                          float* lse, float* D, float* c, float* r,
                          int B, int H, int H_kv, int N, int d, float scale, int dtype, int flags,
                          void* stream);
 
 /* Static description of an error code; for FLASHBOB_ERR_HIP, the HIP error
- * text of the calling thread's last failure. Never NULL. */
-const char* flashbob_strerror(int code);
+ * text of the calling thread's last failure. Never NULL. (Library plumbing;
+ * the method's pages define no error model.) */
+FLASHBOB_API const char* flashbob_strerror(int code);
 
-/* ABI version (major * 100 + minor). */
-int flashbob_version(void);
+/* ABI version (major * 100 + minor). (Library plumbing.) */
+FLASHBOB_API int flashbob_version(void);
 
 #ifdef __cplusplus
 }

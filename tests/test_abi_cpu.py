@@ -35,6 +35,19 @@ def test_library_exports_every_declared_symbol():
         assert hasattr(lib, name), name
 
 
+def test_library_exports_nothing_else():
+    """The dynamic symbol table holds exactly the header's entry points (the
+    build hides everything else: kernels, helpers, compiler globals)."""
+    import shutil
+    import subprocess
+    nm = shutil.which("nm")
+    if nm is None:
+        pytest.skip("nm not available")
+    out = subprocess.run([nm, "-D", "--defined-only", fb.LIB_PATH], capture_output=True, text=True, check=True).stdout
+    names = sorted({ln.split()[-1] for ln in out.splitlines() if ln.strip()})
+    assert names == header_functions()
+
+
 def test_version_and_strerror():
     lib = fb.load_library()
     assert lib.flashbob_version() == 101
@@ -96,6 +109,12 @@ def test_rejects_bad_dtype_and_scale():
     a = list(fake_args())
     a[7] = 7
     assert call(*a) == DT
+    # the dtype is checked before the head dim (which head dims exist depends
+    # on it): an unknown dtype reports the dtype, whatever d is
+    for d in (256, 48):
+        a = list(fake_args(d=d))
+        a[7] = 7
+        assert call(*a) == DT
     for bad in (float("nan"), float("inf"), -float("inf")):
         a = list(fake_args())
         a[6] = bad
