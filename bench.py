@@ -3,10 +3,17 @@
 One step = one exact BoB call (pass 1 + pass 2) over the resident inputs of
 the B=1, H=4, N=65536, d=64 bf16 workload. Prints ONE JSON line on stdout:
 throughput (TFLOP/s with the fixed count 34 B H N^2 d), ms per step, the
-roofline of the dominant kernel (its algorithmic flops over its average
-launch time, from HIP events on the launch stream), and the fp64 CPU oracle
-timed on a bounded sample of the same workload. Everything else goes to
-stderr.
+roofline of the dominant step of the schedule (the method's algorithmic flops
+of that step over its average time, from HIP events on the launch stream),
+and the fp64 CPU oracle timed on a bounded sample of the same workload.
+Everything else goes to stderr.
+
+Work accounting: the method's two passes do 5 and 12 N x N x d products
+(34 B H N^2 d flops per call). This implementation runs pass 2 as two
+launches that together execute 17 products (9 query-side, 8 key-side; the
+5 recompute products are done by both), so pass 2 is timed and credited as
+one step over its two launches with the method's 12 products; the executed
+counts are reported beside it, not credited.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload IDX]
 """
@@ -69,6 +76,35 @@ def measured_mfma(stage, workload="bob_b1h4n65536d64_bf16"):
     return t.get("kernels", {}).get(stage)
 
 
+# N x N x d products (2 N^2 d flops each). Credited: the method's two passes
+# (pass 1: S, G (2), dP, H; pass 2: the recompute plus gradK (2), gradV,
+# gradQ (2), graddO (2)); with the first backward also dQ, dK, dV. Executed:
+# what each launch runs (pass 2's two sweeps both recompute).
+STEP_LAUNCHES = {"pass1": ["pass1"], "pass2": ["pass2_query", "pass2_key"]}
+
+
+def method_units(first_backward):
+    return {"pass1": 5, "pass2": 15 if first_backward else 12}
+
+
+def executed_units(first_backward):
+    return ({"pass1": 5, "pass2_query": 10, "pass2_key": 10} if first_backward
+            else {"pass1": 5, "pass2_query": 9, "pass2_key": 8})
+
+
+def step_accounting(launch_ms, unit_flops, peak, first_backward=False):
+    """Per step of the schedule: time (sum of its launches' average times),
+    the method's products, TFLOP/s and fraction of `peak` they give."""
+    mu = method_units(first_backward)
+    out = {}
+    for sn, launches in STEP_LAUNCHES.items():
+        ms = sum(launch_ms[k] for k in launches)
+        tf = mu[sn] * unit_flops / (ms * 1e-3) / 1e12
+        out[sn] = {"ms": round(ms, 4), "units": mu[sn], "tflops": round(tf, 2), "frac": round(tf / peak, 4),
+                   "launches": launches}
+    return out
+
+
 def cpu_baseline(w, rows, block=512, causal=False):
     """fp64 oracle on `rows` query rows against all keys of head 0 (a bounded
     sample of the workload), scaled to TFLOP/s with the same flop convention
@@ -82,6 +118,15 @@ def cpu_baseline(w, rows, block=512, causal=False):
         cores = max((p.get("num_threads", 1) for p in threadpool_info()), default=os.cpu_count())
     except Exception:  # threadpoolctl missing: report the visible cpus
         cores = len(os.sched_getaffinity(0))
+    cpu_model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    cpu_model = ln.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
     ins = workload_inputs(w)
     xs = [ins[k][0, 0].to(dtype=__import__("torch").float64).numpy() for k in
           ("Q", "K", "V", "dO", "gQ", "gK", "gV")]
@@ -96,7 +141,8 @@ def cpu_baseline(w, rows, block=512, causal=False):
     pairs = rows * (rows + 1) / 2 if causal else rows * w.N
     flops = 34.0 * pairs * w.d
     what = f"the first {rows} query rows (causal)" if causal else f"{rows} query rows x all {w.N} keys"
-    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(cores), "cpu_model": cpu_model,
+            "kind": "oracle",
             "sample": f"{what} of one head (d={w.d}), fp64 row-blocked oracle, {dt:.2f} s; "
                       f"flops counted as 34*d per visible (query, key) pair"}
 
@@ -153,12 +199,9 @@ def main():
         del src, dst
 
     stages = list(fb.STAGES)
-    # algorithmic flops of each kernel: its N x N x d products x 2 N^2 d
-    units = {"pass1": 5, "pass2_query": 9, "pass2_key": 8}
-    if args.first_backward:  # + dQ = s dS K in pass 2q, dK = s dS^T Q and dV = P^T dO in pass 2k
-        units = {"pass1": 5, "pass2_query": 10, "pass2_key": 10}
-    kernel_names = {"pass1": "query_kernel<.., false>", "pass2_query": "query_kernel<.., true>",
-                    "pass2_key": "key_kernel"}
+    mu, eu, step_launches = method_units(args.first_backward), executed_units(args.first_backward), STEP_LAUNCHES
+    kernel_names = {"pass1": "query_kernel<.., false>",
+                    "pass2": "query_kernel<.., true> + key_kernel (pass 2: two launches)"}
 
     def step(ev=None):
         for i, st in enumerate(stages):
@@ -198,31 +241,47 @@ def main():
     flops = (w.flops + (6.0 * w.B * w.H * w.N * w.N * w.d if args.first_backward else 0.0)) * frac_pairs
     tflops = flops / (ms_step * 1e-3) / 1e12
     peak = PEAK_TFLOPS[w.dtype_name]
+    unit_flops = 2.0 * w.B * w.H * w.N * w.N * w.d * frac_pairs
     per_kernel = {}
     for i, st in enumerate(stages):
         ms = sum(e[i].elapsed_time(e[i + 1]) for e in evs) / args.steps
-        kf = 2.0 * units[st] * w.B * w.H * w.N * w.N * w.d * frac_pairs
-        per_kernel[st] = {"ms": round(ms, 4), "tflops": round(kf / (ms * 1e-3) / 1e12, 2),
-                          "frac": round(kf / (ms * 1e-3) / 1e12 / peak, 4), "units": units[st]}
+        per_kernel[st] = {"ms": round(ms, 4), "executed_units": eu[st],
+                          "executed_tflops": round(eu[st] * unit_flops / (ms * 1e-3) / 1e12, 2)}
+    per_step = step_accounting({k: v["ms"] for k, v in per_kernel.items()}, unit_flops, peak, args.first_backward)
     # counter-derived figures (committed profiles of the plain headline run)
     plain = not (args.causal or args.first_backward or args.saved_lse)
     for st in stages:
         traffic = (measured_traffic(st, args.causal, w.name)
                    if not (args.first_backward or args.saved_lse) else None)
         if traffic is not None:
+            per_kernel[st]["hbm_bytes"] = int(traffic)
             per_kernel[st]["hbm_GBps"] = round(traffic / (per_kernel[st]["ms"] * 1e-3) / 1e9, 1)
         m = measured_mfma(st, w.name) if plain else None
         if m is not None:
             per_kernel[st]["mfma_util"] = round(m["mfma_util"], 4)
             per_kernel[st]["sclk_ghz"] = round(m["sclk_ghz"], 3)
+    # the peak at the shader clock the counters measured under load (the
+    # published peak assumes 2.4 GHz; the chip runs slower when power-limited)
+    for sn, launches in step_launches.items():
+        clk = [per_kernel[k].get("sclk_ghz") for k in launches]
+        if all(c is not None for c in clk):
+            t = [per_kernel[k]["ms"] for k in launches]
+            sclk = sum(c * tt for c, tt in zip(clk, t)) / sum(t)  # time-weighted
+            per_step[sn]["sclk_ghz"] = round(sclk, 3)
+            per_step[sn]["frac_at_sclk"] = round(per_step[sn]["tflops"] / (peak * sclk / 2.4), 4)
+        tr = [per_kernel[k].get("hbm_bytes") for k in launches]
+        per_step[sn]["hbm_bytes"] = int(sum(tr)) if all(x is not None for x in tr) else None
     log(f"[bench] ms/step {ms_step:.3f}; {tflops:.1f} TFLOP/s = {100 * tflops / peak:.1f}% of {peak} peak; "
-        f"kernels {per_kernel}")
-    dom = max(stages, key=lambda st: per_kernel[st]["ms"])
-    roofline = {"bound": "mfma", "achieved": per_kernel[dom]["tflops"], "peak": peak, "unit": "TFLOP/s",
-                "frac": per_kernel[dom]["frac"],
-                "traffic": (None if (args.first_backward or args.saved_lse)
-                            else measured_traffic(dom, args.causal, w.name)),
-                "kernel": kernel_names[dom], "launch_ms": per_kernel[dom]["ms"]}
+        f"steps {per_step}; launches {per_kernel}")
+    dom = max(per_step, key=lambda sn: per_step[sn]["ms"])
+    roofline = {"bound": "mfma", "achieved": per_step[dom]["tflops"], "peak": peak, "unit": "TFLOP/s",
+                "frac": per_step[dom]["frac"],
+                "traffic": (None if (args.first_backward or args.saved_lse) else per_step[dom]["hbm_bytes"]),
+                "kernel": kernel_names[dom], "step": dom, "launch_ms": per_step[dom]["ms"],
+                "credited_units": mu[dom], "executed_units": sum(eu[k] for k in step_launches[dom])}
+    if "frac_at_sclk" in per_step[dom]:
+        roofline["sclk_ghz"] = per_step[dom]["sclk_ghz"]
+        roofline["frac_at_sclk"] = per_step[dom]["frac_at_sclk"]
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -251,7 +310,7 @@ def main():
                    "first_backward": bool(args.first_backward), "saved_lse": bool(args.saved_lse), "seed": WORKLOADS.index(w),
                    "flops_per_step": flops, "frac_of_peak": round(tflops / peak, 4),
                    "ms_median_events": round(ms_median, 4), "ms_min_events": round(step_ms[0], 4),
-                   "peak_mem_delta_bytes": int(peak_mem_delta), "kernels": per_kernel},
+                   "peak_mem_delta_bytes": int(peak_mem_delta), "steps": per_step, "kernels": per_kernel},
         "roofline": roofline,
         "cpu_baseline": cpu,
     }

@@ -44,3 +44,19 @@ def test_multi_gpu_request_exits_with_message():
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
                        text=True, timeout=120)
     assert r.returncode == 2 and "one GPU" in r.stderr
+
+
+def test_step_accounting_credits_the_method_not_the_launches():
+    """Pass 2 is credited as one step with the method's 12 products over the
+    sum of its two launches' times (the launches execute 9 + 8), pass 1 with
+    5; the whole call's 17 match the 34 B H N^2 d flop convention."""
+    unit = 2.0 * 1 * 4 * 65536 ** 2 * 64
+    ms = {"pass1": 10.0, "pass2_query": 16.0, "pass2_key": 15.0}
+    acc = bench.step_accounting(ms, unit, 2500.0)
+    assert acc["pass1"]["units"] == 5 and acc["pass2"]["units"] == 12
+    assert acc["pass2"]["ms"] == 31.0 and acc["pass2"]["launches"] == ["pass2_query", "pass2_key"]
+    assert abs(acc["pass2"]["tflops"] - 12 * unit / 31e-3 / 1e12) < 0.01
+    assert sum(bench.method_units(False).values()) * unit == 34.0 * 4 * 65536 ** 2 * 64
+    assert sum(bench.executed_units(False).values()) == 22
+    fb = bench.step_accounting(ms, unit, 2500.0, first_backward=True)
+    assert fb["pass2"]["units"] == 15 and sum(bench.executed_units(True).values()) == 25
