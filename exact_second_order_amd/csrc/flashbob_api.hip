@@ -8,6 +8,7 @@
 #include <cmath>
 #include <cstdint>
 #include <cstring>
+#include <mutex>
 #include <string>
 #include <type_traits>
 
@@ -211,6 +212,36 @@ size_t stats_bytes(int B, int H, int N) {
   return (raw + 255) & ~(size_t)255;
 }
 
+// Static row-scalar buffer of flashbob_bob_noalloc: one copy per GPU the
+// library runs on, found through hipGetSymbolAddress (in host code the array
+// name is only a stand-in for the device address, never used directly).
+static __device__ __align__(256) unsigned char scratch[FLASHBOB_NOALLOC_SCRATCH_BYTES];
+static_assert((size_t)FLASHBOB_NOALLOC_SCRATCH_BYTES >= (size_t)16 * FLASHBOB_NOALLOC_MAX_ROWS,
+              "four float32 scalars per query row");
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of `scratch` on the device current on this thread (looked
+// up once per device).
+int scratch_on_current_device(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e);
+  if (dev < 0 || dev >= kMaxDevices) return hip_fail(hipErrorInvalidDevice);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e);
+    if (p == nullptr) return hip_fail(hipErrorInvalidSymbol);
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return FLASHBOB_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -287,6 +318,30 @@ int flashbob_bob(const void* Q, const void* K, const void* V, const void* dO, co
                          FLASHBOB_STAGES_ALL, workspace, workspace_bytes, stream);
 }
 
+int flashbob_bob_noalloc(const void* Q, const void* K, const void* V, const void* dO, const void* gQ,
+                         const void* gK, const void* gV, float* gradQ, float* gradK, float* gradV,
+                         float* graddO, int B, int H, int N, int d, float scale, int dtype, void* stream) {
+  // every argument check before the HIP call that finds the buffer
+  const void* ins[7] = {Q, K, V, dO, gQ, gK, gV};
+  size_t numel = 0;
+  int rc = check_common(ins, B, H, N, d, scale, dtype, &numel);
+  if (rc != FLASHBOB_OK || numel == 0) return rc;
+  if ((long long)B * H * N > FLASHBOB_NOALLOC_MAX_ROWS) return FLASHBOB_ERR_SCRATCH;
+  const size_t esz = dtype == FLASHBOB_BF16 ? 2 : 4;
+  size_t ib[7];
+  tensor_bytes(numel, numel, esz, ib);
+  void* outs[4] = {gradQ, gradK, gradV, graddO};
+  const size_t ob[4] = {numel * 4, numel * 4, numel * 4, numel * 4};
+  rc = check_outputs(ins, ib, 7, outs, ob, 4);
+  if (rc != FLASHBOB_OK) return rc;
+  void* ws = nullptr;
+  rc = scratch_on_current_device(&ws);
+  if (rc != FLASHBOB_OK) return rc;
+  return flashbob_bob_ex(Q, K, V, dO, gQ, gK, gV, gradQ, gradK, gradV, graddO, nullptr, nullptr, nullptr, nullptr,
+                         B, H, H, N, d, scale, dtype, 0, FLASHBOB_STAGES_ALL, ws, FLASHBOB_NOALLOC_SCRATCH_BYTES,
+                         stream);
+}
+
 int flashbob_bob_pass1(const void* Q, const void* K, const void* V, const void* dO, const void* gQ,
                        const void* gK, const void* gV, float* gradQ, float* gradK, float* gradV, float* graddO,
                        int B, int H, int N, int d, float scale, int dtype, void* workspace,
@@ -356,11 +411,12 @@ const char* flashbob_strerror(int code) {
     case FLASHBOB_ERR_ALIAS: return "an output overlaps an input, the workspace or another output";
     case FLASHBOB_ERR_SCALE: return "scale is not finite";
     case FLASHBOB_ERR_FLAGS: return "unknown flag bits or an empty or unknown stage set";
+    case FLASHBOB_ERR_SCRATCH: return "B*H*N exceeds the static buffer of flashbob_bob_noalloc (1048576 query rows)";
     case FLASHBOB_ERR_HIP: return g_last_hip_error.c_str();
     default: return "unknown error code";
   }
 }
 
-int flashbob_version(void) { return 101; }
+int flashbob_version(void) { return 102; }
 
 }  // extern "C"

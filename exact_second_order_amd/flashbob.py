@@ -33,6 +33,7 @@ ERRORS = {
     -8: "ERR_ALIAS",
     -9: "ERR_SCALE",
     -10: "ERR_FLAGS",
+    -11: "ERR_SCRATCH",
     -100: "ERR_HIP",
 }
 
@@ -44,6 +45,7 @@ EXPORTS = (
     "flashbob_bob_pass2_key",
     "flashbob_rowstats",
     "flashbob_bob_ex",
+    "flashbob_bob_noalloc",
     "flashbob_rowstats_ex",
     "flashbob_strerror",
     "flashbob_version",
@@ -84,6 +86,8 @@ def load_library(path=LIB_PATH):
     lib.flashbob_rowstats.restype = i
     lib.flashbob_bob_ex.argtypes = [vp] * 7 + [vp] * 8 + [i, i, i, i, i, f, i, i, i, vp, sz, vp]
     lib.flashbob_bob_ex.restype = i
+    lib.flashbob_bob_noalloc.argtypes = [vp] * 7 + [vp] * 4 + [i, i, i, i, f, i, vp]
+    lib.flashbob_bob_noalloc.restype = i
     lib.flashbob_rowstats_ex.argtypes = [vp] * 7 + [vp] * 4 + [i, i, i, i, i, f, i, i, vp]
     lib.flashbob_rowstats_ex.restype = i
     lib.flashbob_strerror.argtypes = [i]
@@ -233,6 +237,27 @@ def bob_stage(stage, Q, K, V, dO, gQ, gK, gV, out, workspace, scale=None, stream
                 ctypes.c_size_t(workspace.numel() * workspace.element_size()),
                 _stream_handle(Q.device, stream))
     _check(rc)
+
+
+def bob_noalloc(Q, K, V, dO, gQ, gK, gV, scale=None, out=None, stream=None):
+    """flashbob_bob_noalloc: BoB with the library's static row-scalar buffer
+    instead of a workspace (plain multi-head, non-causal, float32 outputs;
+    B*H*N <= 2^20). With `out` given the call allocates nothing. Calls that
+    overlap on one GPU share the buffer and race."""
+    lib = load_library()
+    ins, Hkv = _inputs(Q, K, V, dO, gQ, gK, gV)
+    if Hkv != Q.shape[1]:
+        raise ValueError("bob_noalloc takes H_kv = H")
+    B, H, N, d = Q.shape
+    if scale is None:
+        scale = d ** -0.5
+    shapes = shapes_of(B, H, Hkv, N, d)
+    if out is None:
+        out = tuple(torch.empty(sh, dtype=torch.float32, device=Q.device) for sh in shapes)
+    out = _check_out(out, shapes, Q.device, "out", torch.float32)
+    _check(lib.flashbob_bob_noalloc(*[_ptr(t) for t in ins], *[_ptr(t) for t in out], B, H, N, d,
+                                    ctypes.c_float(scale), _dtype_code(Q.dtype), _stream_handle(Q.device, stream)))
+    return out
 
 
 def bob(Q, K, V, dO, gQ, gK, gV, scale=None, out=None, workspace=None, stream=None, causal=False,

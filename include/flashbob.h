@@ -73,6 +73,7 @@ enum {
   FLASHBOB_ERR_ALIAS = -8,          /* an output overlaps an input, the workspace or another output */
   FLASHBOB_ERR_SCALE = -9,          /* scale is not finite */
   FLASHBOB_ERR_FLAGS = -10,         /* unknown flag bits, or an empty or unknown stage set */
+  FLASHBOB_ERR_SCRATCH = -11,       /* flashbob_bob_noalloc: B*H*N exceeds its static buffer */
   FLASHBOB_ERR_HIP = -100           /* a HIP call failed; see flashbob_strerror */
 };
 
@@ -200,6 +201,27 @@ FLASHBOB_API int flashbob_bob_ex(const void* Q, const void* K, const void* V, co
                     void* dQ, void* dK, void* dV, const float* lse_in,
                     int B, int H, int H_kv, int N, int d, float scale, int dtype, int flags, int stages,
                     void* workspace, size_t workspace_bytes, void* stream);
+
+/* flashbob_bob without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation). The row scalars go to a static buffer
+ * of the library instead: FLASHBOB_NOALLOC_SCRATCH_BYTES of device memory
+ * that each GPU the library runs on holds until the process ends, enough for
+ * B*H*N <= FLASHBOB_NOALLOC_MAX_ROWS query rows (larger calls return
+ * FLASHBOB_ERR_SCRATCH before any HIP call). Everything else (arguments,
+ * checks, results, asynchrony) is as flashbob_bob; results are bitwise equal
+ * to flashbob_bob's. The buffer belongs to the device current on the
+ * calling thread (its address is looked up on the first call there, the
+ * only HIP call besides the kernel launches) and is shared by every call on
+ * that device: calls that overlap on one GPU (other streams or threads)
+ * race on it, so such callers serialise them. Nothing in it needs clearing:
+ * pass 1 overwrites every value pass 2 reads. */
+#define FLASHBOB_NOALLOC_MAX_ROWS (1 << 20)
+#define FLASHBOB_NOALLOC_SCRATCH_BYTES (16u << 20)
+FLASHBOB_API int flashbob_bob_noalloc(const void* Q, const void* K, const void* V, const void* dO,
+                                      const void* gQ, const void* gK, const void* gV,
+                                      float* gradQ, float* gradK, float* gradV, float* graddO,
+                                      int B, int H, int N, int d, float scale, int dtype, void* stream);
 
 /* Pass 1 alone (row statistics), exported for testing the first pass.
  * Source: FlashBoB (arXiv 2609.24089), Abstract: the two row-wise scalars

@@ -50,8 +50,8 @@ def test_library_exports_nothing_else():
 
 def test_version_and_strerror():
     lib = fb.load_library()
-    assert lib.flashbob_version() == 101
-    for code in (0, -1, -2, -3, -4, -5, -6, -7, -8, -9, -10, -100, 12345):
+    assert lib.flashbob_version() == 102
+    for code in (0, -1, -2, -3, -4, -5, -6, -7, -8, -9, -10, -11, -100, 12345):
         s = lib.flashbob_strerror(code)
         assert isinstance(s, bytes) and len(s) > 0
 
@@ -345,3 +345,27 @@ def test_plain_c_caller_is_built_and_checks_its_arguments():
     r = subprocess.run([build.C_CHECK, "1", "1", "0", "64", "0", "0.1", "0", "/nonexistent", "/nonexistent"],
                        capture_output=True, text=True, timeout=60)
     assert r.returncode == 2 and "bad arguments" in r.stderr
+
+
+def test_noalloc_checks_arguments_and_its_limit_before_any_hip_call():
+    """flashbob_bob_noalloc rejects bad arguments, and problems larger than
+    its static buffer, with error codes and without touching the device
+    (fake pointers, no GPU here)."""
+    lib = fb.load_library()
+    ins = [BASE + i * STRIDE for i in range(7)]
+    outs = [BASE + (7 + i) * STRIDE for i in range(4)]
+
+    def noalloc(B, H, N, d, scale=0.125, dtype=F32, outs=outs, ins=ins):
+        return lib.flashbob_bob_noalloc(*[ctypes.c_void_p(p) for p in ins], *[ctypes.c_void_p(p) for p in outs],
+                                        B, H, N, d, ctypes.c_float(scale), dtype, None)
+    limit = 1 << 20
+    assert noalloc(1, 1, limit + 1, 64) == -11        # FLASHBOB_ERR_SCRATCH
+    assert noalloc(2, 4, limit // 8 + 1, 64) == -11
+    assert noalloc(1, 1, 128, 48) == UD
+    assert noalloc(1, 1, 128, 64, dtype=7) == DT
+    assert noalloc(1, 1, 128, 64, scale=float("nan")) == SCALE
+    assert noalloc(1, 1, 128, 64, outs=[outs[0], outs[0], outs[2], outs[3]]) == ALIAS
+    assert noalloc(1, 1, 128, 64, outs=[outs[0], 0, outs[2], outs[3]]) == NULL
+    assert noalloc(1, 1, 128, 64, ins=[ins[0] + 8] + ins[1:]) == ALIGN
+    assert noalloc(0, 1, 128, 64) == OK               # empty problem: nothing to do
+    assert b"1048576" in lib.flashbob_strerror(-11)
