@@ -360,13 +360,24 @@ __global__ __launch_bounds__(256, (FIRST ? 1 : QueryCfg<T, D, GRADQ>::OCC)) void
   }
 
   const int nblk = (N + BK - 1) / BK;  // 32-key blocks = stages
+  // Key blocks visited and how many of them need no mask. Causal: the
+  // workgroup's queries q0 .. q0+BQ-1 see keys 0 .. q0+BQ-1, and blocks
+  // wholly below q0 are visible to all of them; the blocks across the
+  // diagonal mask per lane at the key limit qlim = q + 1 (the masked path
+  // also covers a partial last block).
+  const bool last_partial = N % BK != 0;
+  const int q0 = qblk * Cfg::BQ;
+  const int nvis = causal ? min(nblk, (q0 + Cfg::BQ + BK - 1) / BK) : nblk;
+  const int nfull = causal ? min(nvis, q0 / BK) : (last_partial ? nblk - 1 : nblk);
   // staging of stage n: prefetch() issues its global reads (into registers,
   // or straight into its LDS buffer when SWZ); commit() makes it visible to
   // this wave's later LDS accesses (register store, or wait for the loads).
+  // A stage past the last visible block is an empty buffer (zeros, no memory
+  // access), so every iteration can prefetch its successor.
   RowPrefetch<T, SWZ ? 0 : BK, D, 256> pk, pgk, pv, pgv;
   auto prefetch = [&](int n) __attribute__((always_inline)) {
-    const int k0 = n * BK;
-    const int nk = min(BK, N - k0);
+    const int k0 = n < nvis ? n * BK : 0;
+    const int nk = n < nvis ? min(BK, N - k0) : 0;
     if constexpr (SWZ) {
       const int b = n & (NBUF - 1);
       load_tile_sw(tile(b, 0), K + koff + (size_t)k0 * D, nk);
@@ -460,31 +471,22 @@ __global__ __launch_bounds__(256, (FIRST ? 1 : QueryCfg<T, D, GRADQ>::OCC)) void
 
   using F0 = std::integral_constant<bool, false>;
   using F1 = std::integral_constant<bool, true>;
-  const bool last_partial = N % BK != 0;
-  // Key blocks visited and how many of them need no mask. Causal: the
-  // workgroup's queries q0 .. q0+BQ-1 see keys 0 .. q0+BQ-1, and blocks
-  // wholly below q0 are visible to all of them; the blocks across the
-  // diagonal mask per lane at the key limit qlim = q + 1 (the masked path
-  // also covers a partial last block).
-  const int q0 = qblk * Cfg::BQ;
-  const int nvis = causal ? min(nblk, (q0 + Cfg::BQ + BK - 1) / BK) : nblk;
-  const int nfull = causal ? min(nvis, q0 / BK) : (last_partial ? nblk - 1 : nblk);
-  const int nsteady = min(nfull, nvis - 1);
+  const int nsteady = nfull;
   Tiles t;
   Frags f;
-  // one iteration per 32-key block; all but the last are branch-free (every
-  // key valid, next stage exists), so each is one straight-line block the
-  // scheduler can interleave freely
-  auto iteration = [&](auto last, auto tail, int n) __attribute__((always_inline)) {
-    constexpr bool LAST = decltype(last)::value;
-    if constexpr (!LAST) prefetch(n + 1);  // its buffer last held stage n-1, read in iteration n-1
+  // one iteration per 32-key block; the unmasked ones are branch-free, so
+  // each is one straight-line block the scheduler can interleave freely (the
+  // last one prefetches an empty stage rather than taking a code path of its
+  // own)
+  auto iteration = [&](auto tail, int n) __attribute__((always_inline)) {
+    prefetch(n + 1);  // its buffer last held stage n-1, read in iteration n-1
     recompute(n, t, 0, NCH);
 #pragma unroll
     for (int cc = 0; cc < 2; ++cc) {
       elementwise(tail, n, cc, t, f);
       outputs(n, cc, f);
     }
-    if constexpr (!LAST) commit(n + 1);
+    commit(n + 1);
     __syncthreads();
   };
   // pass 1 flushes its level-1 sums every kFlush blocks (outside the
@@ -495,18 +497,15 @@ __global__ __launch_bounds__(256, (FIRST ? 1 : QueryCfg<T, D, GRADQ>::OCC)) void
     const int n1 = min(n0 + kFlush, nsteady);
     const int npairs = (n1 - n0) >> 1;
     for (int i = 0; i < npairs; ++i) {
-      iteration(F0{}, F0{}, n0 + 2 * i);
-      iteration(F0{}, F0{}, n0 + 2 * i + 1);
+      iteration(F0{}, n0 + 2 * i);
+      iteration(F0{}, n0 + 2 * i + 1);
     }
-    if ((n1 - n0) & 1) iteration(F0{}, F0{}, n1 - 1);
+    if ((n1 - n0) & 1) iteration(F0{}, n1 - 1);
     if constexpr (!GRADQ) st.flush();
   }
-  // masked blocks before the last (causal diagonal only; at most BQ/BK - 1)
-  for (int n = nsteady; n < nvis - 1; ++n) iteration(F0{}, F1{}, n);
-  if (nvis - 1 >= nfull)
-    iteration(F1{}, F1{}, nvis - 1);
-  else
-    iteration(F1{}, F0{}, nvis - 1);
+  // masked blocks: the causal diagonal (at most BQ/BK of them) and a partial
+  // last block
+  for (int n = nsteady; n < nvis; ++n) iteration(F1{}, n);
 
   if constexpr (!GRADQ) {
     st.flush();
