@@ -24,7 +24,6 @@ ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
 # compiler place accumulators in AGPRs.
 OBJECTS = [
     ("flashbob_api.hip", []),
-    ("bob_prep.hip", []),
     ("bob_query.hip", ["-DFLASHBOB_QUERY_PASS1", "-mllvm", "-amdgpu-mfma-vgpr-form"]),
     ("bob_query.hip", ["-DFLASHBOB_QUERY_PASS2"]),
     ("bob_key.hip", []),

@@ -207,22 +207,6 @@ __device__ __forceinline__ bf16x8 ld_cols_perm_sw(const bf16* t, int krow0, int 
   return __builtin_bit_cast(bf16x8, v);
 }
 
-// Row-transposed 32-row blocks of a [rows][64] bf16 tensor (written by the
-// operand-preparation kernel, bob_prep.hip): a block is [16-row chunk cc]
-// [column d][16 rows], the 16 rows of a chunk in kperm order (position 8 h + s
-// holds row kperm(h, s)) and the two 8-row halves swapped on columns with bit
-// 3 set, so the 16-byte reads below are free of LDS bank conflicts.
-__device__ __forceinline__ constexpr int tposed_pos(int cc, int d, int h, int s) {
-  return cc * 1024 + d * 16 + 8 * (h ^ ((d >> 3) & 1)) + s;
-}
-
-// ld_cols_perm on a row-transposed block, as one 16-byte read: lane l gets
-// column d0 + l % 32 at rows 16 cc + kperm(l / 32, s).
-__device__ __forceinline__ bf16x8 ld_tposed(const bf16* t, int cc, int d0) {
-  const int l = lane_id();
-  return *reinterpret_cast<const bf16x8*>(t + tposed_pos(cc, d0 + (l & 31), l >> 5, 0));
-}
-
 // Raw buffer resource over `bytes` bytes at p: loads at byte offsets past the
 // end return zero. (Word 3 is the gfx9-family raw-buffer format.)
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* p, int bytes) {
@@ -241,6 +225,19 @@ __device__ __forceinline__ void load_tile_sw(bf16* t, const bf16* src, int nvali
   const int c = (l & 7) ^ swz(row);
   typedef __attribute__((address_space(3))) void lds_void;
   __builtin_amdgcn_raw_ptr_buffer_load_lds(buffer_rsrc(src, nvalid * 128), (lds_void*)(t + 8 * w * 64), 16,
+                                           row * 128 + 16 * c, 0, 0, 0);
+}
+
+// Rows 8 rg .. 8 rg + 7 of the same swizzled 32 x 64 tile by one direct
+// global -> LDS load of the calling wave (for workgroups of more than four
+// waves, which split a stage's tiles differently); rows at or past nvalid
+// arrive as zeros (nvalid = 0: no memory access at all).
+__device__ __forceinline__ void load_rows8_sw(bf16* t, const bf16* src, int nvalid, int rg) {
+  const int l = lane_id();
+  const int row = 8 * rg + (l >> 3);
+  const int c = (l & 7) ^ swz(row);
+  typedef __attribute__((address_space(3))) void lds_void;
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(buffer_rsrc(src, nvalid * 128), (lds_void*)(t + 8 * rg * 64), 16,
                                            row * 128 + 16 * c, 0, 0, 0);
 }
 

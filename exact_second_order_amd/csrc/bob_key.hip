@@ -33,7 +33,6 @@ namespace flashbob {
 template <typename T, int D_, bool FIRST = false>
 struct KeyCfg {
   static constexpr int D = D_;
-  static constexpr int BC = 128;                       // keys per workgroup (4 waves x 32)
   static constexpr int BQ = 32;                        // queries per LDS stage (one MFMA block)
   static constexpr int LDQ = D + 16 / (int)sizeof(T);  // padded LDS row (elements)
   static constexpr int NCH = D / 16, NDB = D / 32;
@@ -54,6 +53,12 @@ struct KeyCfg {
   // waves per SIMD leaves over (every per-block LDS read costs time)
   static constexpr int KLDS = (OCC2 && SWZ) ? 0x8 : 0;
   static constexpr int NKLDS = __builtin_popcount(KLDS);
+  // Waves per workgroup, each owning 32 keys: with two waves per SIMD at
+  // bf16 d = 64 both go in one workgroup of eight, so each Q, gQ, dO stage is
+  // fetched into LDS once per 256 keys instead of once per 128 (the chip runs
+  // these sweeps at its power limit, and that traffic costs energy per block)
+  static constexpr int NW = (OCC2 && SWZ) ? 8 : 4;
+  static constexpr int BC = 32 * NW;                   // keys per workgroup
   static constexpr int ROWLEN = SWZ ? D : LDQ;
   static constexpr int QSTAGE = 3 * BQ * ROWLEN;       // Q, gQ, dO elements of one stage
   // floats per row-scalar slot of a stage: SWZ loads a slot with one 4-byte
@@ -63,7 +68,7 @@ struct KeyCfg {
   static constexpr int SSTAGE = 4 * SLOT;              // row scalars of one stage (floats)
   // the LDS-resident key-side tiles (NKLDS per wave, 32 x D each) follow the
   // stage buffers
-  static constexpr size_t KSIDE = (size_t)4 * NKLDS * 32 * D * sizeof(T);
+  static constexpr size_t KSIDE = (size_t)NW * NKLDS * 32 * D * sizeof(T);
   static constexpr size_t STAGE_BYTES = NBUF * (QSTAGE * sizeof(T) + SSTAGE * sizeof(float));
   static constexpr size_t LDS_BYTES = STAGE_BYTES + KSIDE;
   static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
@@ -140,7 +145,8 @@ __device__ __forceinline__ void key_chunk(int cc, const f32x16& S, const f32x16&
 // FIRST: also return the first-backward dK = s dS^T Q and dV = P^T dO (two
 // more products per block against operands already read).
 template <typename T, int D, bool FIRST>
-__global__ __launch_bounds__(256, (KeyCfg<T, D, FIRST>::OCC2 ? 2 : 1)) void key_kernel(
+__global__ __launch_bounds__((KeyCfg<T, D, FIRST>::NW * 64),
+                             ((KeyCfg<T, D, FIRST>::OCC2 ? 2 : 1) * 4 / KeyCfg<T, D, FIRST>::NW)) void key_kernel(
     const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V, const T* __restrict__ dO,
     const T* __restrict__ gQ, const T* __restrict__ gK, const T* __restrict__ gV,
     const float* __restrict__ lse2, const float* __restrict__ Dv, const float* __restrict__ cv,
@@ -249,16 +255,34 @@ __global__ __launch_bounds__(256, (KeyCfg<T, D, FIRST>::OCC2 ? 2 : 1)) void key_
     const int nq = min(BQ, N - q0);
     if constexpr (SWZ) {
       const int b = n & (NBUF - 1);
-      load_tile_sw(tile(b, 0), Q + qoff + (size_t)q0 * D, nq);
-      load_tile_sw(tile(b, 1), gQ + qoff + (size_t)q0 * D, nq);
-      load_tile_sw(tile(b, 2), dO + qoff + (size_t)q0 * D, nq);
-      // wave w fetches row scalar w (LSE*log2e, -D, -c/s, -r) of the stage's
-      // queries: lane L -> row L, written at LDS float L of sS(b, w); rows past
-      // the end (and lanes 32..63) read as zero. No branch: the loop body
-      // stays one straight-line block.
+      if constexpr (Cfg::NW == 8) {
+        // wave w: rows 8 (w % 4) .. + 7 of Q and dO (w < 4), or of gQ and
+        // row scalar w % 4 (w >= 4)
+        const int rg = w & 3;
+        if (w < 4) {
+          load_rows8_sw(tile(b, 0), Q + qoff + (size_t)q0 * D, nq, rg);
+          load_rows8_sw(tile(b, 2), dO + qoff + (size_t)q0 * D, nq, rg);
+        } else {
+          load_rows8_sw(tile(b, 1), gQ + qoff + (size_t)q0 * D, nq, rg);
+        }
+      } else {
+        load_tile_sw(tile(b, 0), Q + qoff + (size_t)q0 * D, nq);
+        load_tile_sw(tile(b, 1), gQ + qoff + (size_t)q0 * D, nq);
+        load_tile_sw(tile(b, 2), dO + qoff + (size_t)q0 * D, nq);
+      }
+      // wave w (four waves) or w + 4 (eight) fetches row scalar w
+      // (LSE*log2e, -D, -c/s, -r) of the stage's queries: lane L -> row L,
+      // written at LDS float L of sS(b, w); rows past the end (and lanes
+      // 32..63) read as zero
       typedef __attribute__((address_space(3))) void lds_void;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(buffer_rsrc(stat_src + q0, nq * 4), (lds_void*)sS(b, w), 4, 4 * l,
-                                               0, 0, 0);
+      auto load_scalars = [&]() __attribute__((always_inline)) {
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(buffer_rsrc(stat_src + q0, nq * 4), (lds_void*)sS(b, w & 3), 4,
+                                                 4 * l, 0, 0, 0);
+      };
+      if constexpr (Cfg::NW == 4)
+        load_scalars();
+      else if (w >= 4)
+        load_scalars();
     } else {
       pq.load(Q + qoff + (size_t)q0 * D, nq);
       pg.load(gQ + qoff + (size_t)q0 * D, nq);
@@ -359,7 +383,7 @@ __global__ __launch_bounds__(256, (KeyCfg<T, D, FIRST>::OCC2 ? 2 : 1)) void key_
     qoff = (size_t)(head * G + g) * N * D;
     soff = (size_t)(head * G + g) * N;
     {
-      const int si = SWZ ? w : (int)(threadIdx.x / BQ) & 3;
+      const int si = SWZ ? (w & 3) : (int)(threadIdx.x / BQ) & 3;
       stat_src = (si == 0 ? lse2 : si == 1 ? Dv : si == 2 ? cv : rv) + soff;
     }
     prefetch(nstart);  // nstart < nblk; the previous member's last barrier freed both buffers
@@ -435,7 +459,7 @@ hipError_t launch_key(const void* Q, const void* K, const void* V, const void* d
   const int nkblk = (N + Cfg::BC - 1) / Cfg::BC;
   const long long nblocks = (long long)nkblk * BHkv * Cfg::OSPLIT;
   if (nblocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-  key_kernel<T, D, FIRST><<<dim3((unsigned)nblocks), dim3(256), 0, stream>>>(
+  key_kernel<T, D, FIRST><<<dim3((unsigned)nblocks), dim3(Cfg::NW * 64), 0, stream>>>(
       (const T*)Q, (const T*)K, (const T*)V, (const T*)dO, (const T*)gQ, (const T*)gK, (const T*)gV, lse2, Dv, cv,
       rv, gradK, gradV, dK, dV, N, nkblk, scale, causal, G, out_bf16);
   return hipGetLastError();

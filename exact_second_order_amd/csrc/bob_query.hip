@@ -39,10 +39,12 @@
 
 namespace flashbob {
 
-template <typename T, int D_, bool GRADQ>
+#ifndef FLASHBOB_PASS1_WIDE
+#define FLASHBOB_PASS1_WIDE 0
+#endif
+template <typename T, int D_, bool GRADQ, bool FIRST = false>
 struct QueryCfg {
   static constexpr int D = D_;
-  static constexpr int BQ = 128;                       // queries per workgroup (4 waves x 32)
   static constexpr int BK = 32;                        // keys per LDS stage (one MFMA block)
   static constexpr int LDK = D + 16 / (int)sizeof(T);  // padded LDS row (elements)
   static constexpr int NCH = D / 16;                   // 16-wide k chunks over d
@@ -66,7 +68,14 @@ struct QueryCfg {
   // loop spill-free; a few values spill around the masked blocks and the
   // epilogue) and runs three, which hides more of each wave's exp and MFMA
   // latency than two
-  static constexpr int OCC = (!GRADQ && SWZ) ? 3 : OCC2 ? 2 : 1;
+  // Waves per workgroup, each owning 32 queries: bf16 d = 64 pass 2q runs
+  // eight (the two waves of each SIMD in one workgroup), so each K, gK, V, gV
+  // stage is fetched into LDS once per 256 queries instead of once per 128:
+  // the chip runs these sweeps at its power limit, and the global -> LDS
+  // traffic is a measurable part of the energy per block.
+  static constexpr int NW = (SWZ && !FIRST && (GRADQ || FLASHBOB_PASS1_WIDE)) ? 8 : 4;
+  static constexpr int BQ = 32 * NW;                   // queries per workgroup
+  static constexpr int OCC = (!GRADQ && SWZ && NW == 4) ? 3 : OCC2 ? 2 : 1;
   static constexpr int NBUF = 2;                       // stage n in use, stage n+1 arriving
   static constexpr int STAGE = 4 * BK * (SWZ ? D : LDK);  // elements of one stage
   static constexpr size_t LDS_BYTES = NBUF * STAGE * sizeof(T);
@@ -190,84 +199,20 @@ __device__ __forceinline__ void query_chunk(int cc, const f32x16& S, const f32x1
   to_frag(fA, A);
 }
 
-// The same step for bf16 operands, done in place on a whole tile: the
-// results of chunk cc are rounded pair by pair and written back into the
-// tiles' own registers, P into S, dS into dP, A into G and dS2 into H, at
-// words 8 cc .. 8 cc + 3 (pair s2 of chunk cc reads words 8 cc + 2 s2, + 1
-// and writes word 8 cc + s2, which an earlier or the same pair has already
-// read). A chunk's bf16 operand fragments are then those four words of each
-// tile, and no separate fragment registers are live.
-// The step runs over both chunks as eight pair steps k = 0..7 (chunk k / 4,
-// pair k % 4). Before step k it calls hook(k), with scheduling barriers
-// around, so whatever the hook issues is spread over the work; each step
-// also starts the two exponentials of step k + 1, so no step waits for the
-// latency of its own.
-template <bool TAIL, typename Hook>
-__device__ __forceinline__ void query_tile_inplace(f32x16& S, f32x16& G, f32x16& dP, f32x16& H, float sl2,
-                                                   float scale, float l2, float Dq, float cq, float rq,
-                                                   int nvalid_rel, Hook&& hook) {
-  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-  typedef float f32x2_t __attribute__((ext_vector_type(2)));
-  auto pack = [](float a, float b) __attribute__((always_inline)) {
-    return __builtin_bit_cast(float, __builtin_convertvector((f32x2_t){a, b}, bf16x2_t));
-  };
-  // (row acc_row(h, i) = acc_row(0, i) + 4 h: the mask compares the
-  // compile-time acc_row(0, i) against one per-lane bound)
-  const int nr = nvalid_rel - 4 * (lane_id() >> 5);
-  auto word = [](int k, int e) { return 8 * (k >> 2) + 2 * (k & 3) + e; };  // tile word of pair k, element e
-  float ex[2];
-#pragma unroll
-  for (int e = 0; e < 2; ++e) ex[e] = fast_exp2(fmaf(S[word(0, e)], sl2, -l2));
-#pragma unroll
-  for (int k = 0; k < 8; ++k) {
-    __builtin_amdgcn_sched_barrier(0);
-    hook(k);
-    __builtin_amdgcn_sched_barrier(0);
-    float pe[2] = {ex[0], ex[1]};
-    if (k < 7) {
-#pragma unroll
-      for (int e = 0; e < 2; ++e) ex[e] = fast_exp2(fmaf(S[word(k + 1, e)], sl2, -l2));
-    }
-    float vp[2], vds[2], va[2], vd2[2];
-#pragma unroll
-    for (int e = 0; e < 2; ++e) {
-      const int i = word(k, e);
-      float p = pe[e];
-      if (TAIL && acc_row(0, i) >= nr) p = 0.f;
-      const float ds = p * (dP[i] + Dq);
-      const float g = fmaf(G[i], scale, cq);
-      vp[e] = p;
-      vds[e] = ds;
-      va[e] = p * g;
-      vd2[e] = fmaf(ds, g, p * (H[i] + rq));
-    }
-    // word 8 (k / 4) + k % 4: read by this or an earlier pair already
-    const int o = 8 * (k >> 2) + (k & 3);
-    S[o] = pack(vp[0], vp[1]);
-    dP[o] = pack(vds[0], vds[1]);
-    G[o] = pack(va[0], va[1]);
-    H[o] = pack(vd2[0], vd2[1]);
-  }
-}
-
-// Words 8 cc .. 8 cc + 3 of a tile as a bf16 operand fragment.
-__device__ __forceinline__ bf16x8 packed_frag(const f32x16& t, int cc) {
-  return __builtin_bit_cast(bf16x8, cc == 0 ? __builtin_shufflevector(t, t, 0, 1, 2, 3)
-                                            : __builtin_shufflevector(t, t, 8, 9, 10, 11));
-}
-
 // FIRST (pass 2q only): also return the first-backward dQ = s dS K (one more
 // product per block against the K^T operand already read; the extra
 // accumulator needs the one-wave-per-SIMD register budget).
 template <typename T, int D, bool GRADQ, bool FIRST, bool SAVED>
-__global__ __launch_bounds__(256, (FIRST ? 1 : QueryCfg<T, D, GRADQ>::OCC)) void query_kernel(
+__global__ __launch_bounds__((QueryCfg<T, D, GRADQ, FIRST>::NW * 64),
+                             ((FIRST ? 1 : QueryCfg<T, D, GRADQ, FIRST>::OCC) * 4 / QueryCfg<T, D, GRADQ, FIRST>::NW))
+void query_kernel(
     const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V, const T* __restrict__ dO,
     const T* __restrict__ gQ, const T* __restrict__ gK, const T* __restrict__ gV, float* __restrict__ lse,
     float* __restrict__ Dv, float* __restrict__ cv, float* __restrict__ rv, void* __restrict__ gradQ,
     void* __restrict__ graddO, void* __restrict__ dQo, const float* __restrict__ lse_in, int N, int nqblk,
     float scale, int lse_natural, int causal, int G, int out_bf16) {
   static_assert(!(SAVED && GRADQ), "a saved log-sum-exp replaces pass 1's running maximum only");
-  using Cfg = QueryCfg<T, D, GRADQ>;
+  using Cfg = QueryCfg<T, D, GRADQ, FIRST>;
   using E = Elem<T>;
   using F = typename E::frag;
   constexpr int BK = Cfg::BK, LDK = Cfg::LDK, NCH = Cfg::NCH, NDB = Cfg::NDB, NBUF = Cfg::NBUF;
@@ -378,7 +323,13 @@ __global__ __launch_bounds__(256, (FIRST ? 1 : QueryCfg<T, D, GRADQ>::OCC)) void
   auto prefetch = [&](int n) __attribute__((always_inline)) {
     const int k0 = n < nvis ? n * BK : 0;
     const int nk = n < nvis ? min(BK, N - k0) : 0;
-    if constexpr (SWZ) {
+    if constexpr (SWZ && Cfg::NW == 8) {
+      // wave w: rows 8 (w % 4) .. + 7 of K and V (w < 4) or of gK and gV
+      const int b = n & (NBUF - 1);
+      const int rg = w & 3;
+      load_rows8_sw(tile(b, w >> 2), (w < 4 ? K : gK) + koff + (size_t)k0 * D, nk, rg);
+      load_rows8_sw(tile(b, 2 + (w >> 2)), (w < 4 ? V : gV) + koff + (size_t)k0 * D, nk, rg);
+    } else if constexpr (SWZ) {
       const int b = n & (NBUF - 1);
       load_tile_sw(tile(b, 0), K + koff + (size_t)k0 * D, nk);
       load_tile_sw(tile(b, 1), gK + koff + (size_t)k0 * D, nk);
@@ -567,379 +518,16 @@ __global__ __launch_bounds__(256, (FIRST ? 1 : QueryCfg<T, D, GRADQ>::OCC)) void
   }
 }
 
-// ---------------------------------------------------------------------------
-// Pass 2q for bf16 inputs at d = 64 as a two-role ("ping-pong") schedule.
-//
-// A workgroup of 8 waves owns 128 queries. Waves w and w + 4 (which the
-// dispatcher places on one SIMD) hold the same 32 queries and take alternate
-// 32-key blocks: wave group g = w / 4 owns the blocks n with n % 2 == g. Time
-// runs in phases separated by workgroup barriers. In phase p the group with
-// p % 2 == g is the matrix group: it issues the output products of its block
-// p - 2 and the recompute products of its block p. The other group runs the
-// elementwise step (exp, affine maps, bf16 packing) of its block p - 1. On
-// every SIMD one wave thus feeds the matrix core while the other does the
-// VALU work, instead of each wave alternating between the two on its own.
-// The two waves' partial gradQ^T, graddO^T are summed through LDS at the end.
-//
-// Block n's K, gK, V, gV rows are read in phase n (recompute) and their
-// row-transposed copies (tposed_pos layout, prepared by bob_prep.hip) in phase
-// n + 2 (output products, one 16-byte LDS read per operand). The owner group
-// loads the rows in phase n - 2 and the transposed copies in phase n, each
-// into its own two-slot ring, and waits for them at the end of its next
-// (VALU) phase.
-struct QueryPP {
-  static constexpr int D = 64, BQ = 128, BK = 32, NCH = 4, NDB = 2;
-  static constexpr int TILE = BK * D;  // elements of one 32 x 64 tile (4 KB)
-  // LDS: two rings of [2 groups][2 slots][K, gK, V, gV] tiles, the rows of the
-  // blocks being recomputed and the row-transposed blocks (tposed_pos layout)
-  // of the blocks whose output products are due, then the workgroup's gQ rows
-  // as four swizzled tiles (read as recompute operands, which frees their
-  // registers): 64 + 64 + 16 KB
-  static constexpr int RING = 2 * 2 * 4 * TILE;
-  static constexpr size_t LDS_BYTES = (2 * RING + 4 * TILE) * sizeof(bf16);
-  static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
-  // the final exchange of partial accumulators reuses the rings
-  static_assert(4 * 2 * NDB * 16 * 64 * sizeof(float) <= 2 * RING * sizeof(bf16), "exchange fits the rings");
-};
-
-// One 1 KB piece (i = 0..3) of a contiguous 4 KB block by one direct
-// global -> LDS load of this wave; nothing arrives from past `bytes` (zeros).
-__device__ __forceinline__ void load_1k(bf16* t, const bf16* src, int bytes, int i) {
-  typedef __attribute__((address_space(3))) void lds_void;
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(buffer_rsrc(src, bytes), (lds_void*)(t + 512 * i), 16,
-                                           1024 * i + 16 * lane_id(), 0, 0, 0);
-}
-
-// Rows 8 rg .. 8 rg + 7 of a swizzled 32 x 64 bf16 tile by one direct
-// global -> LDS load of this wave (the layout of load_tile_sw); rows at or
-// past nvalid arrive as zeros (nvalid = 0: no memory access at all).
-__device__ __forceinline__ void load_rows8_sw(bf16* t, const bf16* src, int nvalid, int rg) {
-  const int l = lane_id();
-  const int row = 8 * rg + (l >> 3);
-  const int c = (l & 7) ^ swz(row);
-  typedef __attribute__((address_space(3))) void lds_void;
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(buffer_rsrc(src, nvalid * 128), (lds_void*)(t + 8 * rg * 64), 16,
-                                           row * 128 + 16 * c, 0, 0, 0);
-}
-
-template <int D_>
-__global__ __launch_bounds__(512, 1) void query2_pp_kernel(
-    const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
-    const bf16* __restrict__ dO, const bf16* __restrict__ gQ, const bf16* __restrict__ gK,
-    const bf16* __restrict__ gV, const bf16* __restrict__ kT, size_t tstride, const float* __restrict__ lse,
-    const float* __restrict__ Dv, const float* __restrict__ cv, const float* __restrict__ rv,
-    void* __restrict__ gradQ, void* __restrict__ graddO, int N, int nqblk, float scale, int causal, int G,
-    int out_bf16) {
-  using C = QueryPP;
-  static_assert(D_ == C::D, "laid out for d = 64");
-  using F = bf16x8;
-  using E = Elem<bf16>;
-  constexpr int BK = C::BK, NCH = C::NCH, NDB = C::NDB, D = C::D;
-  __shared__ __attribute__((aligned(16))) bf16 smem[C::LDS_BYTES / sizeof(bf16)];
-  // ring slot of block n: owner group n % 2, slot (n / 2) % 2 (n may be
-  // negative in the pipeline's fill: blocks -2, -1 map to slot 1)
-  auto slot = [&](int n) __attribute__((always_inline)) { return ((n & 1) * 2 + ((n >> 1) & 1)) * 4; };
-  auto rtile = [&](int n, int t) __attribute__((always_inline)) { return smem + (slot(n) + t) * C::TILE; };
-  auto ttile = [&](int n, int t) __attribute__((always_inline)) {
-    return smem + C::RING + (slot(n) + t) * C::TILE;
-  };
-  bf16* const sgq = smem + 2 * C::RING + C::TILE * (threadIdx.x >> 6 & 3);  // this wave's gQ rows
-
-  const unsigned bid = blockIdx.x;
-  const int nheads = (int)(gridDim.x / nqblk);
-  const int head = causal ? (int)(bid % nheads) : (int)(bid / nqblk);
-  const int qblk = causal ? nqblk - 1 - (int)(bid / nheads) : (int)(bid % nqblk);
-  const size_t hoff = (size_t)head * N * D;        // query head
-  const size_t koff = (size_t)(head / G) * N * D;  // its key/value head
-  const int w = wave_id(), grp = w >> 2, wq = w & 3, l = lane_id(), h = l >> 5, col = l & 31;
-  const int q = qblk * C::BQ + 32 * wq + col;  // this lane's query
-  const bool qvalid = q < N;
-  const int qlim = causal ? min(N, q + 1) : N;  // keys [0, qlim) are visible to it
-
-  F fQ[NCH], fdO[NCH];
-  {
-    const bf16* rq = Q + hoff + (size_t)q * D;
-    const bf16* rgq = gQ + hoff + (size_t)q * D;
-    const bf16* rdo = dO + hoff + (size_t)q * D;
-#pragma unroll
-    for (int c = 0; c < NCH; ++c) {
-      fQ[c] = load_row_frag(rq, qvalid, c);
-      fdO[c] = load_row_frag(rdo, qvalid, c);
-      // gQ goes to LDS in the layout ld_rows_sw reads back (group 0 writes it;
-      // both groups read it after the first barrier)
-      if (grp == 0)
-        *reinterpret_cast<F*>(const_cast<bf16*>(sw_addr(sgq, col, 16 * c + 8 * h))) = load_row_frag(rgq, qvalid, c);
-    }
-  }
-  const float sl2 = scale * kLog2e;
-  // row scalars in pass-2 form: LSE log2(e), -D, -c (= s * (-c/s)), -r
-  float l2 = INFINITY, Dq = 0.f, cq = 0.f, rq = 0.f;
-  if (qvalid) {
-    const size_t o = (size_t)head * N + q;
-    l2 = lse[o];
-    Dq = Dv[o];
-    cq = scale * cv[o];
-    rq = rv[o];
-  }
-  f32x16 accQ[NDB], accO[NDB];
-#pragma unroll
-  for (int j = 0; j < NDB; ++j) {
-    accQ[j] = f32x16{};
-    accO[j] = f32x16{};
-  }
-
-  const int nblk = (N + BK - 1) / BK;
-  const int q0 = qblk * C::BQ;
-  const int nvis = causal ? min(nblk, (q0 + C::BQ + BK - 1) / BK) : nblk;
-  const int nfull = causal ? min(nvis, q0 / BK) : (N % BK != 0 ? nblk - 1 : nblk);
-
-  // Stage loads: wave wq of the loading group fetches tensor wq (K, gK, V,
-  // gV), four direct global -> LDS loads of rows (issue_rows) or of the
-  // row-transposed block (issue_tposed) into the owner group's ring slot;
-  // blocks outside [0, nvis) arrive as zeros.
-  const bf16* const lsrc = (wq == 0 ? K : wq == 1 ? gK : wq == 2 ? V : gV) + koff;
-  const int nblk_all = (N + BK - 1) / BK;  // blocks per head in the transposed copies
-  const bf16* const tsrc = kT + (size_t)wq * tstride + (size_t)(head / G) * nblk_all * C::TILE;
-  auto issue_rows = [&](int n, int rg) __attribute__((always_inline)) {  // rows 8 rg .. 8 rg + 7
-    const bool in = n < nvis;
-    const int k0 = in ? n * BK : 0;
-    const int nk = in ? min(BK, N - k0) : 0;
-    load_rows8_sw(rtile(n, wq), lsrc + (size_t)k0 * D, nk, rg);
-  };
-  auto issue_tposed = [&](int n, int i) __attribute__((always_inline)) {  // 1 KB piece i
-    const bool in = n >= 0 && n < nvis;
-    load_1k(ttile(n, wq), tsrc + (size_t)(in ? n : 0) * C::TILE, in ? 4096 : 0, i);
-  };
-
-  // S^T, G^T, dP^T, H^T of a block (keys x this wave's queries); after the
-  // elementwise step their first words hold the bf16 operand fragments
-  struct Tiles {
-    f32x16 S, G, dP, H;
-  };
-  // The matrix role of phase p: the output products of block p - 2, then the
-  // loads of stage p + 2, then the recompute products of block p. Each group
-  // of MFMAs is issued only after the LDS reads of the next group's operands
-  // (the order pinned with sched_group_barrier), so the LDS latency of one
-  // group runs under the MFMAs of the one before.
-  struct OOps {  // A operands of one (16-key chunk, 32-row d block) group: lane <-> d, k over keys
-    F k, gk, v, gv;
-  };
-  struct ROps {  // operands of one 16-wide d chunk of the recompute
-    F k, gk, v, gv, gq;
-  };
-  auto matrix = [&](int p, Tiles& t) __attribute__((always_inline)) {
-    const bf16* o0 = ttile(p - 2, 0);
-    const bf16* o1 = ttile(p - 2, 1);
-    const bf16* o2 = ttile(p - 2, 2);
-    const bf16* o3 = ttile(p - 2, 3);
-    const bf16* r0 = rtile(p, 0);
-    const bf16* r1 = rtile(p, 1);
-    const bf16* r2 = rtile(p, 2);
-    const bf16* r3 = rtile(p, 3);
-    auto oload = [&](int g) __attribute__((always_inline)) {
-      const int cc = g >> 1, jd = 32 * (g & 1);
-      return OOps{ld_tposed(o0, cc, jd), ld_tposed(o1, cc, jd), ld_tposed(o2, cc, jd), ld_tposed(o3, cc, jd)};
-    };
-    auto rload = [&](int c) __attribute__((always_inline)) {
-      return ROps{ld_rows_sw(r0, 0, c), ld_rows_sw(r1, 0, c), ld_rows_sw(r2, 0, c), ld_rows_sw(r3, 0, c),
-                  ld_rows_sw(sgq, 0, c)};
-    };
-    // output products: gradQ^T / s += K^T dS2 + gK^T dS, graddO^T += V^T A + gV^T P
-    OOps ob[2];
-    ROps rb[2];
-    ob[0] = oload(0);
-    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      if (g < 3)
-        ob[(g + 1) & 1] = oload(g + 1);
-      else
-        rb[0] = rload(0);
-      const int cc = g >> 1, j = g & 1;
-      const OOps& o = ob[g & 1];
-      E::mma(accQ[j], o.k, packed_frag(t.H, cc));   // dS2
-      E::mma(accQ[j], o.gk, packed_frag(t.dP, cc));  // dS
-      E::mma(accO[j], o.v, packed_frag(t.G, cc));   // A
-      E::mma(accO[j], o.gv, packed_frag(t.S, cc));  // P
-        if (g < 3)
-        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
-      else
-        __builtin_amdgcn_sched_group_barrier(0x100, 5, 0);
-      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    // recompute S^T, G^T, dP^T, H^T of block p
-    t.S = f32x16{};
-    t.G = f32x16{};
-    t.dP = f32x16{};
-    t.H = f32x16{};
-#pragma unroll
-    for (int c = 0; c < NCH; ++c) {
-      if (c < NCH - 1) rb[(c + 1) & 1] = rload(c + 1);
-      const ROps& r = rb[c & 1];
-      E::mma(t.S, r.k, fQ[c]);
-      E::mma(t.G, r.k, r.gq);
-      E::mma(t.G, r.gk, fQ[c]);
-      E::mma(t.dP, r.v, fdO[c]);
-      E::mma(t.H, r.gv, fdO[c]);
-      if (c < NCH - 1) __builtin_amdgcn_sched_group_barrier(0x100, 5, 1);
-      __builtin_amdgcn_sched_group_barrier(0x008, 5, 1);
-    }
-  };
-  // elementwise step of block n into operand fragments; blocks outside
-  // [0, nvis) (the pipeline's fill and drain) come out as zeros
-  // (hook(k), k = 0..7, runs before the k-th of its eight pair steps)
-  auto elementwise = [&](auto tail, int n, Tiles& t, auto&& hook) __attribute__((always_inline)) {
-    constexpr bool TAIL = decltype(tail)::value;
-    const int nrel = (n < 0 || n >= nvis) ? 0 : qlim - n * BK;
-    query_tile_inplace<TAIL>(t.S, t.G, t.dP, t.H, sl2, scale, l2, Dq, cq, rq, nrel, hook);
-  };
-  using F0 = std::integral_constant<bool, false>;
-  using F1 = std::integral_constant<bool, true>;
-  // Phase boundary: a bare s_barrier (a __syncthreads() would also wait for
-  // the stage loads still in flight), with compiler memory barriers so no
-  // memory access moves across it. After a matrix phase the wave first waits
-  // for the stage loads it issued in its VALU phase before.
-  auto barrier = [&](auto wait_loads) __attribute__((always_inline)) {
-    __builtin_amdgcn_sched_barrier(0);
-    if constexpr (decltype(wait_loads)::value) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_sched_barrier(0);
-  };
-  // One phase. Every phase does its full work, so the loop body is straight
-  // code: the fill phases multiply zero fragments against zeroed ring slots,
-  // the drain phases recompute zero stages and mask their elementwise steps.
-  // The VALU group of phase p issues the loads the matrix group needs two
-  // phases later (rows of block p + 2, the transposed block p), spread over
-  // its elementwise work: each load takes the issuing wave tens of cycles,
-  // which the matrix waves cannot spare.
-  Tiles t{};  // zero: the first output products add nothing
-  auto phase = [&](auto mrole, int p) __attribute__((always_inline)) {
-    if constexpr (decltype(mrole)::value) {
-      matrix(p, t);
-      barrier(F1{});
-    } else {
-      // the eight loads, one before each pair step of the elementwise work:
-      // issued in a burst they would stall this wave (in-order issue) until
-      // the vector memory path has taken them all
-      auto loads = [&](int k) __attribute__((always_inline)) {
-        if (k < 4)
-          issue_rows(p + 2, k);
-        else
-          issue_tposed(p, k - 4);
-      };
-      const int n = p - 1;
-      if (n >= 0 && n < nfull)
-        elementwise(F0{}, n, t, loads);
-      else
-        elementwise(F1{}, n, t, loads);
-      barrier(F0{});
-    }
-  };
-
-  // the transposed slots of blocks -2 and -1 are read by the fill phases'
-  // output products before any block lands there: zero them
-  {
-    typedef __attribute__((__vector_size__(16))) int v4i;
-    for (int g = 0; g < 2; ++g) {
-      v4i* z = reinterpret_cast<v4i*>(ttile(g - 2, 0));
-      for (int i = threadIdx.x; i < 4 * C::TILE * (int)sizeof(bf16) / 16; i += 512) z[i] = v4i{};
-    }
-  }
-#pragma unroll
-  for (int rg = 0; rg < 4; ++rg) issue_rows(grp, rg);  // blocks 0 and 1 (each group its own)
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();
-  // phases 0 .. nph - 1 (an even count covering the recompute of blocks
-  // 0 .. nvis - 1 at phase n, their elementwise steps at n + 1 and their
-  // output products at n + 2); each group runs its own loop of
-  // (matrix, VALU) or (VALU, matrix) phase pairs
-  const int nph = (nvis + 3) & ~1;
-  auto run = [&](auto g0) __attribute__((always_inline)) {
-    constexpr bool G0 = decltype(g0)::value;
-    for (int p = 0; p < nph; p += 2) {
-      phase(std::integral_constant<bool, G0>{}, p);
-      phase(std::integral_constant<bool, !G0>{}, p + 1);
-    }
-  };
-  if (grp == 0)
-    run(F1{});
-  else
-    run(F0{});
-  // the drain phases' zero-stage loads may still be landing in the ring,
-  // which the exchange below reuses
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();
-
-  // Sum the two groups' partial accumulators through LDS (the stage ring is
-  // free now): group 1 hands over its gradQ^T part, group 0 its graddO^T part;
-  // each group then finishes and stores one of the two outputs.
-  float* xch = reinterpret_cast<float*>(smem);
-  float* mine = xch + (size_t)(wq * 2 + grp) * (NDB * 16 * 64);  // [NDB*4][64 lanes][4]
-  const float* theirs = xch + (size_t)(wq * 2 + (grp ^ 1)) * (NDB * 16 * 64);
-  auto give = [&](const f32x16(&a)[NDB]) __attribute__((always_inline)) {
-#pragma unroll
-    for (int j = 0; j < NDB; ++j)
-#pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        const f32x4 v = {a[j][4 * g4], a[j][4 * g4 + 1], a[j][4 * g4 + 2], a[j][4 * g4 + 3]};
-        *reinterpret_cast<f32x4*>(mine + ((j * 4 + g4) * 64 + l) * 4) = v;
-      }
-  };
-  // a[j] slot i holds d = 32 j + acc_row(h, i) of this lane's query
-  auto finish = [&](f32x16(&a)[NDB], void* out, float os) __attribute__((always_inline)) {
-#pragma unroll
-    for (int j = 0; j < NDB; ++j)
-#pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        const f32x4 v = *reinterpret_cast<const f32x4*>(theirs + ((j * 4 + g4) * 64 + l) * 4);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) a[j][4 * g4 + e] += v[e];
-      }
-    if (qvalid) {
-      const size_t row = hoff + (size_t)q * D;
-#pragma unroll
-      for (int j = 0; j < NDB; ++j)
-#pragma unroll
-        for (int g4 = 0; g4 < 4; ++g4) {
-          const int d0 = 32 * j + 8 * g4 + 4 * h;
-          store_out4(out, row + d0, os * a[j][4 * g4], os * a[j][4 * g4 + 1], os * a[j][4 * g4 + 2],
-                     os * a[j][4 * g4 + 3], out_bf16);
-        }
-    }
-  };
-  if (grp == 0)
-    give(accO);
-  else
-    give(accQ);
-  __syncthreads();
-  if (grp == 0)
-    finish(accQ, gradQ, scale);
-  else
-    finish(accO, graddO, 1.f);
-}
-
 template <typename T, int D, bool GRADQ, bool FIRST, bool SAVED>
 hipError_t launch_query(const void* Q, const void* K, const void* V, const void* dO, const void* gQ,
                         const void* gK, const void* gV, float* lse, float* Dv, float* cv, float* rv,
-                        void* gradQ, void* graddO, void* dQ, const float* lse_in, const bf16* kT, size_t tstride,
-                        int BH, int N, float scale, int lse_natural, int causal, int G, int out_bf16,
-                        hipStream_t stream) {
-  using Cfg = QueryCfg<T, D, GRADQ>;
+                        void* gradQ, void* graddO, void* dQ, const float* lse_in, int BH, int N, float scale,
+                        int lse_natural, int causal, int G, int out_bf16, hipStream_t stream) {
+  using Cfg = QueryCfg<T, D, GRADQ, FIRST>;
   const int nqblk = (N + Cfg::BQ - 1) / Cfg::BQ;
   const long long nblocks = (long long)nqblk * BH * Cfg::OSPLIT;
   if (nblocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-  // bf16 d = 64 pass 2q with the row-transposed key-side copies at hand: the
-  // two-role kernel (otherwise the general one below)
-  if constexpr (std::is_same_v<T, bf16> && D == 64 && GRADQ && !FIRST) if (kT != nullptr) {
-    query2_pp_kernel<D><<<dim3((unsigned)nblocks), dim3(512), 0, stream>>>(
-        (const bf16*)Q, (const bf16*)K, (const bf16*)V, (const bf16*)dO, (const bf16*)gQ, (const bf16*)gK,
-        (const bf16*)gV, kT, tstride, lse, Dv, cv, rv, gradQ, graddO, N, nqblk, scale, causal, G, out_bf16);
-    return hipGetLastError();
-  }
-  query_kernel<T, D, GRADQ, FIRST, SAVED><<<dim3((unsigned)nblocks), dim3(256), 0, stream>>>(
+  query_kernel<T, D, GRADQ, FIRST, SAVED><<<dim3((unsigned)nblocks), dim3(Cfg::NW * 64), 0, stream>>>(
       (const T*)Q, (const T*)K, (const T*)V, (const T*)dO, (const T*)gQ, (const T*)gK, (const T*)gV, lse, Dv,
       cv, rv, gradQ, graddO, dQ, lse_in, N, nqblk, scale, lse_natural, causal, G, out_bf16);
   return hipGetLastError();
@@ -948,9 +536,8 @@ hipError_t launch_query(const void* Q, const void* K, const void* V, const void*
 #define FLASHBOB_INST_QUERY(T, D, G, F, S)                                                                \
   template hipError_t launch_query<T, D, G, F, S>(const void*, const void*, const void*, const void*,      \
                                                   const void*, const void*, const void*, float*, float*,   \
-                                                  float*, float*, void*, void*, void*, const float*,       \
-                                                  const bf16*, size_t, int, int, float, int, int, int, int, \
-                                                  hipStream_t);
+                                                  float*, float*, void*, void*, void*, const float*, int,  \
+                                                  int, float, int, int, int, int, hipStream_t);
 // Pass 1 and pass 2q instantiations are built as separate objects (pass 1
 // with MFMA results kept in VGPRs, which its register budget allows).
 // Pass 1: plain and with a saved log-sum-exp; pass 2q: plain and with the

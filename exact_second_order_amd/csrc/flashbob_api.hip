@@ -19,11 +19,8 @@ typedef __bf16 bf16;
 template <typename T, int D, bool GRADQ, bool FIRST, bool SAVED>
 hipError_t launch_query(const void* Q, const void* K, const void* V, const void* dO, const void* gQ,
                         const void* gK, const void* gV, float* lse, float* Dv, float* cv, float* rv,
-                        void* gradQ, void* graddO, void* dQ, const float* lse_in, const bf16* kT, size_t tstride,
-                        int BH, int N, float scale, int lse_natural, int causal, int G, int out_bf16,
-                        hipStream_t stream);
-hipError_t launch_transpose_blocks(const bf16* const* src, bf16* const* dst, int n, int slices, int N,
-                                   hipStream_t stream);
+                        void* gradQ, void* graddO, void* dQ, const float* lse_in, int BH, int N, float scale,
+                        int lse_natural, int causal, int G, int out_bf16, hipStream_t stream);
 template <typename T, int D, bool FIRST>
 hipError_t launch_key(const void* Q, const void* K, const void* V, const void* dO, const void* gQ, const void* gK,
                       const void* gV, const float* lse2, const float* Dv, const float* cv, const float* rv,
@@ -102,8 +99,6 @@ struct Call {
   int stages, causal;
   const float* lse_in;  // the rows' saved log-sum-exp for pass 1, or null
   float* stats;         // workspace: [4][B*H*N] row scalars
-  __bf16* tposed;       // workspace (bf16, d = 64, if large enough): row-transposed K, gK, V, gV, or null
-  size_t tstride;       // elements between those four tensors
   void *gradQ, *gradK, *gradV, *graddO;
   void *dQ, *dK, *dV;   // first-backward outputs, or null
   int out_bf16;         // outputs stored as bf16 instead of float32
@@ -122,34 +117,23 @@ hipError_t run_stages(const void* const* in, const Call& c) {
   if (c.stages & kPass1) {
     e = c.lse_in ? flashbob::launch_query<T, D, false, false, true>(in[0], in[1], in[2], in[3], in[4], in[5], in[6],
                                                                     lse, Dv, cv, rv, nullptr, nullptr, nullptr,
-                                                                    c.lse_in, nullptr, 0, c.BH, c.N, c.scale, 0,
-                                                                    c.causal, c.G, 0, c.stream)
+                                                                    c.lse_in, c.BH, c.N, c.scale, 0, c.causal, c.G,
+                                                                    0, c.stream)
                  : flashbob::launch_query<T, D, false, false, false>(in[0], in[1], in[2], in[3], in[4], in[5],
                                                                      in[6], lse, Dv, cv, rv, nullptr, nullptr,
-                                                                     nullptr, nullptr, nullptr, 0, c.BH, c.N,
-                                                                     c.scale, 0, c.causal, c.G, 0, c.stream);
+                                                                     nullptr, nullptr, c.BH, c.N, c.scale, 0,
+                                                                     c.causal, c.G, 0, c.stream);
     if (e != hipSuccess) return e;
-  }
-  // bf16 at d = 64 with a full-size workspace: pass 2q contracts row-transposed
-  // copies of K, gK, V, gV (of the key/value heads), written there first
-  constexpr bool kTposed = std::is_same_v<T, __bf16> && D == 64;
-  const __bf16* kT = nullptr;
-  if (kTposed && (c.stages & kPass2Query) && !first && c.tposed != nullptr) {
-    const __bf16* src[4] = {(const __bf16*)in[1], (const __bf16*)in[5], (const __bf16*)in[2], (const __bf16*)in[6]};
-    __bf16* dst[4] = {c.tposed, c.tposed + c.tstride, c.tposed + 2 * c.tstride, c.tposed + 3 * c.tstride};
-    e = flashbob::launch_transpose_blocks(src, dst, 4, c.BH / c.G, c.N, c.stream);
-    if (e != hipSuccess) return e;
-    kT = c.tposed;
   }
   if (c.stages & kPass2Query) {
     e = first ? flashbob::launch_query<T, D, true, true, false>(in[0], in[1], in[2], in[3], in[4], in[5], in[6],
                                                                 lse, Dv, cv, rv, c.gradQ, c.graddO, c.dQ, nullptr,
-                                                                nullptr, 0, c.BH, c.N, c.scale, 0, c.causal, c.G,
-                                                                c.out_bf16, c.stream)
+                                                                c.BH, c.N, c.scale, 0, c.causal, c.G, c.out_bf16,
+                                                                c.stream)
               : flashbob::launch_query<T, D, true, false, false>(in[0], in[1], in[2], in[3], in[4], in[5], in[6],
                                                                  lse, Dv, cv, rv, c.gradQ, c.graddO, nullptr,
-                                                                 nullptr, kT, c.tstride, c.BH, c.N, c.scale, 0,
-                                                                 c.causal, c.G, c.out_bf16, c.stream);
+                                                                 nullptr, c.BH, c.N, c.scale, 0, c.causal, c.G,
+                                                                 c.out_bf16, c.stream);
     if (e != hipSuccess) return e;
   }
   if (c.stages & kPass2Key) {
@@ -198,8 +182,8 @@ template <typename T, int D>
 hipError_t rowstats_launch(const void* const* in, float* lse, float* Dv, float* cv, float* rv, int BH, int G,
                            int N, float scale, int causal, hipStream_t st) {
   return flashbob::launch_query<T, D, false, false, false>(in[0], in[1], in[2], in[3], in[4], in[5], in[6], lse,
-                                                           Dv, cv, rv, nullptr, nullptr, nullptr, nullptr, nullptr, 0,
-                                                           BH, N, scale, 1, causal, G, 0, st);
+                                                           Dv, cv, rv, nullptr, nullptr, nullptr, nullptr, BH, N,
+                                                           scale, 1, causal, G, 0, st);
 }
 
 hipError_t dispatch_rowstats(int dtype, int d, int causal, const void* const* in, float* lse, float* Dv, float* cv,
@@ -226,14 +210,6 @@ void tensor_bytes(size_t numel_q, size_t numel_kv, size_t esz, size_t* in_bytes)
 size_t stats_bytes(int B, int H, int N) {
   const size_t raw = (size_t)4 * sizeof(float) * (size_t)B * (size_t)H * (size_t)N;
   return (raw + 255) & ~(size_t)255;
-}
-
-// Row-transposed copies the bf16 d = 64 pass 2q reads (K, gK, V, gV of up to
-// B*H heads, ceil(N/32) blocks of 32 x 64 each), after the row scalars; 0 for
-// other head dims.
-size_t tposed_elems(int B, int H, int N) { return (size_t)B * H * (size_t)((N + 31) / 32) * 2048; }
-size_t tposed_bytes(int B, int H, int N, int d) {
-  return d == 64 ? ((4 * tposed_elems(B, H, N) * sizeof(__bf16) + 255) & ~(size_t)255) : 0;
 }
 
 // Static row-scalar buffer of flashbob_bob_noalloc: one copy per GPU the
@@ -271,11 +247,7 @@ int scratch_on_current_device(void** out) {
 extern "C" {
 
 size_t flashbob_workspace_bytes(int B, int H, int N, int d) {
-  if (B <= 0 || H <= 0 || N <= 0) return 0;
-  return stats_bytes(B, H, N) + tposed_bytes(B, H, N, d);
-}
-
-size_t flashbob_workspace_min_bytes(int B, int H, int N) {
+  (void)d;
   if (B <= 0 || H <= 0 || N <= 0) return 0;
   return stats_bytes(B, H, N);
 }
@@ -298,13 +270,9 @@ int flashbob_bob_ex(const void* Q, const void* K, const void* V, const void* dO,
   const size_t esz = dtype == FLASHBOB_BF16 ? 2 : 4;
   const size_t osz = bf16_out ? 2 : 4;  // output element size
   const size_t numel_kv = numel / (size_t)H * (size_t)H_kv;
-  // the row scalars are required; the transposed copies (d = 64) are used
-  // when the workspace also has room for them
   const size_t ws_need = stats_bytes(B, H, N);
-  const size_t ws_full = ws_need + tposed_bytes(B, H, N, d);
   if (workspace == nullptr) return FLASHBOB_ERR_NULL;
   if (workspace_bytes < ws_need) return FLASHBOB_ERR_WORKSPACE;
-  const size_t ws_used = workspace_bytes >= ws_full ? ws_full : ws_need;
   if (saved) {  // one float per query row, read as scalars: 4-byte alignment
     if (lse_in == nullptr) return FLASHBOB_ERR_NULL;
     if (reinterpret_cast<uintptr_t>(lse_in) % 4) return FLASHBOB_ERR_ALIGN;
@@ -313,7 +281,7 @@ int flashbob_bob_ex(const void* Q, const void* K, const void* V, const void* dO,
   tensor_bytes(numel, numel_kv, esz, ib);
   ib[7] = numel / (size_t)d * 4;  // lse_in: B*H*N floats
   void* outs[8] = {gradQ, gradK, gradV, graddO, workspace, dQ, dK, dV};
-  const size_t ob[8] = {numel * osz, numel_kv * osz, numel_kv * osz, numel * osz, ws_used,
+  const size_t ob[8] = {numel * osz, numel_kv * osz, numel_kv * osz, numel * osz, ws_need,
                         numel * osz, numel_kv * osz, numel_kv * osz};
   // dQ, dK, dV are outputs only with their flag, lse_in an input only with its
   rc = check_outputs(ins, ib, saved ? 8 : 7, outs, ob, first ? 8 : 5);
@@ -323,10 +291,6 @@ int flashbob_bob_ex(const void* Q, const void* K, const void* V, const void* dO,
   c.causal = (flags & FLASHBOB_CAUSAL) ? 1 : 0;
   c.lse_in = saved ? lse_in : nullptr;
   c.stats = static_cast<float*>(workspace);
-  if (ws_used > ws_need) {
-    c.tposed = reinterpret_cast<__bf16*>(static_cast<char*>(workspace) + ws_need);
-    c.tstride = tposed_elems(B, H, N);
-  }
   c.gradQ = gradQ;
   c.gradK = gradK;
   c.gradV = gradV;
@@ -453,6 +417,6 @@ const char* flashbob_strerror(int code) {
   }
 }
 
-int flashbob_version(void) { return 103; }
+int flashbob_version(void) { return 104; }
 
 }  // extern "C"

@@ -42,7 +42,6 @@ ERRORS = {
 
 EXPORTS = (
     "flashbob_workspace_bytes",
-    "flashbob_workspace_min_bytes",
     "flashbob_bob",
     "flashbob_bob_pass1",
     "flashbob_bob_pass2_query",
@@ -80,8 +79,6 @@ def load_library(path=LIB_PATH):
     vp, i, f, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
     lib.flashbob_workspace_bytes.argtypes = [i, i, i, i]
     lib.flashbob_workspace_bytes.restype = sz
-    lib.flashbob_workspace_min_bytes.argtypes = [i, i, i]
-    lib.flashbob_workspace_min_bytes.restype = sz
     lib.flashbob_bob.argtypes = [vp] * 7 + [vp] * 4 + [i, i, i, i, f, i, vp, sz, vp]
     lib.flashbob_bob.restype = i
     for name in STAGES.values():
@@ -156,14 +153,7 @@ def shapes_of(B, H, Hkv, N, d):
 
 
 def workspace_bytes(B, H, N, d):
-    """Workspace bytes for the fastest path (row scalars and, at d = 64, the
-    rearranged key-side copies pass 2q reads)."""
     return int(load_library().flashbob_workspace_bytes(B, H, N, d))
-
-
-def workspace_min_bytes(B, H, N):
-    """Smallest workspace accepted: the row scalars only."""
-    return int(load_library().flashbob_workspace_min_bytes(B, H, N))
 
 
 def _check_out(tensors, shapes, device, what, dtype=torch.float32):
@@ -210,9 +200,8 @@ def _call_ex(lib, ins, out, first, lse, B, H, Hkv, N, d, scale, dtype, causal, s
 def _check_workspace(ws, B, H, N, d, device):
     if not isinstance(ws, torch.Tensor) or ws.device != device or not ws.is_contiguous():
         raise TypeError(f"workspace must be a contiguous tensor on {device}")
-    if ws.numel() * ws.element_size() < workspace_min_bytes(B, H, N):
-        raise ValueError(f"workspace needs at least {workspace_min_bytes(B, H, N)} bytes "
-                         f"({workspace_bytes(B, H, N, d)} for the fastest path)")
+    if ws.numel() * ws.element_size() < workspace_bytes(B, H, N, d):
+        raise ValueError(f"workspace needs {workspace_bytes(B, H, N, d)} bytes")
     return ws
 
 

@@ -93,24 +93,12 @@ enum {
   FLASHBOB_STAGES_ALL = 7
 };
 
-/* Bytes of device workspace for the fastest path of flashbob_bob: the row
- * scalars (flashbob_workspace_min_bytes) and, for d = 64, room for bf16
- * copies of K, gK, V, gV rearranged for pass 2 (4 * B*H*ceil(N/32)*32*64
- * elements, rounded up to 256 bytes), which the bf16 pass 2q kernel for
- * d = 64 reads. Returns 0 for B*H*N == 0 or for invalid (negative) sizes.
+/* Bytes of device workspace flashbob_bob needs: four float32 row-scalar
+ * vectors [B, H, N] (LSE, D, c, r), rounded up to 256 bytes. Returns 0 for
+ * B*H*N == 0 or for invalid (negative) sizes.
  * Source: FlashBoB (arXiv 2609.24089), Abstract: the first pass hands the
- * second one row statistics only, O(N) per head, never an N x N tensor; the
- * copies are O(N d) per head, the size of the inputs. */
+ * second one row statistics only, O(N) per head, never an N x N tensor. */
 FLASHBOB_API size_t flashbob_workspace_bytes(int B, int H, int N, int d);
-
-/* Smallest workspace the entry points accept: four float32 row-scalar
- * vectors [B, H, N] (LSE, D, c, r), rounded up to 256 bytes. With less than
- * flashbob_workspace_bytes the rearranged copies are skipped and pass 2q
- * runs a kernel that reads K, gK, V, gV in place (same results to within
- * float32 summation order, somewhat slower). Returns 0 as above.
- * Source: FlashBoB (arXiv 2609.24089), Abstract: row statistics only pass
- * between the two passes. */
-FLASHBOB_API size_t flashbob_workspace_min_bytes(int B, int H, int N);
 
 /* Exact BoB (the method's two-pass schedule: row scalars, then outputs).
  * Source: FlashBoB (arXiv 2609.24089), Abstract: exact differentiation
@@ -122,11 +110,9 @@ FLASHBOB_API size_t flashbob_workspace_min_bytes(int B, int H, int N);
  *   gradQ, gradK,
  *   gradV, graddO    [B, H, N, d] float32 outputs: dL/dQ, dL/dK, dL/dV, dL/ddO
  *   scale            softmax scale s (finite; commonly 1/sqrt(d))
- *   workspace        device buffer of at least flashbob_workspace_min_bytes(B,H,N)
- *                    bytes (flashbob_workspace_bytes(B,H,N,d) for the fastest
- *                    path); its contents on entry do not matter and on return
- *                    its first flashbob_workspace_min_bytes hold the row
- *                    scalars in the form pass 2 consumes,
+ *   workspace        device buffer of at least flashbob_workspace_bytes(B,H,N,d)
+ *                    bytes; its contents on entry do not matter and on return
+ *                    hold the row scalars in the form pass 2 consumes,
  *                    (LSE * log2(e), -D, -c/s, -r) as [4][B][H][N] float32
  *                    (flashbob_rowstats returns them plainly).
  * Pass 1 (one kernel) computes the row scalars of every query. Pass 2
@@ -223,16 +209,13 @@ FLASHBOB_API int flashbob_bob_ex(const void* Q, const void* K, const void* V, co
  * that each GPU the library runs on holds until the process ends, enough for
  * B*H*N <= FLASHBOB_NOALLOC_MAX_ROWS query rows (larger calls return
  * FLASHBOB_ERR_SCRATCH before any HIP call). Everything else (arguments,
- * checks, results, asynchrony) is as flashbob_bob given the buffer as its
- * workspace: results are bitwise equal to flashbob_bob's with a workspace of
- * FLASHBOB_NOALLOC_SCRATCH_BYTES bytes (so the rearranged key-side copies
- * of flashbob_workspace_bytes are used where they fit in it beside the row
- * scalars, and otherwise not). The buffer belongs to the device current on the
+ * checks, results, asynchrony) is as flashbob_bob; results are bitwise equal
+ * to flashbob_bob's. The buffer belongs to the device current on the
  * calling thread (its address is looked up on the first call there, the
  * only HIP call besides the kernel launches) and is shared by every call on
  * that device: calls that overlap on one GPU (other streams or threads)
  * race on it, so such callers serialise them. Nothing in it needs clearing:
- * pass 1 and the copies overwrite every value pass 2 reads. */
+ * pass 1 overwrites every value pass 2 reads. */
 #define FLASHBOB_NOALLOC_MAX_ROWS (1 << 20)
 #define FLASHBOB_NOALLOC_SCRATCH_BYTES (16u << 20)
 FLASHBOB_API int flashbob_bob_noalloc(const void* Q, const void* K, const void* V, const void* dO,

@@ -1,13 +1,7 @@
 """GPU check of flashbob_bob_noalloc (the entry point that allocates nothing:
-its row scalars, and the rearranged key-side copies where they fit, live in
-a static device buffer of the library) against flashbob_bob, through the C
-ABI, on two calls in a row, the second one smaller, for both input dtypes:
-- bitwise equal to flashbob_bob given a workspace of the buffer's size,
-  which takes the same kernels;
-- within float32 summation-order error of flashbob_bob given the minimum
-  workspace (row scalars only), whose bf16 d = 64 pass 2q reads K, gK, V, gV
-  in place (relative Frobenius difference <= 1e-4, the float32 bar: both
-  sides add the same float32 products, only in another order)."""
+its row scalars live in a static device buffer of the library) against
+flashbob_bob, through the C ABI: bitwise equal outputs on two calls in a row,
+the second one smaller, for both input dtypes."""
 
 import ctypes
 import math
@@ -41,19 +35,16 @@ def test_noalloc_matches_flashbob_bob_two_calls(dtype):
         x = [ins[k].cuda() for k in NAMES]
         scale = 1.0 / math.sqrt(d)
         ref = [torch.empty(x[0].shape, dtype=torch.float32, device="cuda") for _ in range(4)]
-        small = [torch.empty(x[0].shape, dtype=torch.float32, device="cuda") for _ in range(4)]
         got = [torch.full(x[0].shape, float("nan"), dtype=torch.float32, device="cuda") for _ in range(4)]
-        for out, nws in ((ref, fb.FLASHBOB_NOALLOC_SCRATCH_BYTES), (small, lib.flashbob_workspace_min_bytes(B, H, N))):
-            ws = torch.empty(nws, dtype=torch.uint8, device="cuda")
-            rc = lib.flashbob_bob(*_ptrs(x), *_ptrs(out), B, H, N, d, ctypes.c_float(scale), dt,
-                                  ctypes.c_void_p(ws.data_ptr()), ctypes.c_size_t(ws.numel()), sh)
-            assert rc == 0, rc
+        ws = torch.empty(lib.flashbob_workspace_bytes(B, H, N, d), dtype=torch.uint8, device="cuda")
+        rc = lib.flashbob_bob(*_ptrs(x), *_ptrs(ref), B, H, N, d, ctypes.c_float(scale), dt,
+                              ctypes.c_void_p(ws.data_ptr()), ctypes.c_size_t(ws.numel()), sh)
+        assert rc == 0, rc
         rc = lib.flashbob_bob_noalloc(*_ptrs(x), *_ptrs(got), B, H, N, d, ctypes.c_float(scale), dt, sh)
         assert rc == 0, rc
         torch.cuda.synchronize()
-        for g, r, m in zip(got, ref, small):
+        for g, r in zip(got, ref):
             assert torch.equal(g, r)
-            assert ((g - m).norm() / m.norm()).item() <= 1e-4
     # the Python wrapper goes through the same entry point
     out = fb.bob_noalloc(*x, scale=scale)
     torch.cuda.synchronize()
