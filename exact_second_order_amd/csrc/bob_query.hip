@@ -39,9 +39,6 @@
 
 namespace flashbob {
 
-#ifndef FLASHBOB_PASS1_WIDE
-#define FLASHBOB_PASS1_WIDE 0
-#endif
 template <typename T, int D_, bool GRADQ, bool FIRST = false>
 struct QueryCfg {
   static constexpr int D = D_;
@@ -64,18 +61,17 @@ struct QueryCfg {
   // d = 32; the rest run one wave per SIMD.
   static constexpr bool SWZ = sizeof(T) == 2 && D == 64;
   static constexpr bool OCC2 = SWZ || (!GRADQ && sizeof(T) == 2) || D == 32;
-  // waves per SIMD: pass 1 in bf16 at d = 64 fits 168 registers (its steady
-  // loop spill-free; a few values spill around the masked blocks and the
-  // epilogue) and runs three, which hides more of each wave's exp and MFMA
-  // latency than two
   // Waves per workgroup, each owning 32 queries: bf16 d = 64 pass 2q runs
   // eight (the two waves of each SIMD in one workgroup), so each K, gK, V, gV
   // stage is fetched into LDS once per 256 queries instead of once per 128:
   // the chip runs these sweeps at its power limit, and the global -> LDS
-  // traffic is a measurable part of the energy per block.
-  static constexpr int NW = (SWZ && !FIRST && (GRADQ || FLASHBOB_PASS1_WIDE)) ? 8 : 4;
+  // traffic is a measurable part of the energy per block. Pass 1 keeps four
+  // (see OCC; eight at two waves per SIMD measured slower).
+  static constexpr int NW = (SWZ && !FIRST && GRADQ) ? 8 : 4;
   static constexpr int BQ = 32 * NW;                   // queries per workgroup
-  static constexpr int OCC = (!GRADQ && SWZ && NW == 4) ? 3 : OCC2 ? 2 : 1;
+  // waves per SIMD: pass 1 in bf16 at d = 64 fits 168 registers and runs
+  // three, which hides more of each wave's exp and MFMA latency than two
+  static constexpr int OCC = (!GRADQ && SWZ) ? 3 : OCC2 ? 2 : 1;
   static constexpr int NBUF = 2;                       // stage n in use, stage n+1 arriving
   static constexpr int STAGE = 4 * BK * (SWZ ? D : LDK);  // elements of one stage
   static constexpr size_t LDS_BYTES = NBUF * STAGE * sizeof(T);
