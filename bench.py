@@ -105,6 +105,33 @@ def step_accounting(launch_ms, unit_flops, peak, first_backward=False):
     return out
 
 
+CEILING_EXE = os.path.join(ROOT, "exact_second_order_amd", "_build", "mfma_ceiling")
+
+
+def mfma_ceiling():
+    """Sustained 32x32x16 bf16 MFMA rate of this GPU under its power limit
+    (random-normal operands changing every instruction, and zeros), from the
+    standalone program built next to the library; run as a child process after
+    the timed region. None if it is missing or fails."""
+    import subprocess
+    if not os.path.exists(CEILING_EXE):
+        log("[bench] mfma ceiling: program not built (run build())")
+        return None
+    try:
+        res = subprocess.run([CEILING_EXE], capture_output=True, text=True, timeout=120)
+    except (OSError, subprocess.TimeoutExpired) as e:
+        log(f"[bench] mfma ceiling failed: {e}")
+        return None
+    if res.returncode != 0:
+        log(f"[bench] mfma ceiling failed ({res.returncode}): {res.stderr.strip()[-500:]}")
+        return None
+    try:
+        return json.loads(res.stdout.strip().splitlines()[-1])
+    except (ValueError, IndexError):
+        log(f"[bench] mfma ceiling: unreadable output {res.stdout[-300:]!r}")
+        return None
+
+
 def cpu_baseline(w, rows, block=512, causal=False):
     """fp64 oracle on `rows` query rows against all keys of head 0 (a bounded
     sample of the workload), scaled to TFLOP/s with the same flop convention
@@ -164,6 +191,8 @@ def main():
     ap.add_argument("--saved-lse", action="store_true",
                     help="pass 1 starts from a saved log-sum-exp (computed once before timing, as a forward "
                          "would have kept it)")
+    ap.add_argument("--no-ceiling", action="store_true",
+                    help="skip the sustained-MFMA measurement after the timed region")
     ap.add_argument("--copy-mb", type=int, default=0,
                     help="run one plain device copy of this many MiB first (calibrates HBM byte counters)")
     args = ap.parse_args()
@@ -282,6 +311,18 @@ def main():
     if "frac_at_sclk" in per_step[dom]:
         roofline["sclk_ghz"] = per_step[dom]["sclk_ghz"]
         roofline["frac_at_sclk"] = per_step[dom]["frac_at_sclk"]
+    # what the kernels execute (pass 2 recomputes the score tiles in both
+    # sweeps), against the MFMA rate this GPU sustains under its power limit
+    roofline["executed_tflops"] = round(roofline["executed_units"] * unit_flops
+                                        / (per_step[dom]["ms"] * 1e-3) / 1e12, 2)
+    if not args.no_ceiling and w.dtype_name == "bf16":
+        ceil = mfma_ceiling()
+        if ceil is not None:
+            log(f"[bench] mfma ceiling {ceil}")
+            roofline["mfma_ceiling"] = {"tflops": ceil["random"]["tflops"], "sclk_ghz": ceil["random"]["sclk_ghz"],
+                                        "zero_operands_tflops": ceil["zero"]["tflops"],
+                                        "instruction": ceil["instruction"]}
+            roofline["executed_frac_of_ceiling"] = round(roofline["executed_tflops"] / ceil["random"]["tflops"], 4)
 
     cpu = None
     if not args.no_cpu_baseline:

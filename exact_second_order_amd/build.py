@@ -16,6 +16,10 @@ LIB = os.path.join(PKG, "libflashbob.so")
 # a plain C program that drives the C ABI without torch (run by the tests)
 C_CHECK_SRC = os.path.join(ROOT, "tests", "c_abi_check.c")
 C_CHECK = os.path.join(PKG, "_build", "c_abi_check")
+# a standalone program measuring the sustained MFMA rate under the power limit
+# (run by bench.py after its timed region)
+CEILING_SRC = os.path.join(CSRC, "mfma_ceiling.hip")
+CEILING = os.path.join(PKG, "_build", "mfma_ceiling")
 ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
 
 # (source, extra flags): bob_query.hip is built twice. The pass-1 object keeps
@@ -80,6 +84,8 @@ def build(verbose=False):
     _run([hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", *objs,
           "-Wl,--version-script=" + os.path.join(CSRC, "exports.map"), "-o", tmp], verbose)
     os.replace(tmp, LIB)
+    _run([hipcc(), *[f for f in HIPCC_FLAGS if f not in ("-fPIC", "-fvisibility=hidden")], CEILING_SRC,
+          "-o", CEILING], verbose)
     if os.path.exists(C_CHECK_SRC):
         _run(["gcc", "-std=c11", "-O2", "-Wall", "-Werror", "-D__HIP_PLATFORM_AMD__", "-I", os.path.join(ROCM, "include"),
               "-I", INCLUDE, C_CHECK_SRC, "-L", PKG, "-lflashbob", "-L", os.path.join(ROCM, "lib"), "-lamdhip64",

@@ -228,6 +228,20 @@ __device__ __forceinline__ void load_tile_sw(bf16* t, const bf16* src, int nvali
                                            row * 128 + 16 * c, 0, 0, 0);
 }
 
+// The same copy for one 64-column half of a 32-row tile of a tensor with
+// `pitch` bytes per row (d = 128: two such halves make a stage tile, 2048
+// elements apart): wave w fills rows 8w .. 8w+7 of the half starting at
+// column 64 * half. Rows at or past nvalid arrive as zeros.
+__device__ __forceinline__ void load_half_sw(bf16* t, const bf16* src, int nvalid, int pitch, int half) {
+  const int l = lane_id(), w = wave_id();
+  const int row = 8 * w + (l >> 3);
+  const int c = (l & 7) ^ swz(row);
+  typedef __attribute__((address_space(3))) void lds_void;
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(buffer_rsrc(src + 64 * half, nvalid * pitch),
+                                           (lds_void*)(t + 2048 * half + 8 * w * 64), 16, row * pitch + 16 * c, 0,
+                                           0, 0);
+}
+
 // Rows 8 rg .. 8 rg + 7 of the same swizzled 32 x 64 tile by one direct
 // global -> LDS load of the calling wave (for workgroups of more than four
 // waves, which split a stage's tiles differently); rows at or past nvalid
@@ -290,6 +304,36 @@ __device__ __forceinline__ void store_out4(void* base, size_t i, float a, float 
     st4(static_cast<bf16*>(base) + i, a, b, c, d);
   else
     st4(static_cast<float*>(base) + i, a, b, c, d);
+}
+
+// Store one 32 x 32 output block of a wave (32 rows: this lane's row l % 32;
+// 32 columns col0 .. col0 + 31, slot i of the lane half h holding column
+// col0 + acc_row(h, i)) times `os`, through the wave's 4 KB of LDS `xs`, so
+// each global store instruction writes whole rows of the block (eight lanes
+// per 128-byte row) instead of 16 bytes in each of 64 rows: partially written
+// cache lines that every workgroup leaves at once otherwise reach HBM more
+// than once. Rows at or past nrows are not stored. Contains workgroup
+// barriers: every wave of the workgroup calls it the same number of times,
+// with the LDS free.
+__device__ __forceinline__ void store_block_lds(float* xs, const f32x16& a, float os, void* out, size_t base,
+                                                int ld, int col0, int nrows, int bf16out) {
+  typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4_t;
+  const int l = lane_id(), r = l & 31, h = l >> 5;
+  // 16-byte chunk k of row r at position k ^ (r & 7): conflict-free both ways
+#pragma unroll
+  for (int g = 0; g < 4; ++g) {
+    const int k = 2 * g + h;
+    const f32x4_t v = {os * a[4 * g], os * a[4 * g + 1], os * a[4 * g + 2], os * a[4 * g + 3]};
+    *reinterpret_cast<f32x4_t*>(xs + 32 * r + 4 * (k ^ (r & 7))) = v;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int it = 0; it < 4; ++it) {
+    const int row = 8 * it + (l >> 3), k = l & 7;
+    const f32x4_t v = *reinterpret_cast<const f32x4_t*>(xs + 32 * row + 4 * (k ^ (row & 7)));
+    if (row < nrows) store_out4(out, base + (size_t)row * ld + col0 + 4 * k, v[0], v[1], v[2], v[3], bf16out);
+  }
+  __syncthreads();
 }
 
 // ---------------------------------------------------------------------------

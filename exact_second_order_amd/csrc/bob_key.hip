@@ -45,19 +45,21 @@ struct KeyCfg {
   // same staging choices as the query-major kernel; two waves per SIMD for
   // bf16 d = 64 and for d = 32 (FIRST: the first-backward dK, dV accumulators
   // need the one-wave budget)
-  static constexpr bool SWZ = sizeof(T) == 2 && D == 64;
-  static constexpr bool OCC2 = (SWZ || D == 32) && !FIRST;
+  // (d = 128: a stage tile is two swizzled 32 x 64 halves)
+  static constexpr bool SWZ = sizeof(T) == 2 && (D == 64 || D == 128);
+  static constexpr bool SWZ64 = SWZ && D == 64;
+  static constexpr bool OCC2 = (SWZ64 || D == 32) && !FIRST;
   static constexpr int NBUF = 2;                       // stage n in use, stage n+1 arriving
   // SWZ: which of the wave's K, gK, V, gV operand tensors (bits 0..3) live in
   // LDS instead of registers: gV only, which is what the register budget of two
   // waves per SIMD leaves over (every per-block LDS read costs time)
-  static constexpr int KLDS = (OCC2 && SWZ) ? 0x8 : 0;
+  static constexpr int KLDS = (OCC2 && SWZ64) ? 0x8 : 0;
   static constexpr int NKLDS = __builtin_popcount(KLDS);
   // Waves per workgroup, each owning 32 keys: with two waves per SIMD at
   // bf16 d = 64 both go in one workgroup of eight, so each Q, gQ, dO stage is
   // fetched into LDS once per 256 keys instead of once per 128 (the chip runs
   // these sweeps at its power limit, and that traffic costs energy per block)
-  static constexpr int NW = (OCC2 && SWZ) ? 8 : 4;
+  static constexpr int NW = (OCC2 && SWZ64) ? 8 : 4;
   static constexpr int BC = 32 * NW;                   // keys per workgroup
   static constexpr int ROWLEN = SWZ ? D : LDQ;
   static constexpr int QSTAGE = 3 * BQ * ROWLEN;       // Q, gQ, dO elements of one stage
@@ -168,11 +170,11 @@ __global__ __launch_bounds__((KeyCfg<T, D, FIRST>::NW * 64),
     return reinterpret_cast<float*>(smem + NBUF * Cfg::QSTAGE * sizeof(T)) + (b * 4 + t) * Cfg::SLOT;
   };
   auto lds_rows = [&](int b, int t, int c16) __attribute__((always_inline)) -> F {
-    if constexpr (SWZ) return ld_rows_sw(tile(b, t), 0, c16);
+    if constexpr (SWZ) return ld_rows_sw(tile(b, t) + 2048 * (c16 >> 2), 0, c16 & 3);
     else return ld_rows(sQ(b, t, 0, 16 * c16), LDQ);
   };
   auto lds_cols = [&](int b, int t, int krow0, int col0) __attribute__((always_inline)) -> F {
-    if constexpr (SWZ) return ld_cols_perm_sw(tile(b, t), krow0, col0);
+    if constexpr (SWZ) return ld_cols_perm_sw(tile(b, t) + 2048 * (col0 >> 6), krow0, col0 & 63);
     else return ld_cols_perm(sQ(b, t, krow0, col0), LDQ);
   };
 
@@ -265,10 +267,17 @@ __global__ __launch_bounds__((KeyCfg<T, D, FIRST>::NW * 64),
         } else {
           load_rows8_sw(tile(b, 1), gQ + qoff + (size_t)q0 * D, nq, rg);
         }
-      } else {
+      } else if constexpr (D == 64) {
         load_tile_sw(tile(b, 0), Q + qoff + (size_t)q0 * D, nq);
         load_tile_sw(tile(b, 1), gQ + qoff + (size_t)q0 * D, nq);
         load_tile_sw(tile(b, 2), dO + qoff + (size_t)q0 * D, nq);
+      } else {
+        const T* const src[3] = {Q, gQ, dO};
+#pragma unroll
+        for (int t = 0; t < 3; ++t)
+#pragma unroll
+          for (int hf = 0; hf < D / 64; ++hf)
+            load_half_sw(tile(b, t), src[t] + qoff + (size_t)q0 * D, nq, D * (int)sizeof(T), hf);
       }
       // wave w (four waves) or w + 4 (eight) fetches row scalar w
       // (LSE*log2e, -D, -c/s, -r) of the stage's queries: lane L -> row L,
@@ -425,27 +434,22 @@ __global__ __launch_bounds__((KeyCfg<T, D, FIRST>::NW * 64),
 #undef FLASHBOB_KEY_BLOCK
   }
 
-  // accK[j] slot i holds d = 32 j + acc_row(h, i) of this lane's key
-  if (kvalid) {
-    const size_t row = hoff + (size_t)key * D;
+  // accK[j] slot i holds d = 32 j + acc_row(h, i) of this lane's key; each
+  // 32 x 32 block goes out through LDS (free: the last block ended with a
+  // barrier and prefetched nothing)
+  static_assert(Cfg::LDS_BYTES >= (size_t)Cfg::NW * 4096, "output staging fits the LDS");
+  float* xs = reinterpret_cast<float*>(smem) + 1024 * w;
+  const int k0w = kblk * Cfg::BC + 32 * w;  // the wave's first key
+  const size_t base = hoff + (size_t)k0w * D;
+  const int nrows = min(32, N - k0w);
 #pragma unroll
-    for (int j = 0; j < NDBO; ++j) {
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int d0 = 32 * (part * NDBO + j) + 8 * g + 4 * h;
-        const f32x16& a = accK[j];
-        const f32x16& v = accV[j];
-        store_out4(gradK, row + d0, scale * a[4 * g], scale * a[4 * g + 1], scale * a[4 * g + 2],
-                   scale * a[4 * g + 3], out_bf16);
-        store_out4(gradV, row + d0, v[4 * g], v[4 * g + 1], v[4 * g + 2], v[4 * g + 3], out_bf16);
-        if constexpr (FIRST) {
-          const f32x16& fk = accdK[j];
-          const f32x16& fv = accdV[j];
-          store_out4(dKo, row + d0, scale * fk[4 * g], scale * fk[4 * g + 1], scale * fk[4 * g + 2],
-                     scale * fk[4 * g + 3], out_bf16);
-          store_out4(dVo, row + d0, fv[4 * g], fv[4 * g + 1], fv[4 * g + 2], fv[4 * g + 3], out_bf16);
-        }
-      }
+  for (int j = 0; j < NDBO; ++j) {
+    const int col0 = 32 * (part * NDBO + j);
+    store_block_lds(xs, accK[j], scale, gradK, base, D, col0, nrows, out_bf16);
+    store_block_lds(xs, accV[j], 1.f, gradV, base, D, col0, nrows, out_bf16);
+    if constexpr (FIRST) {
+      store_block_lds(xs, accdK[j], scale, dKo, base, D, col0, nrows, out_bf16);
+      store_block_lds(xs, accdV[j], 1.f, dVo, base, D, col0, nrows, out_bf16);
     }
   }
 }

@@ -52,26 +52,29 @@ struct QueryCfg {
   // accumulators for only part of d
   static constexpr int OSPLIT = (GRADQ && D >= 256) ? 2 : 1;
   static constexpr int NDBO = NDB / OSPLIT;            // 32-row blocks of d per workgroup
-  // bf16 d = 64 stages tiles with direct global->LDS loads into swizzled
-  // unpadded rows (no staging registers); the other variants stage through
-  // registers into padded rows. Two waves per SIMD (<= 256 registers: the
-  // second wave hides the first one's latencies and overlaps its VALU work
-  // with the other's MFMAs) where the per-wave state fits: bf16 d = 64, pass 1
-  // in bf16 at every d (a few bytes spill at d = 96, 128, still faster), and
-  // d = 32; the rest run one wave per SIMD.
-  static constexpr bool SWZ = sizeof(T) == 2 && D == 64;
-  static constexpr bool OCC2 = SWZ || (!GRADQ && sizeof(T) == 2) || D == 32;
+  // bf16 d = 64 and d = 128 stage tiles with direct global->LDS loads into
+  // swizzled unpadded rows (no staging registers; at d = 128 a tile is two
+  // swizzled 32 x 64 halves), which the transposing LDS reads take without
+  // bank conflicts; the other variants stage through registers into padded
+  // rows. Two waves per SIMD (<= 256 registers: the second wave hides the
+  // first one's latencies and overlaps its VALU work with the other's MFMAs)
+  // where the per-wave state fits: bf16 d = 64, pass 1 in bf16 at every d (a
+  // few bytes spill at d = 96, 128, still faster), and d = 32; the rest run
+  // one wave per SIMD.
+  static constexpr bool SWZ = sizeof(T) == 2 && (D == 64 || D == 128);
+  static constexpr bool SWZ64 = SWZ && D == 64;
+  static constexpr bool OCC2 = SWZ64 || (!GRADQ && sizeof(T) == 2) || D == 32;
   // Waves per workgroup, each owning 32 queries: bf16 d = 64 pass 2q runs
   // eight (the two waves of each SIMD in one workgroup), so each K, gK, V, gV
   // stage is fetched into LDS once per 256 queries instead of once per 128:
   // the chip runs these sweeps at its power limit, and the global -> LDS
   // traffic is a measurable part of the energy per block. Pass 1 keeps four
   // (see OCC; eight at two waves per SIMD measured slower).
-  static constexpr int NW = (SWZ && !FIRST && GRADQ) ? 8 : 4;
+  static constexpr int NW = (SWZ64 && !FIRST && GRADQ) ? 8 : 4;
   static constexpr int BQ = 32 * NW;                   // queries per workgroup
   // waves per SIMD: pass 1 in bf16 at d = 64 fits 168 registers and runs
   // three, which hides more of each wave's exp and MFMA latency than two
-  static constexpr int OCC = (!GRADQ && SWZ) ? 3 : OCC2 ? 2 : 1;
+  static constexpr int OCC = (!GRADQ && SWZ64) ? 3 : OCC2 ? 2 : 1;
   static constexpr int NBUF = 2;                       // stage n in use, stage n+1 arriving
   static constexpr int STAGE = 4 * BK * (SWZ ? D : LDK);  // elements of one stage
   static constexpr size_t LDS_BYTES = NBUF * STAGE * sizeof(T);
@@ -212,18 +215,19 @@ void query_kernel(
   using E = Elem<T>;
   using F = typename E::frag;
   constexpr int BK = Cfg::BK, LDK = Cfg::LDK, NCH = Cfg::NCH, NDB = Cfg::NDB, NBUF = Cfg::NBUF;
-  constexpr bool SWZ = Cfg::SWZ;
+  constexpr bool SWZ = Cfg::SWZ, SWZ64 = Cfg::SWZ64;
   constexpr int ROWLEN = SWZ ? D : LDK;
   // [NBUF][4][BK][ROWLEN]: K, gK, V, gV of a stage
   __shared__ __attribute__((aligned(16))) T smem[NBUF * Cfg::STAGE];
   auto sK = [&](int b, int t, int row, int col) __attribute__((always_inline)) { return smem + ((b * 4 + t) * BK + row) * ROWLEN + col; };
   auto tile = [&](int b, int t) __attribute__((always_inline)) { return smem + (b * 4 + t) * BK * ROWLEN; };
+  // (SWZ: from the 64-column half c16 / 4, resp. col0 / 64, of the tile)
   auto lds_rows = [&](int b, int t, int row0, int c16) __attribute__((always_inline)) -> typename Elem<T>::frag {
-    if constexpr (SWZ) return ld_rows_sw(tile(b, t), row0, c16);
+    if constexpr (SWZ) return ld_rows_sw(tile(b, t) + 2048 * (c16 >> 2), row0, c16 & 3);
     else return ld_rows(sK(b, t, row0, 16 * c16), LDK);
   };
   auto lds_cols = [&](int b, int t, int krow0, int col0) __attribute__((always_inline)) -> typename Elem<T>::frag {
-    if constexpr (SWZ) return ld_cols_perm_sw(tile(b, t), krow0, col0);
+    if constexpr (SWZ) return ld_cols_perm_sw(tile(b, t) + 2048 * (col0 >> 6), krow0, col0 & 63);
     else return ld_cols_perm(sK(b, t, krow0, col0), LDK);
   };
 
@@ -325,12 +329,20 @@ void query_kernel(
       const int rg = w & 3;
       load_rows8_sw(tile(b, w >> 2), (w < 4 ? K : gK) + koff + (size_t)k0 * D, nk, rg);
       load_rows8_sw(tile(b, 2 + (w >> 2)), (w < 4 ? V : gV) + koff + (size_t)k0 * D, nk, rg);
-    } else if constexpr (SWZ) {
+    } else if constexpr (SWZ64) {
       const int b = n & (NBUF - 1);
       load_tile_sw(tile(b, 0), K + koff + (size_t)k0 * D, nk);
       load_tile_sw(tile(b, 1), gK + koff + (size_t)k0 * D, nk);
       load_tile_sw(tile(b, 2), V + koff + (size_t)k0 * D, nk);
       load_tile_sw(tile(b, 3), gV + koff + (size_t)k0 * D, nk);
+    } else if constexpr (SWZ) {
+      const int b = n & (NBUF - 1);
+      const T* const src[4] = {K, gK, V, gV};
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int hf = 0; hf < D / 64; ++hf)
+          load_half_sw(tile(b, t), src[t] + koff + (size_t)k0 * D, nk, D * (int)sizeof(T), hf);
     } else {
       pk.load(K + koff + (size_t)k0 * D, nk);
       pgk.load(gK + koff + (size_t)k0 * D, nk);
@@ -490,26 +502,20 @@ void query_kernel(
       }
     }
   } else {
-    // accQ[j] slot i holds d = 32 j + acc_row(h, i) of this lane's query
-    if (qvalid) {
-      const size_t row = hoff + (size_t)q * D;
+    // accQ[j] slot i holds d = 32 j + acc_row(h, i) of this lane's query;
+    // each 32 x 32 block goes out through LDS (the stage buffers are free:
+    // the last iteration ended with a barrier)
+    static_assert(Cfg::LDS_BYTES >= (size_t)Cfg::NW * 4096, "output staging fits the stage buffers");
+    float* xs = reinterpret_cast<float*>(smem) + 1024 * w;
+    const int q0w = qblk * Cfg::BQ + 32 * w;  // the wave's first query
+    const size_t base = hoff + (size_t)q0w * D;
+    const int nrows = min(32, N - q0w);
 #pragma unroll
-      for (int j = 0; j < NDBO; ++j) {
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int d0 = 32 * (part * NDBO + j) + 8 * g + 4 * h;
-          const f32x16& a = accQ[j];
-          const f32x16& o = accO[j];
-          store_out4(gradQ, row + d0, scale * a[4 * g], scale * a[4 * g + 1], scale * a[4 * g + 2],
-                     scale * a[4 * g + 3], out_bf16);
-          store_out4(graddO, row + d0, o[4 * g], o[4 * g + 1], o[4 * g + 2], o[4 * g + 3], out_bf16);
-          if constexpr (FIRST) {
-            const f32x16& f = accdQ[j];
-            store_out4(dQo, row + d0, scale * f[4 * g], scale * f[4 * g + 1], scale * f[4 * g + 2],
-                       scale * f[4 * g + 3], out_bf16);
-          }
-        }
-      }
+    for (int j = 0; j < NDBO; ++j) {
+      const int col0 = 32 * (part * NDBO + j);
+      store_block_lds(xs, accQ[j], scale, gradQ, base, D, col0, nrows, out_bf16);
+      store_block_lds(xs, accO[j], 1.f, graddO, base, D, col0, nrows, out_bf16);
+      if constexpr (FIRST) store_block_lds(xs, accdQ[j], scale, dQo, base, D, col0, nrows, out_bf16);
     }
   }
 }
