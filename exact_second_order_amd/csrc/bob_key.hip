@@ -43,17 +43,19 @@ struct KeyCfg {
   static constexpr int OSPLIT = D >= 256 ? 4 : 1;
   static constexpr int NDBO = NDB / OSPLIT;  // 32-row blocks of d per workgroup
   // same staging choices as the query-major kernel; two waves per SIMD for
-  // bf16 d = 64 and for d = 32 (FIRST: the first-backward dK, dV accumulators
-  // need the one-wave budget)
+  // bf16 d = 64 (with the first backward too: its dK, dV accumulators fit once
+  // the operand fragments are packed into the score tiles and more key-side
+  // tensors live in LDS) and for d = 32 (FIRST: one wave)
   // (d = 128: a stage tile is two swizzled 32 x 64 halves)
   static constexpr bool SWZ = sizeof(T) == 2 && (D == 64 || D == 128);
   static constexpr bool SWZ64 = SWZ && D == 64;
-  static constexpr bool OCC2 = (SWZ64 || D == 32) && !FIRST;
+  static constexpr bool OCC2 = SWZ64 || (D == 32 && !FIRST);
   static constexpr int NBUF = 2;                       // stage n in use, stage n+1 arriving
   // SWZ: which of the wave's K, gK, V, gV operand tensors (bits 0..3) live in
   // LDS instead of registers: gV only, which is what the register budget of two
-  // waves per SIMD leaves over (every per-block LDS read costs time)
-  static constexpr int KLDS = (OCC2 && SWZ64) ? 0x8 : 0;
+  // waves per SIMD leaves over (every per-block LDS read costs time); with the
+  // first backward gK and V as well (with gK alone the loop still spills)
+  static constexpr int KLDS = (OCC2 && SWZ64) ? (FIRST ? 0xE : 0x8) : 0;
   static constexpr int NKLDS = __builtin_popcount(KLDS);
   // Waves per workgroup, each owning 32 keys: with two waves per SIMD at
   // bf16 d = 64 both go in one workgroup of eight, so each Q, gQ, dO stage is
@@ -142,6 +144,57 @@ __device__ __forceinline__ void key_chunk(int cc, const f32x16& S, const f32x16&
   to_frag(fdS2, dS2);
   to_frag(fA, A);
   if constexpr (FIRST) to_frag(fP, P);
+}
+
+// The same step for bf16 operands, done in place: the results of chunk cc
+// are rounded pair by pair and written back into the tiles' own registers
+// (dS into dP, A into G, dS2 into H and, with the first backward, P into S) at
+// words 8 cc .. 8 cc + 3: pair s2 reads words 8 cc + 2 s2, + 1 and writes
+// word 8 cc + s2, which the same or an earlier pair has already read. The
+// chunk's bf16 operand fragments are then those four words of each tile.
+template <bool TAIL, bool FIRST>
+__device__ __forceinline__ void key_chunk_inplace(int cc, f32x16& S, f32x16& G, f32x16& dP, f32x16& H,
+                                                  const float* sl, float sl2, float scale, bool kvalid, int q_lo,
+                                                  int nq_rel) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  typedef float f32x2_t __attribute__((ext_vector_type(2)));
+  auto pack = [](float a, float b) __attribute__((always_inline)) {
+    return __builtin_bit_cast(float, __builtin_convertvector((f32x2_t){a, b}, bf16x2_t));
+  };
+  const int h = lane_id() >> 5;
+#pragma unroll
+  for (int gg = 0; gg < 2; ++gg) {
+    const int g = 2 * cc + gg;
+    const int r0 = 8 * g + 4 * h;  // this lane-half's 4 consecutive query rows
+    const f32x4 L4 = *reinterpret_cast<const f32x4*>(sl + r0);
+#pragma unroll
+    for (int e2 = 0; e2 < 2; ++e2) {
+      float vds[2], va[2], vd2[2], vp[2];
+#pragma unroll
+      for (int e1 = 0; e1 < 2; ++e1) {
+        const int e = 2 * e2 + e1, i = 4 * g + e;
+        float p = fast_exp2(fmaf(S[i], sl2, -L4[e]));
+        if (TAIL && (!kvalid || r0 + e >= nq_rel || r0 + e < q_lo)) p = 0.f;
+        const float ds = p * dP[i];
+        const float gv = G[i] * scale;
+        vds[e1] = ds;
+        va[e1] = p * gv;
+        vd2[e1] = fmaf(ds, gv, p * H[i]);
+        vp[e1] = p;
+      }
+      const int o = 8 * cc + 2 * gg + e2;
+      dP[o] = pack(vds[0], vds[1]);
+      G[o] = pack(va[0], va[1]);
+      H[o] = pack(vd2[0], vd2[1]);
+      if constexpr (FIRST) S[o] = pack(vp[0], vp[1]);
+    }
+  }
+}
+
+// Words 8 cc .. 8 cc + 3 of a tile as a bf16 operand fragment.
+__device__ __forceinline__ bf16x8 packed_frag(const f32x16& t, int cc) {
+  return __builtin_bit_cast(bf16x8, cc == 0 ? __builtin_shufflevector(t, t, 0, 1, 2, 3)
+                                            : __builtin_shufflevector(t, t, 8, 9, 10, 11));
 }
 
 // FIRST: also return the first-backward dK = s dS^T Q and dV = P^T dO (two
@@ -344,19 +397,35 @@ __global__ __launch_bounds__((KeyCfg<T, D, FIRST>::NW * 64),
       E::mma(t.H, ado, keyop(3, c));
     }
   };
+  // bf16 packs the operand fragments into the score tiles' own registers
+  // (key_chunk_inplace); fp32 keeps them apart
+  constexpr bool INPLACE = sizeof(T) == 2;
   struct Frags {
     F dS[2], dS2[2], A[2], P[FIRST ? 2 : 1];
   };
   // TAIL: masks keys past the end (the whole sweep of the last key block)
   // and query rows past the end (last query block)
-  auto elementwise = [&](auto tail, int n, int cc, const Tiles& t, Frags& f) __attribute__((always_inline)) {
+  auto elementwise = [&](auto tail, int n, int cc, Tiles& t, Frags& f) __attribute__((always_inline)) {
     constexpr bool TAIL = decltype(tail)::value;
     const int b = n & (NBUF - 1);
-    key_chunk<T, TAIL, FIRST>(cc, t.S, t.G, t.dP, t.H, sS(b, 0), sl2, scale, kvalid, causal ? key - n * BQ : 0,
-                       N - n * BQ, f.dS[cc], f.dS2[cc], f.A[cc], f.P[FIRST ? cc : 0]);
+    if constexpr (INPLACE)
+      key_chunk_inplace<TAIL, FIRST>(cc, t.S, t.G, t.dP, t.H, sS(b, 0), sl2, scale, kvalid,
+                                     causal ? key - n * BQ : 0, N - n * BQ);
+    else
+      key_chunk<T, TAIL, FIRST>(cc, t.S, t.G, t.dP, t.H, sS(b, 0), sl2, scale, kvalid, causal ? key - n * BQ : 0,
+                                N - n * BQ, f.dS[cc], f.dS2[cc], f.A[cc], f.P[FIRST ? cc : 0]);
   };
-  auto outputs = [&](int n, int cc, const Frags& f) __attribute__((always_inline)) {
+  auto outputs = [&](int n, int cc, const Tiles& t, const Frags& f0) __attribute__((always_inline)) {
     const int b = n & (NBUF - 1);
+    Frags f;
+    if constexpr (INPLACE) {
+      f.dS[cc] = packed_frag(t.dP, cc);
+      f.dS2[cc] = packed_frag(t.H, cc);
+      f.A[cc] = packed_frag(t.G, cc);
+      if constexpr (FIRST) f.P[cc] = packed_frag(t.S, cc);
+    } else {
+      f = f0;
+    }
 #pragma unroll
     for (int j = 0; j < NDBO; ++j) {
       // lane <-> d, k over this chunk's queries (accumulator row order); this
@@ -414,7 +483,7 @@ __global__ __launch_bounds__((KeyCfg<T, D, FIRST>::NW * 64),
     recompute((n), t, 0, NCH);                        \
     _Pragma("unroll") for (int cc = 0; cc < 2; ++cc) { \
       elementwise(TAIL, (n), cc, t, f);               \
-      outputs((n), cc, f);                            \
+      outputs((n), cc, t, f);                         \
     }                                                 \
     if (PF) commit((n) + 1);                          \
     __syncthreads();                                  \

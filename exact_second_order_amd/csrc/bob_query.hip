@@ -70,11 +70,14 @@ struct QueryCfg {
   // the chip runs these sweeps at its power limit, and the global -> LDS
   // traffic is a measurable part of the energy per block. Pass 1 keeps four
   // (see OCC; eight at two waves per SIMD measured slower).
-  static constexpr int NW = (SWZ64 && !FIRST && GRADQ) ? 8 : 4;
+  static constexpr int NW = (SWZ64 && GRADQ) ? 8 : 4;
   static constexpr int BQ = 32 * NW;                   // queries per workgroup
   // waves per SIMD: pass 1 in bf16 at d = 64 fits 168 registers and runs
   // three, which hides more of each wave's exp and MFMA latency than two
-  static constexpr int OCC = (!GRADQ && SWZ64) ? 3 : OCC2 ? 2 : 1;
+  // (the first-backward dQ accumulator fits two waves per SIMD at bf16 d = 64,
+  // with the operand fragments packed into the score tiles; elsewhere its
+  // kernels run one)
+  static constexpr int OCC = (FIRST && !SWZ64) ? 1 : (!GRADQ && SWZ64) ? 3 : OCC2 ? 2 : 1;
   static constexpr int NBUF = 2;                       // stage n in use, stage n+1 arriving
   static constexpr int STAGE = 4 * BK * (SWZ ? D : LDK);  // elements of one stage
   static constexpr size_t LDS_BYTES = NBUF * STAGE * sizeof(T);
@@ -198,12 +201,57 @@ __device__ __forceinline__ void query_chunk(int cc, const f32x16& S, const f32x1
   to_frag(fA, A);
 }
 
+// The same step for bf16 operands, done in place: the results of chunk cc
+// are rounded pair by pair and written back into the tiles' own registers,
+// P into S, dS into dP, A into G and dS2 into H, at words 8 cc .. 8 cc + 3
+// (pair s2 reads words 8 cc + 2 s2, + 1 and writes word 8 cc + s2, which the
+// same or an earlier pair has already read). The chunk's bf16 operand
+// fragments are then those four words of each tile (packed_frag), and no
+// separate fragment registers are live.
+template <bool TAIL>
+__device__ __forceinline__ void query_chunk_inplace(int cc, f32x16& S, f32x16& G, f32x16& dP, f32x16& H,
+                                                    float sl2, float scale, float l2, float Dq, float cq, float rq,
+                                                    int nvalid_rel) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  typedef float f32x2_t __attribute__((ext_vector_type(2)));
+  auto pack = [](float a, float b) __attribute__((always_inline)) {
+    return __builtin_bit_cast(float, __builtin_convertvector((f32x2_t){a, b}, bf16x2_t));
+  };
+  const int h = lane_id() >> 5;
+#pragma unroll
+  for (int s2 = 0; s2 < 4; ++s2) {
+    float vp[2], vds[2], va[2], vd2[2];
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const int i = 8 * cc + 2 * s2 + e;
+      float p = fast_exp2(fmaf(S[i], sl2, -l2));
+      if (TAIL && acc_row(h, i) >= nvalid_rel) p = 0.f;
+      const float ds = p * (dP[i] + Dq);
+      const float g = fmaf(G[i], scale, cq);
+      vp[e] = p;
+      vds[e] = ds;
+      va[e] = p * g;
+      vd2[e] = fmaf(ds, g, p * (H[i] + rq));
+    }
+    S[8 * cc + s2] = pack(vp[0], vp[1]);
+    dP[8 * cc + s2] = pack(vds[0], vds[1]);
+    G[8 * cc + s2] = pack(va[0], va[1]);
+    H[8 * cc + s2] = pack(vd2[0], vd2[1]);
+  }
+}
+
+// Words 8 cc .. 8 cc + 3 of a tile as a bf16 operand fragment.
+__device__ __forceinline__ bf16x8 packed_frag(const f32x16& t, int cc) {
+  return __builtin_bit_cast(bf16x8, cc == 0 ? __builtin_shufflevector(t, t, 0, 1, 2, 3)
+                                            : __builtin_shufflevector(t, t, 8, 9, 10, 11));
+}
+
 // FIRST (pass 2q only): also return the first-backward dQ = s dS K (one more
 // product per block against the K^T operand already read; the extra
 // accumulator needs the one-wave-per-SIMD register budget).
 template <typename T, int D, bool GRADQ, bool FIRST, bool SAVED>
 __global__ __launch_bounds__((QueryCfg<T, D, GRADQ, FIRST>::NW * 64),
-                             ((FIRST ? 1 : QueryCfg<T, D, GRADQ, FIRST>::OCC) * 4 / QueryCfg<T, D, GRADQ, FIRST>::NW))
+                             (QueryCfg<T, D, GRADQ, FIRST>::OCC * 4 / QueryCfg<T, D, GRADQ, FIRST>::NW))
 void query_kernel(
     const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V, const T* __restrict__ dO,
     const T* __restrict__ gQ, const T* __restrict__ gK, const T* __restrict__ gV, float* __restrict__ lse,
@@ -388,24 +436,41 @@ void query_kernel(
       E::mma(t.H, agv, fdO[c]);
     }
   };
+  // bf16 pass 2q packs the operand fragments into the score tiles' own
+  // registers (query_chunk_inplace); fp32 keeps them apart
+  constexpr bool INPLACE = GRADQ && sizeof(T) == 2;
   struct Frags {
     F P[2], dS[2], dS2[2], A[2];
   };
   // elementwise work of 16-key chunk cc of block n: online sums (pass 1) or
   // operand fragments (pass 2q); TAIL masks keys past the sequence end
-  auto elementwise = [&](auto tail, int n, int cc, const Tiles& t, Frags& f) __attribute__((always_inline)) {
+  auto elementwise = [&](auto tail, int n, int cc, Tiles& t, Frags& f) __attribute__((always_inline)) {
     constexpr bool TAIL = decltype(tail)::value;
     const int nrel = qlim - n * BK;
     if constexpr (!GRADQ)
       online_chunk<TAIL, SAVED>(cc, t.S, t.G, t.dP, t.H, sl2, nrel, st, mu);
+    else if constexpr (INPLACE)
+      query_chunk_inplace<TAIL>(cc, t.S, t.G, t.dP, t.H, sl2, scale, l2, Dq, cq, rq, nrel);
     else
       query_chunk<T, TAIL>(cc, t.S, t.G, t.dP, t.H, sl2, scale, l2, Dq, cq, rq, nrel, f.P[cc], f.dS[cc],
                            f.dS2[cc], f.A[cc]);
   };
   // output products of 16-key chunk cc of block n (pass 2q)
-  auto outputs = [&](int n, int cc, const Frags& f) __attribute__((always_inline)) {
+  auto outputs = [&](int n, int cc, const Tiles& t, const Frags& f) __attribute__((always_inline)) {
     if constexpr (GRADQ) {
       const int b = n & (NBUF - 1);
+      F fP, fdS, fdS2, fA;
+      if constexpr (INPLACE) {
+        fP = packed_frag(t.S, cc);
+        fdS = packed_frag(t.dP, cc);
+        fdS2 = packed_frag(t.H, cc);
+        fA = packed_frag(t.G, cc);
+      } else {
+        fP = f.P[cc];
+        fdS = f.dS[cc];
+        fdS2 = f.dS2[cc];
+        fA = f.A[cc];
+      }
 #pragma unroll
       for (int j = 0; j < NDBO; ++j) {
         // lane <-> d, k over this chunk's keys (accumulator row order); this
@@ -415,11 +480,11 @@ void query_kernel(
         const F tgK = lds_cols(b, 1, 16 * cc, jd);
         const F tV = lds_cols(b, 2, 16 * cc, jd);
         const F tgV = lds_cols(b, 3, 16 * cc, jd);
-        E::mma(accQ[j], tK, f.dS2[cc]);
-        E::mma(accQ[j], tgK, f.dS[cc]);
-        E::mma(accO[j], tV, f.A[cc]);
-        E::mma(accO[j], tgV, f.P[cc]);
-        if constexpr (FIRST) E::mma(accdQ[j], tK, f.dS[cc]);
+        E::mma(accQ[j], tK, fdS2);
+        E::mma(accQ[j], tgK, fdS);
+        E::mma(accO[j], tV, fA);
+        E::mma(accO[j], tgV, fP);
+        if constexpr (FIRST) E::mma(accdQ[j], tK, fdS);
       }
     }
   };
@@ -443,7 +508,7 @@ void query_kernel(
 #pragma unroll
     for (int cc = 0; cc < 2; ++cc) {
       elementwise(tail, n, cc, t, f);
-      outputs(n, cc, f);
+      outputs(n, cc, t, f);
     }
     commit(n + 1);
     __syncthreads();
