@@ -52,10 +52,11 @@ struct KeyCfg {
   static constexpr bool OCC2 = SWZ64 || (D == 32 && !FIRST);
   static constexpr int NBUF = 2;                       // stage n in use, stage n+1 arriving
   // SWZ: which of the wave's K, gK, V, gV operand tensors (bits 0..3) live in
-  // LDS instead of registers: gV only, which is what the register budget of two
-  // waves per SIMD leaves over (every per-block LDS read costs time); with the
-  // first backward gK and V as well (with gK alone the loop still spills)
-  static constexpr int KLDS = (OCC2 && SWZ64) ? (FIRST ? 0xE : 0x8) : 0;
+  // LDS instead of registers (every per-block LDS read costs energy): none in
+  // the plain kernel, whose operand fragments are packed into the score tiles'
+  // registers; with the first backward's accumulators gK, V and gV (with gK
+  // alone the loop still spills)
+  static constexpr int KLDS = (OCC2 && SWZ64 && FIRST) ? 0xE : 0;
   static constexpr int NKLDS = __builtin_popcount(KLDS);
   // Waves per workgroup, each owning 32 keys: with two waves per SIMD at
   // bf16 d = 64 both go in one workgroup of eight, so each Q, gQ, dO stage is
@@ -74,7 +75,9 @@ struct KeyCfg {
   // stage buffers
   static constexpr size_t KSIDE = (size_t)NW * NKLDS * 32 * D * sizeof(T);
   static constexpr size_t STAGE_BYTES = NBUF * (QSTAGE * sizeof(T) + SSTAGE * sizeof(float));
-  static constexpr size_t LDS_BYTES = STAGE_BYTES + KSIDE;
+  // (at least the epilogue's 4 KB of output staging per wave)
+  static constexpr size_t LDS_BYTES =
+      STAGE_BYTES + KSIDE > (size_t)NW * 4096 ? STAGE_BYTES + KSIDE : (size_t)NW * 4096;
   static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
 };
 
