@@ -168,10 +168,16 @@ def cpu_baseline(w, rows, block=512, causal=False):
     pairs = rows * (rows + 1) / 2 if causal else rows * w.N
     flops = 34.0 * pairs * w.d
     what = f"the first {rows} query rows (causal)" if causal else f"{rows} query rows x all {w.N} keys"
-    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(cores), "cpu_model": cpu_model,
+    rate = flops / dt
+    # the whole call at the sampled rate (an extrapolation, not a run): all
+    # B*H heads, all visible (query, key) pairs
+    full_pairs = w.B * w.H * (w.N * (w.N + 1) / 2 if causal else float(w.N) * w.N)
+    return {"value": round(rate / 1e12, 6), "unit": "TFLOP/s", "cores": int(cores), "cpu_model": cpu_model,
             "kind": "oracle",
             "sample": f"{what} of one head (d={w.d}), fp64 row-blocked oracle, {dt:.2f} s; "
-                      f"flops counted as 34*d per visible (query, key) pair"}
+                      f"flops counted as 34*d per visible (query, key) pair",
+            "extrapolated_full_call_s": round(34.0 * full_pairs * w.d / rate, 1),
+            "extrapolation": "the whole workload (all heads and rows) at the sampled rate; not run"}
 
 
 def main():
