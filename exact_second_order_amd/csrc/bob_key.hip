@@ -39,15 +39,18 @@ struct KeyCfg {
   // d >= 256: each key block is handled by OSPLIT workgroups, each
   // accumulating its own share of gradK, gradV's columns (the score tiles are
   // recomputed by each), so the key-side operands stay in registers beside
-  // accumulators for only part of d
-  static constexpr int OSPLIT = D >= 256 ? 4 : 1;
+  // accumulators for only part of d (two shares fit once the stage tiles load
+  // straight into LDS and the operand fragments live in the score tiles: 13
+  // products instead of the 23 of four; the first backward's extra
+  // accumulators still need four)
+  static constexpr int OSPLIT = D >= 256 ? (FIRST ? 4 : 2) : 1;
   static constexpr int NDBO = NDB / OSPLIT;  // 32-row blocks of d per workgroup
   // same staging choices as the query-major kernel; two waves per SIMD for
   // bf16 d = 64 (with the first backward too: its dK, dV accumulators fit once
   // the operand fragments are packed into the score tiles and more key-side
   // tensors live in LDS) and for d = 32 (FIRST: one wave)
-  // (d = 128: a stage tile is two swizzled 32 x 64 halves)
-  static constexpr bool SWZ = sizeof(T) == 2 && (D == 64 || D == 128);
+  // (d = 128, 256: a stage tile is d/64 swizzled 32 x 64 pieces)
+  static constexpr bool SWZ = sizeof(T) == 2 && (D == 64 || D == 128 || D == 256);
   static constexpr bool SWZ64 = SWZ && D == 64;
   static constexpr bool OCC2 = SWZ64 || (D == 32 && !FIRST);
   static constexpr int NBUF = 2;                       // stage n in use, stage n+1 arriving

@@ -52,16 +52,16 @@ struct QueryCfg {
   // accumulators for only part of d
   static constexpr int OSPLIT = (GRADQ && D >= 256) ? 2 : 1;
   static constexpr int NDBO = NDB / OSPLIT;            // 32-row blocks of d per workgroup
-  // bf16 d = 64 and d = 128 stage tiles with direct global->LDS loads into
-  // swizzled unpadded rows (no staging registers; at d = 128 a tile is two
-  // swizzled 32 x 64 halves), which the transposing LDS reads take without
+  // bf16 d = 64, 128 and 256 stage tiles with direct global->LDS loads into
+  // swizzled unpadded rows (no staging registers; above d = 64 a tile is d/64
+  // swizzled 32 x 64 pieces), which the transposing LDS reads take without
   // bank conflicts; the other variants stage through registers into padded
   // rows. Two waves per SIMD (<= 256 registers: the second wave hides the
   // first one's latencies and overlaps its VALU work with the other's MFMAs)
   // where the per-wave state fits: bf16 d = 64, pass 1 in bf16 at every d (a
   // few bytes spill at d = 96, 128, still faster), and d = 32; the rest run
   // one wave per SIMD.
-  static constexpr bool SWZ = sizeof(T) == 2 && (D == 64 || D == 128);
+  static constexpr bool SWZ = sizeof(T) == 2 && (D == 64 || D == 128 || D == 256);
   static constexpr bool SWZ64 = SWZ && D == 64;
   static constexpr bool OCC2 = SWZ64 || (!GRADQ && sizeof(T) == 2) || D == 32;
   // Waves per workgroup, each owning 32 queries: bf16 d = 64 pass 2q runs

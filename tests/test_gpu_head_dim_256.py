@@ -1,8 +1,8 @@
 """Head dim 256 (bf16 inputs only) on the HIP path against the fp64 oracle:
 every option of flashbob_bob_ex (causal mask, grouped key/value heads, the
 first-backward outputs, a saved log-sum-exp, bf16 outputs), ragged lengths
-across several tiles, pass 1 alone, and the fp32 refusal. The d = 256
-instantiations spill registers (correct, not tuned), so the sizes stay small.
+across several tiles, pass 1 alone, and the fp32 refusal. The sizes stay
+small: the oracle's N x N tiles at d = 256 are the slow part here.
 """
 
 import numpy as np
