@@ -8,8 +8,8 @@
 //   gradK_j = s sum_i (dS2_ij Q_i + dS_ij gQ_i),   gradV_j = sum_i A_ij dO_i,
 // with S = Q K^T, dP = dO V^T, G = s (gQ K^T + Q gK^T), H = dO gV^T.
 //
-// gfx950 schedule: a workgroup of 4 waves owns 128 keys (32 per wave) and
-// streams the queries (Q, gQ, dO and their row scalars) in 32-row stages
+// gfx950 schedule: a workgroup of 4 waves (8 in bf16 d = 64) owns 32 keys per
+// wave and streams the queries (Q, gQ, dO and their row scalars) in 32-row stages
 // through two LDS buffers, issuing each stage's global reads one stage ahead.
 // Per 32-query block a wave builds S, G, dP, H (queries x its keys) with
 // MFMA, so each lane holds one key and 16 queries. The dP, G and H
@@ -21,8 +21,9 @@
 // accumulator row order), against Q^T, gQ^T, dO^T read from the LDS stage with
 // transpose loads in the same order. gradK^T and gradV^T (FIRST: also the
 // first-backward dK^T = s dS^T Q and dV^T = P^T dO) stay in registers for the
-// whole sweep. The masked blocks (causal diagonal, partial blocks) run apart
-// from a branch-free pair loop over the rest.
+// whole sweep and leave through LDS in whole-line stores. The masked blocks
+// (causal diagonal, partial blocks) run apart from a branch-free pair loop over
+// the rest.
 
 #include <type_traits>
 

@@ -22,16 +22,18 @@
 //            (the key-major kernel starts its dP, G, H accumulators from them).
 //            FIRST: also the first-backward dQ = s dS K.
 //
-// gfx950 schedule: a workgroup of 4 waves owns 128 queries (32 per wave) and
-// streams the keys in 32-row stages (K, gK, V, gV) through two LDS buffers,
-// issuing each stage's global reads one stage ahead. Per 32-key block a wave builds the transposed tiles S^T, G^T,
+// gfx950 schedule: a workgroup of 4 waves (8 in bf16 d = 64 pass 2q) owns 32
+// queries per wave and streams the keys in 32-row stages (K, gK, V, gV)
+// through two LDS buffers, issuing each stage's global reads one stage ahead.
+// Per 32-key block a wave builds the transposed tiles S^T, G^T,
 // dP^T, H^T (keys x its queries) with MFMA; the accumulator layout then puts
 // one query per lane, so the row scalars are per-lane registers. In pass 2q
 // the elementwise results (P, dS, dS2, A) go straight from the accumulator
 // registers into the next MFMAs as B operands (k = keys, in the accumulator's
 // row order); the A operands K^T, gK^T, V^T, gV^T come from the LDS stage via
 // transpose reads in the same k order. gradQ^T and graddO^T stay in registers
-// for the whole sweep: no atomics, no cross-wave reduction.
+// for the whole sweep (no atomics, no cross-wave reduction) and leave through
+// LDS in whole-line stores.
 
 #include <type_traits>
 
