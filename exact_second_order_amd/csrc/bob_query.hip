@@ -209,11 +209,13 @@ __device__ __forceinline__ void query_chunk(int cc, const f32x16& S, const f32x1
 // (pair s2 reads words 8 cc + 2 s2, + 1 and writes word 8 cc + s2, which the
 // same or an earlier pair has already read). The chunk's bf16 operand
 // fragments are then those four words of each tile (packed_frag), and no
-// separate fragment registers are live.
-template <bool TAIL>
+// separate fragment registers are live. With SHIFTED, dP and H arrive
+// already shifted by the row's -D and -r (their accumulators start from
+// them); otherwise Dq and rq (-D and -r) are added here.
+template <bool TAIL, bool SHIFTED>
 __device__ __forceinline__ void query_chunk_inplace(int cc, f32x16& S, f32x16& G, f32x16& dP, f32x16& H,
-                                                    float sl2, float scale, float l2, float Dq, float cq, float rq,
-                                                    int nvalid_rel) {
+                                                    float sl2, float scale, float l2, float Dq, float cq,
+                                                    float rq, int nvalid_rel) {
   typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
   typedef float f32x2_t __attribute__((ext_vector_type(2)));
   auto pack = [](float a, float b) __attribute__((always_inline)) {
@@ -228,12 +230,12 @@ __device__ __forceinline__ void query_chunk_inplace(int cc, f32x16& S, f32x16& G
       const int i = 8 * cc + 2 * s2 + e;
       float p = fast_exp2(fmaf(S[i], sl2, -l2));
       if (TAIL && acc_row(h, i) >= nvalid_rel) p = 0.f;
-      const float ds = p * (dP[i] + Dq);
+      const float ds = p * (SHIFTED ? dP[i] : dP[i] + Dq);
       const float g = fmaf(G[i], scale, cq);
       vp[e] = p;
       vds[e] = ds;
       va[e] = p * g;
-      vd2[e] = fmaf(ds, g, p * (H[i] + rq));
+      vd2[e] = fmaf(ds, g, p * (SHIFTED ? H[i] : H[i] + rq));
     }
     S[8 * cc + s2] = pack(vp[0], vp[1]);
     dP[8 * cc + s2] = pack(vds[0], vds[1]);
@@ -417,13 +419,25 @@ void query_kernel(
     f32x16 S, G, dP, H;
   };
   // d-chunks [c0, c1) of the recompute products of block n
+  // bf16 pass 2q packs the operand fragments into the score tiles' own
+  // registers (query_chunk_inplace); fp32 keeps them apart
+  constexpr bool INPLACE = GRADQ && sizeof(T) == 2;
+  // start dP and H from -D and -r: two fewer VALU operations per element,
+  // left out where the first-backward accumulator leaves no registers for it
+  constexpr bool SHIFTED = INPLACE && !FIRST;
   auto recompute = [&](int n, Tiles& t, int c0, int c1) __attribute__((always_inline)) {
     const int b = n & (NBUF - 1);
     if (c0 == 0) {
       t.S = f32x16{};
       t.G = f32x16{};
-      t.dP = f32x16{};
-      t.H = f32x16{};
+      if constexpr (SHIFTED) {
+        // the row's -D and -r (one query per lane: a broadcast)
+        t.dP = f32x16{Dq, Dq, Dq, Dq, Dq, Dq, Dq, Dq, Dq, Dq, Dq, Dq, Dq, Dq, Dq, Dq};
+        t.H = f32x16{rq, rq, rq, rq, rq, rq, rq, rq, rq, rq, rq, rq, rq, rq, rq, rq};
+      } else {
+        t.dP = f32x16{};
+        t.H = f32x16{};
+      }
     }
 #pragma unroll
     for (int c = c0; c < c1; ++c) {
@@ -438,9 +452,6 @@ void query_kernel(
       E::mma(t.H, agv, fdO[c]);
     }
   };
-  // bf16 pass 2q packs the operand fragments into the score tiles' own
-  // registers (query_chunk_inplace); fp32 keeps them apart
-  constexpr bool INPLACE = GRADQ && sizeof(T) == 2;
   struct Frags {
     F P[2], dS[2], dS2[2], A[2];
   };
@@ -452,7 +463,7 @@ void query_kernel(
     if constexpr (!GRADQ)
       online_chunk<TAIL, SAVED>(cc, t.S, t.G, t.dP, t.H, sl2, nrel, st, mu);
     else if constexpr (INPLACE)
-      query_chunk_inplace<TAIL>(cc, t.S, t.G, t.dP, t.H, sl2, scale, l2, Dq, cq, rq, nrel);
+      query_chunk_inplace<TAIL, SHIFTED>(cc, t.S, t.G, t.dP, t.H, sl2, scale, l2, Dq, cq, rq, nrel);
     else
       query_chunk<T, TAIL>(cc, t.S, t.G, t.dP, t.H, sl2, scale, l2, Dq, cq, rq, nrel, f.P[cc], f.dS[cc],
                            f.dS2[cc], f.A[cc]);
