@@ -109,10 +109,10 @@ CEILING_EXE = os.path.join(ROOT, "exact_second_order_amd", "_build", "mfma_ceili
 
 
 def mfma_ceiling():
-    """Sustained 32x32x16 bf16 MFMA rate of this GPU under its power limit
-    (random-normal operands changing every instruction, and zeros), from the
-    standalone program built next to the library; run as a child process after
-    the timed region. None if it is missing or fails."""
+    """Sustained 32x32x16 (and 16x16x32) bf16 MFMA rate of this GPU under its
+    power limit (random-normal operands changing every instruction, and
+    zeros), from the standalone program built next to the library; run as a
+    child process after the timed region. None if it is missing or fails."""
     import subprocess
     if not os.path.exists(CEILING_EXE):
         log("[bench] mfma ceiling: program not built (run build())")
@@ -343,6 +343,10 @@ def main():
             roofline["mfma_ceiling"] = {"tflops": ceil["random"]["tflops"], "sclk_ghz": ceil["random"]["sclk_ghz"],
                                         "zero_operands_tflops": ceil["zero"]["tflops"],
                                         "instruction": ceil["instruction"]}
+            # the 16-row tile instruction under the same limit
+            m16 = ceil.get("v_mfma_f32_16x16x32_bf16")
+            if m16:
+                roofline["mfma_ceiling"]["tflops_16x16x32"] = m16["random"]["tflops"]
             roofline["executed_frac_of_ceiling"] = round(roofline["executed_tflops"] / ceil["random"]["tflops"], 4)
 
     cpu = None
