@@ -279,6 +279,15 @@ __device__ __forceinline__ void negate(f32x8& f) {
   f = __builtin_bit_cast(f32x8, __builtin_bit_cast(u32x8, f) ^ 0x80000000u);
 }
 
+// Multiply every element by a power of two a (exact for bf16: the product of
+// two values carrying at most 8 significant bits, re-rounded, is itself).
+__device__ __forceinline__ void scale_frag(bf16x8& f, float a) {
+  typedef float f32x8v __attribute__((ext_vector_type(8)));
+  typedef __bf16 bf16x8v __attribute__((ext_vector_type(8)));
+  const f32x8v x = __builtin_convertvector(__builtin_bit_cast(bf16x8v, f), f32x8v) * a;
+  f = __builtin_bit_cast(bf16x8, __builtin_convertvector(x, bf16x8v));
+}
+
 // Wait for this wave's outstanding global loads, including direct-to-LDS ones.
 __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 

@@ -35,6 +35,7 @@
 // for the whole sweep (no atomics, no cross-wave reduction) and leave through
 // LDS in whole-line stores.
 
+#include <cmath>
 #include <type_traits>
 
 #include "bob_device.h"
@@ -134,8 +135,10 @@ constexpr int kFlush = 64;  // blocks per level-1 chain
 // chunk adds its 8 keys. In the TAIL variant keys at relative index
 // >= nvalid_rel are masked out. FIXED: the row's saved log-sum-exp serves as
 // the maximum for the whole sweep (p <= 1 throughout), so there is neither a
-// block maximum nor a rescale.
-template <bool TAIL, bool FIXED>
+// block maximum nor a rescale. PRE: S and G arrive scaled by s (the kernel
+// scaled Q and gQ), so ae takes the whole sum P (dP G + H) that r needs
+// (one fma fewer per element) and ah stays zero.
+template <bool TAIL, bool FIXED, bool PRE>
 __device__ __forceinline__ void online_chunk(int cc, const f32x16& S, const f32x16& G, const f32x16& dP,
                                              const f32x16& H, float sl2, int nvalid_rel, OnlineSums& st,
                                              float& mu) {
@@ -165,12 +168,19 @@ __device__ __forceinline__ void online_chunk(int cc, const f32x16& S, const f32x
     const int i = 8 * cc + s;
     float p = fast_exp2(fmaf(S[i], sl2, -mu));
     if (TAIL && acc_row(h, i) >= nvalid_rel) p = 0.f;
-    const float t = p * dP[i];
-    st.l += p;
-    st.aD += t;
-    st.ac = fmaf(p, G[i], st.ac);
-    st.ae = fmaf(t, G[i], st.ae);
-    st.ah = fmaf(p, H[i], st.ah);
+    if constexpr (PRE) {
+      st.l += p;
+      st.aD = fmaf(p, dP[i], st.aD);
+      st.ac = fmaf(p, G[i], st.ac);
+      st.ae = fmaf(p, fmaf(dP[i], G[i], H[i]), st.ae);
+    } else {
+      const float t = p * dP[i];
+      st.l += p;
+      st.aD += t;
+      st.ac = fmaf(p, G[i], st.ac);
+      st.ae = fmaf(t, G[i], st.ae);
+      st.ah = fmaf(p, H[i], st.ah);
+    }
   }
 }
 
@@ -253,7 +263,9 @@ __device__ __forceinline__ bf16x8 packed_frag(const f32x16& t, int cc) {
 // FIRST (pass 2q only): also return the first-backward dQ = s dS K (one more
 // product per block against the K^T operand already read; the extra
 // accumulator needs the one-wave-per-SIMD register budget).
-template <typename T, int D, bool GRADQ, bool FIRST, bool SAVED>
+// PRE (pass 1, bf16, |s| a power of two in (0, 1]): Q and gQ are scaled by |s|
+// in registers, which is exact, so S and G come out of the MFMAs scaled.
+template <typename T, int D, bool GRADQ, bool FIRST, bool SAVED, bool PRE = false>
 __global__ __launch_bounds__((QueryCfg<T, D, GRADQ, FIRST>::NW * 64),
                              (QueryCfg<T, D, GRADQ, FIRST>::OCC * 4 / QueryCfg<T, D, GRADQ, FIRST>::NW))
 void query_kernel(
@@ -263,6 +275,7 @@ void query_kernel(
     void* __restrict__ graddO, void* __restrict__ dQo, const float* __restrict__ lse_in, int N, int nqblk,
     float scale, int lse_natural, int causal, int G, int out_bf16) {
   static_assert(!(SAVED && GRADQ), "a saved log-sum-exp replaces pass 1's running maximum only");
+  static_assert(!PRE || (!GRADQ && sizeof(T) == 2), "pre-scaled operands: bf16 pass 1 only");
   using Cfg = QueryCfg<T, D, GRADQ, FIRST>;
   using E = Elem<T>;
   using F = typename E::frag;
@@ -326,7 +339,14 @@ void query_kernel(
     }
   }
   scale *= sgn;
-  const float sl2 = scale * kLog2e;
+  if constexpr (PRE) {
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+      scale_frag(fQ[c], scale);
+      scale_frag(fgQ[c], scale);
+    }
+  }
+  const float sl2 = (PRE ? 1.f : scale) * kLog2e;
   OnlineSums st;  // pass 1 state
   float mu = 0.f;  // pass 1: the running max used for the current block
   if constexpr (SAVED) {
@@ -461,7 +481,7 @@ void query_kernel(
     constexpr bool TAIL = decltype(tail)::value;
     const int nrel = qlim - n * BK;
     if constexpr (!GRADQ)
-      online_chunk<TAIL, SAVED>(cc, t.S, t.G, t.dP, t.H, sl2, nrel, st, mu);
+      online_chunk<TAIL, SAVED, PRE>(cc, t.S, t.G, t.dP, t.H, sl2, nrel, st, mu);
     else if constexpr (INPLACE)
       query_chunk_inplace<TAIL, SHIFTED>(cc, t.S, t.G, t.dP, t.H, sl2, scale, l2, Dq, cq, rq, nrel);
     else
@@ -561,10 +581,10 @@ void query_kernel(
       const float inv = 1.f / L;
       const float Dr = AD * inv;
       // scale is |s| here and G carried the sign of s, so c = |s| AC / L and
-      // c / s = sgn AC / L
-      const float cr = scale * AC * inv;
-      const float cbar = sgn * AC * inv;
-      const float rr = scale * AE * inv - Dr * cr + AH * inv;
+      // c / s = sgn AC / L (PRE: G is s G already, and AE holds s AE + AH)
+      const float cr = PRE ? AC * inv : scale * AC * inv;
+      const float cbar = PRE ? sgn * AC * inv / scale : sgn * AC * inv;
+      const float rr = PRE ? AE * inv - Dr * cr : scale * AE * inv - Dr * cr + AH * inv;
       const size_t o = (size_t)head * N + q;
       const float lse2 = mm + log2f(L);
       if (lse_natural) {  // the row statistics themselves
@@ -607,6 +627,17 @@ hipError_t launch_query(const void* Q, const void* K, const void* V, const void*
   const int nqblk = (N + Cfg::BQ - 1) / Cfg::BQ;
   const long long nblocks = (long long)nqblk * BH * Cfg::OSPLIT;
   if (nblocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  // bf16 pass 1 at d = 64 with |s| = 2^-k (k = 0 .. 60): the pre-scaled variant
+  if constexpr (!GRADQ && !FIRST && sizeof(T) == 2 && D == 64) {
+    int e = 0;
+    const float a = std::fabs(scale);
+    if (a > 0.f && a <= 1.f && std::frexp(a, &e) == 0.5f && e >= -59) {
+      query_kernel<T, D, GRADQ, FIRST, SAVED, true><<<dim3((unsigned)nblocks), dim3(Cfg::NW * 64), 0, stream>>>(
+          (const T*)Q, (const T*)K, (const T*)V, (const T*)dO, (const T*)gQ, (const T*)gK, (const T*)gV, lse, Dv,
+          cv, rv, gradQ, graddO, dQ, lse_in, N, nqblk, scale, lse_natural, causal, G, out_bf16);
+      return hipGetLastError();
+    }
+  }
   query_kernel<T, D, GRADQ, FIRST, SAVED><<<dim3((unsigned)nblocks), dim3(Cfg::NW * 64), 0, stream>>>(
       (const T*)Q, (const T*)K, (const T*)V, (const T*)dO, (const T*)gQ, (const T*)gK, (const T*)gV, lse, Dv,
       cv, rv, gradQ, graddO, dQ, lse_in, N, nqblk, scale, lse_natural, causal, G, out_bf16);
