@@ -221,8 +221,9 @@ __device__ __forceinline__ void query_chunk(int cc, const f32x16& S, const f32x1
 // fragments are then those four words of each tile (packed_frag), and no
 // separate fragment registers are live. With SHIFTED, dP and H arrive
 // already shifted by the row's -D and -r (their accumulators start from
-// them); otherwise Dq and rq (-D and -r) are added here.
-template <bool TAIL, bool SHIFTED>
+// them); otherwise Dq and rq (-D and -r) are added here. GSCALED: G arrives
+// as s G - c (pre-scaled operands, accumulator started from -c).
+template <bool TAIL, bool SHIFTED, bool GSCALED = false>
 __device__ __forceinline__ void query_chunk_inplace(int cc, f32x16& S, f32x16& G, f32x16& dP, f32x16& H,
                                                     float sl2, float scale, float l2, float Dq, float cq,
                                                     float rq, int nvalid_rel) {
@@ -241,7 +242,7 @@ __device__ __forceinline__ void query_chunk_inplace(int cc, f32x16& S, f32x16& G
       float p = fast_exp2(fmaf(S[i], sl2, -l2));
       if (TAIL && acc_row(h, i) >= nvalid_rel) p = 0.f;
       const float ds = p * (SHIFTED ? dP[i] : dP[i] + Dq);
-      const float g = fmaf(G[i], scale, cq);
+      const float g = GSCALED ? G[i] : fmaf(G[i], scale, cq);
       vp[e] = p;
       vds[e] = ds;
       va[e] = p * g;
@@ -263,8 +264,10 @@ __device__ __forceinline__ bf16x8 packed_frag(const f32x16& t, int cc) {
 // FIRST (pass 2q only): also return the first-backward dQ = s dS K (one more
 // product per block against the K^T operand already read; the extra
 // accumulator needs the one-wave-per-SIMD register budget).
-// PRE (pass 1, bf16, |s| a power of two in (0, 1]): Q and gQ are scaled by |s|
-// in registers, which is exact, so S and G come out of the MFMAs scaled.
+// PRE (bf16 pass 1 and plain pass 2q, |s| a power of two in (0, 1]): Q and gQ
+// are scaled by s (pass 1: |s|, after its sign flip) in registers, which is
+// exact, so S and G come out of the MFMAs scaled; pass 2q then starts G from
+// the row's -c like dP and H.
 template <typename T, int D, bool GRADQ, bool FIRST, bool SAVED, bool PRE = false>
 __global__ __launch_bounds__((QueryCfg<T, D, GRADQ, FIRST>::NW * 64),
                              (QueryCfg<T, D, GRADQ, FIRST>::OCC * 4 / QueryCfg<T, D, GRADQ, FIRST>::NW))
@@ -275,7 +278,7 @@ void query_kernel(
     void* __restrict__ graddO, void* __restrict__ dQo, const float* __restrict__ lse_in, int N, int nqblk,
     float scale, int lse_natural, int causal, int G, int out_bf16) {
   static_assert(!(SAVED && GRADQ), "a saved log-sum-exp replaces pass 1's running maximum only");
-  static_assert(!PRE || (!GRADQ && sizeof(T) == 2), "pre-scaled operands: bf16 pass 1 only");
+  static_assert(!PRE || (sizeof(T) == 2 && !FIRST), "pre-scaled operands: bf16 pass 1 and plain pass 2q");
   using Cfg = QueryCfg<T, D, GRADQ, FIRST>;
   using E = Elem<T>;
   using F = typename E::frag;
@@ -449,7 +452,10 @@ void query_kernel(
     const int b = n & (NBUF - 1);
     if (c0 == 0) {
       t.S = f32x16{};
-      t.G = f32x16{};
+      if constexpr (GRADQ && PRE)  // s G - c: the lane's -c
+        t.G = f32x16{cq, cq, cq, cq, cq, cq, cq, cq, cq, cq, cq, cq, cq, cq, cq, cq};
+      else
+        t.G = f32x16{};
       if constexpr (SHIFTED) {
         // the row's -D and -r (one query per lane: a broadcast)
         t.dP = f32x16{Dq, Dq, Dq, Dq, Dq, Dq, Dq, Dq, Dq, Dq, Dq, Dq, Dq, Dq, Dq, Dq};
@@ -483,7 +489,7 @@ void query_kernel(
     if constexpr (!GRADQ)
       online_chunk<TAIL, SAVED, PRE>(cc, t.S, t.G, t.dP, t.H, sl2, nrel, st, mu);
     else if constexpr (INPLACE)
-      query_chunk_inplace<TAIL, SHIFTED>(cc, t.S, t.G, t.dP, t.H, sl2, scale, l2, Dq, cq, rq, nrel);
+      query_chunk_inplace<TAIL, SHIFTED, PRE>(cc, t.S, t.G, t.dP, t.H, sl2, scale, l2, Dq, cq, rq, nrel);
     else
       query_chunk<T, TAIL>(cc, t.S, t.G, t.dP, t.H, sl2, scale, l2, Dq, cq, rq, nrel, f.P[cc], f.dS[cc],
                            f.dS2[cc], f.A[cc]);
@@ -627,8 +633,9 @@ hipError_t launch_query(const void* Q, const void* K, const void* V, const void*
   const int nqblk = (N + Cfg::BQ - 1) / Cfg::BQ;
   const long long nblocks = (long long)nqblk * BH * Cfg::OSPLIT;
   if (nblocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-  // bf16 pass 1 at d = 64 with |s| = 2^-k (k = 0 .. 60): the pre-scaled variant
-  if constexpr (!GRADQ && !FIRST && sizeof(T) == 2 && D == 64) {
+  // bf16 pass 1 and plain pass 2q at d = 64 with |s| = 2^-k (k = 0 .. 59):
+  // the pre-scaled variant
+  if constexpr (!FIRST && sizeof(T) == 2 && D == 64) {
     int e = 0;
     const float a = std::fabs(scale);
     if (a > 0.f && a <= 1.f && std::frexp(a, &e) == 0.5f && e >= -59) {

@@ -11,7 +11,7 @@ the fp64 oracle's textbook first backward (oracle.attention_backward_batched).
     any size (columns of dK sum to zero, those of dV to the sum of dO's rows,
     and sum_i Q_i . dQ_i = sum_j K_j . dK_j);
   * the BoB outputs of the same call equal those of the plain call (bf16
-    gradQ up to a different rounding order);
+    gradQ and graddO up to a different rounding order);
   * stage subsets: each pass-2 stage fills its own first-backward outputs.
 """
 
@@ -95,21 +95,24 @@ def test_first_workload_4096(causal):
     say(f"{label}: worst rel {check_against_oracle(ins, outs, w.scale, causal, TOL[w.dtype], label):.3e}")
 
 
-# bf16 gradQ of the plain call starts the dP and H accumulators from the rows'
-# -D and -r, the first-backward kernel adds them after the dot products (it
-# has no registers to spare for the broadcast). The fp32 sums round
-# differently, the differences dP - D and H - r cancel, and the bf16 rounding
-# of the dS, dS2 operands then flips the last bit of a few of them: a relative
-# change of order 2^-8 on a small fraction of the terms of gradQ's sums,
-# 1e-5 in the Frobenius norm at N = 1000, far inside the bf16 parity bar.
+# The plain call's bf16 query-side kernel starts its dP, H and G accumulators
+# from the rows' -D, -r and -c and, when |s| is a power of two, scales Q and
+# gQ by s first; the first-backward kernel adds the row scalars after the dot
+# products and scales G there (it has no registers to spare). The fp32 sums
+# round differently, the differences dP - D, H - r and s G - c cancel, and
+# the bf16 rounding of the dS, dS2 and A operands then flips the last bit of
+# a few of them: a relative change of order 2^-8 on a small fraction of the
+# terms of gradQ's and graddO's sums, about 1e-5 in the Frobenius norm at
+# N = 1000, far inside the bf16 parity bar. (gradK and gradV come from the
+# same key-side kernel code in both calls.)
 BF16_GRADQ_REORDER = 1e-4
 
 
 def test_first_leaves_bob_outputs_unchanged():
     # the extra products must not disturb the BoB ones: the BoB products and
     # their order are those of the plain call, so the same values up to fp32
-    # rounding, except bf16 gradQ, where -D and -r enter the sums at another
-    # point (BF16_GRADQ_REORDER)
+    # rounding, except bf16 gradQ and graddO, whose row scalars and scale
+    # enter the sums at another point (BF16_GRADQ_REORDER)
     for dtype, causal, Hkv in ((torch.bfloat16, False, 4), (torch.float32, True, 2), (torch.bfloat16, True, 1)):
         say(f"[first] unchanged BoB outputs {dtype} causal={causal} Hkv={Hkv}")
         ins = make_inputs(1, 4, 1000, 64, dtype, seed=41, H_kv=Hkv)
@@ -119,7 +122,7 @@ def test_first_leaves_bob_outputs_unchanged():
         torch.cuda.synchronize()
         for k in range(4):
             e = rel_fro(to_f64(both[k]), to_f64(plain[k]))
-            bound = BF16_GRADQ_REORDER if (k == 0 and dtype == torch.bfloat16) else 1e-6
+            bound = BF16_GRADQ_REORDER if (k in (0, 3) and dtype == torch.bfloat16) else 1e-6
             assert e <= bound, f"output {k}: {e:.3e}"
 
 
@@ -216,5 +219,5 @@ def test_first_big_key_side_identities(big_first):
 def test_first_big_bob_outputs_unchanged(big_first):
     w, _, both, plain = big_first
     for k in range(4):
-        bound = BF16_GRADQ_REORDER if (k == 0 and w.dtype == torch.bfloat16) else 1e-6
+        bound = BF16_GRADQ_REORDER if (k in (0, 3) and w.dtype == torch.bfloat16) else 1e-6
         assert rel_fro(to_f64(both[k]), to_f64(plain[k])) <= bound, k
