@@ -15,11 +15,15 @@
 //            l = sum Pt, aD = sum Pt dP, ac = sum Pt G, ae = sum Pt dP G,
 //            ah = sum Pt H (Pt = exp(s S - m)), then D = aD/l, c = ac/l,
 //            r = ae/l - D c + ah/l, LSE = m + ln l. (SAVED: m is fixed at a
-//            saved log-sum-exp of the row for the whole sweep.)
+//            saved log-sum-exp of the row for the whole sweep. PRE: Q and gQ
+//            arrive scaled by s, G is s G, and ae = sum Pt (dP G + H) holds
+//            both of r's sums.)
 //   pass 2q: dS  = P (dP - D),  A = P (G - c),  dS2 = dS (G - c) + P (H - r),
 //            gradQ = s (dS2 K + dS gK),  graddO = A V + P gV.
 //            Pass 1 hands the scalars over as LSE log2(e), -D, -c/s and -r
-//            (the key-major kernel starts its dP, G, H accumulators from them).
+//            (the key-major kernel starts its dP, G, H accumulators from them;
+//            in bf16 this one starts dP and H from -D and -r, and with PRE G
+//            from -c).
 //            FIRST: also the first-backward dQ = s dS K.
 //
 // gfx950 schedule: a workgroup of 4 waves (8 in bf16 d = 64 pass 2q) owns 32
