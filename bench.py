@@ -41,10 +41,15 @@ def log(*a):
 
 
 def kernel_source_hash():
+    """Hash of the kernel sources' code: `//` comments, trailing blanks and
+    empty lines are left out, so the recorded counters survive comment edits."""
     h = hashlib.sha256()
     for rel in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, rel), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, rel), encoding="utf-8") as f:
+            for line in f:
+                code = line.split("//", 1)[0].rstrip()
+                if code:
+                    h.update(code.encode() + b"\n")
     return h.hexdigest()[:16]
 
 

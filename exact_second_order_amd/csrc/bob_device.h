@@ -279,8 +279,9 @@ __device__ __forceinline__ void negate(f32x8& f) {
   f = __builtin_bit_cast(f32x8, __builtin_bit_cast(u32x8, f) ^ 0x80000000u);
 }
 
-// Multiply every element by a power of two a (exact for bf16: the product of
-// two values carrying at most 8 significant bits, re-rounded, is itself).
+// Multiply every element by a power of two a. Only the exponent changes, so
+// the result is exact unless it falls below the normal range (2^-126), where
+// it is rounded and stays negligible beside any normal term.
 __device__ __forceinline__ void scale_frag(bf16x8& f, float a) {
   typedef float f32x8v __attribute__((ext_vector_type(8)));
   typedef __bf16 bf16x8v __attribute__((ext_vector_type(8)));

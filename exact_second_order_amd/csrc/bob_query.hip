@@ -269,9 +269,9 @@ __device__ __forceinline__ bf16x8 packed_frag(const f32x16& t, int cc) {
 // product per block against the K^T operand already read; the extra
 // accumulator needs the one-wave-per-SIMD register budget).
 // PRE (bf16 pass 1 and plain pass 2q, |s| a power of two in (0, 1]): Q and gQ
-// are scaled by s (pass 1: |s|, after its sign flip) in registers, which is
-// exact, so S and G come out of the MFMAs scaled; pass 2q then starts G from
-// the row's -c like dP and H.
+// are scaled by s (pass 1: |s|, after its sign flip) in registers, exactly
+// short of elements pushed below the normal range, so S and G come out of
+// the MFMAs scaled; pass 2q then starts G from the row's -c like dP and H.
 template <typename T, int D, bool GRADQ, bool FIRST, bool SAVED, bool PRE = false>
 __global__ __launch_bounds__((QueryCfg<T, D, GRADQ, FIRST>::NW * 64),
                              (QueryCfg<T, D, GRADQ, FIRST>::OCC * 4 / QueryCfg<T, D, GRADQ, FIRST>::NW))
