@@ -639,17 +639,13 @@ hipError_t launch_query(const void* Q, const void* K, const void* V, const void*
   if (nblocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   // bf16 pass 1 and plain pass 2q at d = 64 with |s| = 2^-k (k = 0 .. 59):
   // the pre-scaled variant
+  auto kern = query_kernel<T, D, GRADQ, FIRST, SAVED, false>;
   if constexpr (!FIRST && sizeof(T) == 2 && D == 64) {
     int e = 0;
     const float a = std::fabs(scale);
-    if (a > 0.f && a <= 1.f && std::frexp(a, &e) == 0.5f && e >= -59) {
-      query_kernel<T, D, GRADQ, FIRST, SAVED, true><<<dim3((unsigned)nblocks), dim3(Cfg::NW * 64), 0, stream>>>(
-          (const T*)Q, (const T*)K, (const T*)V, (const T*)dO, (const T*)gQ, (const T*)gK, (const T*)gV, lse, Dv,
-          cv, rv, gradQ, graddO, dQ, lse_in, N, nqblk, scale, lse_natural, causal, G, out_bf16);
-      return hipGetLastError();
-    }
+    if (a > 0.f && a <= 1.f && std::frexp(a, &e) == 0.5f && e >= -58) kern = query_kernel<T, D, GRADQ, FIRST, SAVED, true>;
   }
-  query_kernel<T, D, GRADQ, FIRST, SAVED><<<dim3((unsigned)nblocks), dim3(Cfg::NW * 64), 0, stream>>>(
+  kern<<<dim3((unsigned)nblocks), dim3(Cfg::NW * 64), 0, stream>>>(
       (const T*)Q, (const T*)K, (const T*)V, (const T*)dO, (const T*)gQ, (const T*)gK, (const T*)gV, lse, Dv,
       cv, rv, gradQ, graddO, dQ, lse_in, N, nqblk, scale, lse_natural, causal, G, out_bf16);
   return hipGetLastError();
