@@ -27,6 +27,8 @@ CASES = [
     (0.125, 1.0, True),          # the default at d = 64
     (-0.125, 1.0, True),         # negative: pass 1 flips the sign, pass 2q scales by s
     (2.0 ** -10, 1.0, True),     # nearly uniform softmax
+    (2.0 ** -59, 1.0, True),     # the smallest pre-scaled one
+    (2.0 ** -60, 1.0, False),    # just past it: general kernels
     (2.0, 0.0625, False),        # a power of two above 1: general kernels
     (0.13, 1.0, False),
     (-0.3, 0.5, False),
